@@ -1,0 +1,129 @@
+/*
+ * attn.h: C ABI of the MI355X (gfx950) exact-attention library libmi355attn.so.
+ *
+ * What it computes. Exact scaled-dot-product attention
+ *     O = softmax(Q K^T * scale + mask) V
+ * computed tile by tile with an online softmax, so the S x S score matrix is
+ * never written to device memory. Sources:
+ *   - "ms-swift集成FlashAttention 2/3，长文本训练更高效", section
+ *     "FlashAttention 如何破局": Q, K and V are split along the sequence; each
+ *     workgroup holds a Q block on chip and streams the matching K/V blocks;
+ *     QK^T, softmax and PV stay on chip, a running maximum and normaliser are
+ *     kept per row, and only the output goes back to global memory.
+ *   - The same page's section on why standard attention is memory-hungry
+ *     defines the unfused computation this must equal (QK^T, softmax, PV over
+ *     a [B, H, S, S] tensor).
+ *   - The backward recomputes the probabilities from the saved log-sum-exp;
+ *     the same memory section notes that the backward needs the intermediates
+ *     again.
+ * The shapes are one GPU's share of Ulysses sequence parallelism
+ * ("ms-swift长文本训练秘诀：Ulysses并行技术解析" §1; FlashAttention page, the
+ * Ulysses part of the sequence-parallel section): after the all-to-all a GPU
+ * holds the full sequence for a subset of heads. Nothing here communicates.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are device pointers unless stated. Tensors are contiguous and
+ *     16-byte aligned. Q, O, dO, dQ are [B, S, Hq, D]; K, V, dK, dV are
+ *     [B, S, Hkv, D]; LSE is float32 [B, Hq, S]: the natural-log
+ *     log-sum-exp of each row's scaled, masked scores.
+ *   - GQA: query head h reads key/value head h / (Hq / Hkv); Hq must be a
+ *     multiple of Hkv.
+ *   - Masks: causal means key j is visible to query i iff j <= i. With
+ *     cu_seqlens (int32 device array of num_seqs + 1 prefix sums, first 0,
+ *     strictly increasing, last == seqlen) the batch must be 1 and seqlen is
+ *     the total packed length. Key j is then visible to query i only when
+ *     both lie in the same segment (block-diagonal), and causal applies
+ *     within the segment. Packing several samples into one long sequence is
+ *     the packing of the Ulysses page §5 and of the FlashAttention page's
+ *     section on engineering results. cu_seqlens contents are not checked on
+ *     the device; a malformed array gives undefined results.
+ *   - scale must be finite and > 0 (the configurations use 1/sqrt(D)).
+ *   - head_dim must be 64 or 128 (bf16 paths) or 128 (fp8 path); other values
+ *     return ATTN_ERR_UNSUPPORTED so the caller can fall back to a standard
+ *     implementation. Automatic fallback when the fused kernel is unusable
+ *     is described in the FlashAttention page's "实际怎么用" section.
+ *   - Ownership: the caller allocates and owns every buffer, including the
+ *     backward workspace. The library allocates nothing and keeps no state
+ *     besides its loaded code. It is safe to call from several host threads.
+ *   - Asynchrony: each call only enqueues kernels on `stream` (0 = the null
+ *     stream). Results are valid once the stream reaches that point.
+ *   - Errors: every argument check runs before any HIP call. A non-OK status
+ *     means nothing was enqueued, except ATTN_ERR_HIP, which reports a failed
+ *     launch (attn_last_hip_error() then gives the hipError_t value).
+ *   - Determinism: no atomics; identical inputs give bitwise identical outputs.
+ */
+#ifndef MI355ATTN_ATTN_H_
+#define MI355ATTN_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* attn_stream_t; /* same object as hipStream_t */
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARGUMENT = 1, /* inconsistent shape, flag or pointer; nothing enqueued */
+  ATTN_ERR_UNSUPPORTED = 2,      /* valid request this build has no kernel for; caller may fall back */
+  ATTN_ERR_HIP = 3               /* a kernel launch failed; see attn_last_hip_error() */
+} attn_status;
+
+/* Forward, bf16 in and out.
+ * q [B,S,Hq,D], k and v [B,S,Hkv,D] bfloat16 (read only).
+ * o [B,S,Hq,D] bfloat16 (written). lse [B,Hq,S] float32 (written).
+ * Rounding: O is accumulated in fp32 and rounded to bf16 (nearest-even).
+ */
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int batch, int hq, int hkv, int seqlen, int head_dim,
+                     int causal, const int32_t* cu_seqlens, int num_seqs,
+                     float scale, attn_stream_t stream);
+
+/* Forward with OCP FP8 E4M3FN inputs and per-tensor scales.
+ * FP8 appears in the FA-3 paragraph of the FlashAttention page; per-tensor
+ * scaling of E4M3 data appears in the Q-Galore section of
+ * "ms-swift支持GPU显存碎片整理提升利用率".
+ * q8, k8, v8: uint8 E4M3FN codes, shapes as q, k, v. The real inputs are
+ * code * descale. descale_q/k/v: device pointers to one float each.
+ * o: bfloat16 [B,S,Hq,D]; lse: float32 [B,Hq,S] of the dequantised scores.
+ * The probabilities fed to the PV product are rounded to E4M3. The row sum is
+ * taken from the fp32 probabilities. head_dim must be 128.
+ */
+attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
+                         const float* descale_q, const float* descale_k, const float* descale_v,
+                         void* o, float* lse,
+                         int batch, int hq, int hkv, int seqlen, int head_dim,
+                         int causal, const int32_t* cu_seqlens, int num_seqs,
+                         float scale, attn_stream_t stream);
+
+/* Bytes of device workspace attn_bwd needs: 4 * batch * hq * seqlen (the
+ * per-row Delta_i = dO_i . O_i in fp32). Returns 0 for non-positive sizes. */
+size_t attn_bwd_workspace_bytes(int batch, int hq, int seqlen);
+
+/* Backward: dq, dk, dv from q, k, v, the forward's o and lse, and dout.
+ * The probabilities are recomputed from lse. No S x S buffer is used.
+ * Inputs are bf16 (lse float32); dq [B,S,Hq,D], dk and dv [B,S,Hkv,D] are
+ * bf16 and fully overwritten. For GQA, dk and dv sum over the query heads of
+ * each group. workspace: at least attn_bwd_workspace_bytes() bytes, 16-byte
+ * aligned, owned by the caller, contents on entry ignored.
+ * Three kernels run on `stream` in order: Delta, dK/dV, dQ.
+ */
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                     int batch, int hq, int hkv, int seqlen, int head_dim,
+                     int causal, const int32_t* cu_seqlens, int num_seqs,
+                     float scale, attn_stream_t stream);
+
+/* Static string naming a status code ("ATTN_OK", ...). Never NULL. */
+const char* attn_status_str(attn_status s);
+
+/* hipError_t of the last failed launch on the calling thread (0 if none). */
+int attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI355ATTN_ATTN_H_ */

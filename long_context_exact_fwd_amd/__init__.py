@@ -1,0 +1,164 @@
+"""MI355X (gfx950) exact long-context attention: Python binding of libmi355attn.so.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/attn.h``. PyTorch supplies
+device memory and the current stream. The binding raises if the compiled
+library is missing; there is no fallback implementation.
+
+    o, lse = fwd(q, k, v, causal=True)                       # bf16 [B,S,H,D]
+    o, lse = fwd_fp8(q8, k8, v8, dq, dk, dv, causal=True)    # uint8 E4M3 codes
+    dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmi355attn.so")
+
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARGUMENT = 1
+ATTN_ERR_UNSUPPORTED = 2
+ATTN_ERR_HIP = 3
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libmi355attn.so and declare the C signatures. Raises if it is not built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing: build it with `python -m long_context_exact_fwd_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i, f, st = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, f, st]
+    lib.attn_fwd.restype = i
+    lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, f, st]
+    lib.attn_fwd_fp8.restype = i
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, f, st]
+    lib.attn_bwd.restype = i
+    lib.attn_bwd_workspace_bytes.argtypes = [i, i, i]
+    lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_status_str.argtypes = [i]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_last_hip_error.argtypes = []
+    lib.attn_last_hip_error.restype = i
+    if path is None:
+        _lib = lib
+    return lib
+
+
+EXPORTED = ("attn_fwd", "attn_fwd_fp8", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str",
+            "attn_last_hip_error")
+
+
+def _check(status: int, what: str) -> None:
+    if status != ATTN_OK:
+        lib = load_library()
+        name = lib.attn_status_str(status).decode()
+        extra = f" (hipError {lib.attn_last_hip_error()})" if status == ATTN_ERR_HIP else ""
+        raise AttnError(status, f"{what}: {name}{extra}")
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _shape(q, k, cu_seqlens):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [B, S, H, D]")
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if k.shape[0] != B or k.shape[1] != S or k.shape[3] != D:
+        raise ValueError("k/v shape must be [B, S, Hkv, D] with q's B, S, D")
+    n = 0
+    if cu_seqlens is not None:
+        import torch
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_cuda:
+            raise ValueError("cu_seqlens must be a 1-D int32 device tensor")
+        n = cu_seqlens.numel() - 1
+    return B, S, Hq, Hkv, D, n
+
+
+def _check_tensors(*ts, dtype=None):
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous device tensors")
+        if dtype is not None and t.dtype != dtype:
+            raise ValueError(f"expected {dtype}, got {t.dtype}")
+
+
+def fwd(q, k, v, *, causal: bool, cu_seqlens=None, scale: Optional[float] = None, out=None, lse=None):
+    """Forward, bf16. Returns (o [B,S,Hq,D] bf16, lse [B,Hq,S] fp32)."""
+    import torch
+    _check_tensors(q, k, v, dtype=torch.bfloat16)
+    B, S, Hq, Hkv, D, n = _shape(q, k, cu_seqlens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = out if out is not None else torch.empty_like(q)
+    l_ = lse if lse is not None else torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    st = load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l_), B, Hq, Hkv, S, D, int(bool(causal)),
+                                 _ptr(cu_seqlens), n, float(scale), _stream())
+    _check(st, "attn_fwd")
+    return o, l_
+
+
+def fwd_fp8(q8, k8, v8, descale_q, descale_k, descale_v, *, causal: bool, cu_seqlens=None,
+            scale: Optional[float] = None, out=None, lse=None):
+    """Forward with E4M3FN codes (uint8 tensors) and fp32 device descales (1 element each)."""
+    import torch
+    _check_tensors(q8, k8, v8, dtype=torch.uint8)
+    _check_tensors(descale_q, descale_k, descale_v, dtype=torch.float32)
+    B, S, Hq, Hkv, D, n = _shape(q8, k8, cu_seqlens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = out if out is not None else torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device=q8.device)
+    l_ = lse if lse is not None else torch.empty((B, Hq, S), dtype=torch.float32, device=q8.device)
+    st = load_library().attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(descale_q), _ptr(descale_k),
+                                     _ptr(descale_v), _ptr(o), _ptr(l_), B, Hq, Hkv, S, D, int(bool(causal)),
+                                     _ptr(cu_seqlens), n, float(scale), _stream())
+    _check(st, "attn_fwd_fp8")
+    return o, l_
+
+
+def bwd_workspace_bytes(batch: int, hq: int, seqlen: int) -> int:
+    return int(load_library().attn_bwd_workspace_bytes(batch, hq, seqlen))
+
+
+def bwd(q, k, v, o, lse, do, *, causal: bool, cu_seqlens=None, scale: Optional[float] = None, workspace=None,
+        dq=None, dk=None, dv=None):
+    """Backward, bf16. Returns (dq, dk, dv) shaped like q, k, v."""
+    import torch
+    _check_tensors(q, k, v, o, do, dtype=torch.bfloat16)
+    _check_tensors(lse, dtype=torch.float32)
+    B, S, Hq, Hkv, D, n = _shape(q, k, cu_seqlens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = dq if dq is not None else torch.empty_like(q)
+    dk = dk if dk is not None else torch.empty_like(k)
+    dv = dv if dv is not None else torch.empty_like(v)
+    if workspace is None:
+        nbytes = bwd_workspace_bytes(B, Hq, S)
+        workspace = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=q.device)
+    st = load_library().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), _ptr(workspace), B, Hq, Hkv, S, D, int(bool(causal)), _ptr(cu_seqlens), n,
+                                 float(scale), _stream())
+    _check(st, "attn_bwd")
+    return dq, dk, dv

@@ -1,0 +1,164 @@
+// C ABI of libmi355attn.so: argument checks, then kernel launches on the
+// caller's stream. Every check runs before any HIP call; see include/attn.h.
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/attn.h"
+#include "attn_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Largest element count of any tensor must fit the kernels' 32-bit row
+// arithmetic per (batch) slice and 64-bit offsets overall.
+attn_status check_common(int batch, int hq, int hkv, int seqlen, int head_dim, int causal,
+                         const int32_t* cu_seqlens, int num_seqs, float scale) {
+  if (batch < 1 || hq < 1 || hkv < 1 || seqlen < 1 || head_dim < 1) return ATTN_ERR_INVALID_ARGUMENT;
+  if (hq % hkv != 0) return ATTN_ERR_INVALID_ARGUMENT;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!(scale > 0.f) || !isfinite(scale)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (cu_seqlens != nullptr) {
+    if (batch != 1 || num_seqs < 1 || num_seqs > seqlen) return ATTN_ERR_INVALID_ARGUMENT;
+    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return ATTN_ERR_INVALID_ARGUMENT;
+  } else if (num_seqs != 0) {
+    return ATTN_ERR_INVALID_ARGUMENT;
+  }
+  // per-(b) slice of Q must be addressable with 32-bit row offsets times D
+  if ((long long)seqlen * hq * head_dim > (long long)INT32_MAX) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+attn_status launch_result(hipError_t e) {
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_str(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARGUMENT: return "ATTN_ERR_INVALID_ARGUMENT";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+  }
+  return "ATTN_ERR_UNKNOWN";
+}
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
+
+size_t attn_bwd_workspace_bytes(int batch, int hq, int seqlen) {
+  if (batch <= 0 || hq <= 0 || seqlen <= 0) return 0;
+  return (size_t)4 * (size_t)batch * (size_t)hq * (size_t)seqlen;
+}
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
+                     int seqlen, int head_dim, int causal, const int32_t* cu_seqlens, int num_seqs, float scale,
+                     attn_stream_t stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  attn_status st = check_common(batch, hq, hkv, seqlen, head_dim, causal, cu_seqlens, num_seqs, scale);
+  if (st != ATTN_OK) return st;
+  if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  mi355attn::FwdParams p{};
+  p.q = static_cast<const __bf16*>(q);
+  p.k = static_cast<const __bf16*>(k);
+  p.v = static_cast<const __bf16*>(v);
+  p.o = static_cast<__bf16*>(o);
+  p.lse = lse;
+  p.cu_seqlens = cu_seqlens;
+  p.num_seqs = num_seqs;
+  p.batch = batch;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.seqlen = seqlen;
+  p.head_dim = head_dim;
+  p.causal = causal;
+  p.scale = scale;
+  p.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  return launch_result(mi355attn::run_fwd_bf16(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* descale_q,
+                         const float* descale_k, const float* descale_v, void* o, float* lse, int batch, int hq,
+                         int hkv, int seqlen, int head_dim, int causal, const int32_t* cu_seqlens, int num_seqs,
+                         float scale, attn_stream_t stream) {
+  if (!q8 || !k8 || !v8 || !descale_q || !descale_k || !descale_v || !o || !lse) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o) || !aligned16(lse))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(descale_q) & 3u) || (reinterpret_cast<uintptr_t>(descale_k) & 3u) ||
+      (reinterpret_cast<uintptr_t>(descale_v) & 3u))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  attn_status st = check_common(batch, hq, hkv, seqlen, head_dim, causal, cu_seqlens, num_seqs, scale);
+  if (st != ATTN_OK) return st;
+  if (head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  mi355attn::Fp8FwdParams p{};
+  p.q = static_cast<const uint8_t*>(q8);
+  p.k = static_cast<const uint8_t*>(k8);
+  p.v = static_cast<const uint8_t*>(v8);
+  p.descale_q = descale_q;
+  p.descale_k = descale_k;
+  p.descale_v = descale_v;
+  p.o = static_cast<__bf16*>(o);
+  p.lse = lse;
+  p.cu_seqlens = cu_seqlens;
+  p.num_seqs = num_seqs;
+  p.batch = batch;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.seqlen = seqlen;
+  p.head_dim = head_dim;
+  p.causal = causal;
+  p.scale = scale;
+  return launch_result(mi355attn::run_fwd_fp8(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                     void* dq, void* dk, void* dv, void* workspace, int batch, int hq, int hkv, int seqlen,
+                     int head_dim, int causal, const int32_t* cu_seqlens, int num_seqs, float scale,
+                     attn_stream_t stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return ATTN_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, workspace};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return ATTN_ERR_INVALID_ARGUMENT;
+  attn_status st = check_common(batch, hq, hkv, seqlen, head_dim, causal, cu_seqlens, num_seqs, scale);
+  if (st != ATTN_OK) return st;
+  if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  mi355attn::BwdParams p{};
+  p.q = static_cast<const __bf16*>(q);
+  p.k = static_cast<const __bf16*>(k);
+  p.v = static_cast<const __bf16*>(v);
+  p.o = static_cast<const __bf16*>(o);
+  p.lse = lse;
+  p.dout = static_cast<const __bf16*>(dout);
+  p.dq = static_cast<__bf16*>(dq);
+  p.dk = static_cast<__bf16*>(dk);
+  p.dv = static_cast<__bf16*>(dv);
+  p.delta = static_cast<float*>(workspace);
+  p.cu_seqlens = cu_seqlens;
+  p.num_seqs = num_seqs;
+  p.batch = batch;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.seqlen = seqlen;
+  p.head_dim = head_dim;
+  p.causal = causal;
+  p.scale = scale;
+  p.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  return launch_result(mi355attn::run_bwd(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,180 @@
+// Device-side building blocks shared by the gfx950 attention kernels.
+//
+// MFMA operand layouts (v_mfma_f32_32x32x16_bf16, wave64), checked on gfx950:
+//   A (32 x 16): lane l holds row l % 32, k = 8 * (l / 32) + 0..7
+//   B (16 x 32): lane l holds column l % 32, k = 8 * (l / 32) + 0..7
+//   C (32 x 32): lane l holds column l % 32, rows 8 * (r / 4) + 4 * (l / 32) + r % 4, r = 0..15
+// The k order inside one product is free as long as A and B agree, which the
+// kernels use to permute keys so that a score tile in C layout can feed the
+// next product as its B operand without any data movement.
+//
+// ds_read_b64_tr_b16 (transposing LDS read), checked on gfx950: in each group
+// of 16 lanes, source lane 16g + j supplies the address of 4 consecutive
+// 16-bit elements; destination lane 16g + t receives element t % 4 of the
+// sources 16g + t / 4 + 4e, e = 0..3 (in that order).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi355attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// A running row maximum below any real scaled score; exp2(-1e30 - x) == 0.
+constexpr float kMaxInit = -1.0e30f;
+// The running maximum used for exponentiation is only moved when the tile
+// maximum exceeds it by more than this (log2 units). Probabilities are then
+// at most 2^8 before normalisation, well inside fp32 and bf16 range; the
+// final division uses the same offset, so the result is unchanged.
+constexpr float kRescaleThreshold = 8.0f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_max_halves(float x) {
+  // lanes l and l ^ 32 hold the same query column
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+// Swap bits 2 and 3 of a row index in [0, 32): the K (or Q, dO) row a lane
+// loads for the score product, so that C-layout register r of lane half h
+// holds key 16 * (r / 8) + 8 * h + r % 8.
+__device__ __forceinline__ int perm_rows(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// Key offset (within a 32-key block) of C-layout register r of lane half h
+// when the rows were loaded through perm_rows.
+__device__ __forceinline__ int c_key(int r, int h) { return 16 * (r >> 3) + 8 * h + (r & 7); }
+
+// ---------------------------------------------------------------------------
+// LDS tile layouts: row-major [rows][D] bf16 with XOR swizzles.
+//
+// "B128" tiles are read with 16-byte reads: lane l reads row perm_rows(l % 32)
+// (+32 per block) at chunk 2t + l / 32. The swizzle permutes 16-byte chunks
+// so that any 8 or 16 consecutive lanes hit distinct banks.
+// "TR" tiles are read with transposing 8-byte reads (4 rows x 16 columns per
+// 16 lanes). The swizzle permutes 8-byte units with a 4-row period.
+// Both swizzles keep each 16-byte chunk contiguous, so tiles are written with
+// 16-byte stores.
+// ---------------------------------------------------------------------------
+
+template <int D>
+__device__ __forceinline__ int swz_b128(int row, int chunk) {
+  if constexpr (D == 128) {
+    const int f = (row & 3) | (((row >> 3) & 1) << 2) | (((row >> 2) & 1) << 3);
+    return chunk ^ f;
+  } else {
+    const int f = ((row >> 1) & 1) | (((row >> 3) & 1) << 1) | (((row ^ (row >> 2)) & 1) << 2);
+    return chunk ^ f;
+  }
+}
+
+// 8-byte unit XOR pattern for TR tiles, in units of 16-byte chunks (>> 1).
+template <int D>
+__device__ __forceinline__ int swz_tr_chunk(int row, int chunk) {
+  // unit XOR table {0, 12, 24, 20} (8-byte units), halved to 16-byte chunks
+  const int t = row & 3;
+  int x = (t == 0) ? 0 : (t == 1) ? 6 : (t == 2) ? 12 : 10;
+  if constexpr (D == 64) x &= 7;
+  return chunk ^ x;
+}
+
+// Element offset of (row, 16-byte chunk) in a tile.
+template <int D>
+__device__ __forceinline__ int off_b128(int row, int chunk) { return row * D + swz_b128<D>(row, chunk) * 8; }
+template <int D>
+__device__ __forceinline__ int off_tr(int row, int chunk) { return row * D + swz_tr_chunk<D>(row, chunk) * 8; }
+
+// Element offset of (row, 8-byte unit) in a TR tile.
+template <int D>
+__device__ __forceinline__ int off_tr_unit(int row, int unit) {
+  return row * D + swz_tr_chunk<D>(row, unit >> 1) * 8 + (unit & 1) * 4;
+}
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const __bf16* base, int elem_off) {
+  return *LDS_PTR(const bf16x8, base + elem_off);
+}
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* base, int elem_off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, const_cast<__bf16*>(base) + elem_off));
+}
+
+// A-operand fragment of the transposed tile X^T (m = column of X, k = 8 rows of X):
+// lane l gets X[row0 + 8 * (l / 32) + 0..7][col0 + l % 32] from a TR tile.
+// row0 must be a multiple of 16 and col0 a multiple of 32.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_fragment(const __bf16* tile, int row0, int col0, int lane) {
+  const int r = row0 + 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const int unit = (col0 >> 2) + 4 * ((lane >> 4) & 1) + (lane & 3);
+  const bf16x4 lo = lds_read_tr(tile, off_tr_unit<D>(r, unit));
+  const bf16x4 hi = lds_read_tr(tile, off_tr_unit<D>(r + 4, unit));
+  bf16x8 out;
+  out[0] = lo[0]; out[1] = lo[1]; out[2] = lo[2]; out[3] = lo[3];
+  out[4] = hi[0]; out[5] = hi[1]; out[6] = hi[2]; out[7] = hi[3];
+  return out;
+}
+
+__device__ __forceinline__ u32x4 load16(const __bf16* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x4 load16_pred(const __bf16* p, bool ok) {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return ok ? *reinterpret_cast<const u32x4*>(p) : z;
+}
+__device__ __forceinline__ void lds_store16(__bf16* base, int elem_off, u32x4 v) {
+  *LDS_PTR(u32x4, base + elem_off) = v;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Eight fp32 values -> bf16x8, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x8 pack_bf16(float a0, float a1, float a2, float a3, float a4, float a5,
+                                            float a6, float a7) {
+  bf16x8 o;
+  o[0] = (__bf16)a0; o[1] = (__bf16)a1; o[2] = (__bf16)a2; o[3] = (__bf16)a3;
+  o[4] = (__bf16)a4; o[5] = (__bf16)a5; o[6] = (__bf16)a6; o[7] = (__bf16)a7;
+  return o;
+}
+
+// Segment [start, end) of token i for packed sequences (binary search over
+// the prefix sums cu[0..n]); the whole sequence when cu is null.
+__device__ __forceinline__ void segment_of(const int32_t* cu, int n, int seqlen, int i, int& start, int& end) {
+  if (cu == nullptr) {
+    start = 0;
+    end = seqlen;
+    return;
+  }
+  int lo = 0, hi = n;  // invariant: cu[lo] <= i < cu[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= i) lo = mid; else hi = mid;
+  }
+  start = cu[lo];
+  end = cu[hi];
+}
+
+__device__ __forceinline__ int wave_min(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = min(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o));
+  return x;
+}
+
+}  // namespace mi355attn

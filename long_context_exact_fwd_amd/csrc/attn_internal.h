@@ -1,0 +1,66 @@
+// Internal interface between the C ABI layer (attn_api.hip) and the kernel
+// files. Argument checking happens before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi355attn {
+
+struct FwdParams {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  __bf16* o;
+  float* lse;
+  const int32_t* cu_seqlens;  // null when not packed
+  int num_seqs;
+  int batch, hq, hkv, seqlen, head_dim;
+  int causal;
+  float scale;
+  float scale_log2e;  // scale * log2(e)
+  int num_qblk;       // set by the launcher
+};
+
+struct Fp8FwdParams {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const float* descale_q;
+  const float* descale_k;
+  const float* descale_v;
+  __bf16* o;
+  float* lse;
+  const int32_t* cu_seqlens;
+  int num_seqs;
+  int batch, hq, hkv, seqlen, head_dim;
+  int causal;
+  float scale;
+  int num_qblk;
+};
+
+struct BwdParams {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* o;
+  const float* lse;
+  const __bf16* dout;
+  __bf16* dq;
+  __bf16* dk;
+  __bf16* dv;
+  float* delta;  // workspace [B, Hq, S]
+  const int32_t* cu_seqlens;
+  int num_seqs;
+  int batch, hq, hkv, seqlen, head_dim;
+  int causal;
+  float scale;
+  float scale_log2e;
+  int num_blk;  // set by the launchers
+};
+
+hipError_t run_fwd_bf16(const FwdParams& p, hipStream_t stream);
+hipError_t run_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream);
+hipError_t run_bwd(const BwdParams& p, hipStream_t stream);
+
+}  // namespace mi355attn

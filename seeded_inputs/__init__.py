@@ -185,8 +185,11 @@ class Inputs:
 
 def make_inputs(batch: int, hq: int, hkv: int, seqlen: int, head_dim: int, seed: int,
                 lengths=None, random_lengths: bool = False, fp8: bool = False,
-                with_do: bool = True, std: float = 1.0) -> Inputs:
-    """Draw Q, K, V, dO ~ N(0, std^2) in [B, S, H, D] and round them to the kernel formats."""
+                with_do: bool = True, qk_std: float = 1.0) -> Inputs:
+    """Draw Q, K, V, dO ~ N(0, 1) in [B, S, H, D] and round them to the kernel formats.
+
+    ``qk_std`` multiplies Q and K only (sharper softmax rows, V unchanged).
+    """
     rng = np.random.default_rng(seed)
     cu = None
     if random_lengths:
@@ -200,10 +203,9 @@ def make_inputs(batch: int, hq: int, hkv: int, seqlen: int, head_dim: int, seed:
     q = rng.standard_normal((batch, seqlen, hq, head_dim), dtype=np.float32)
     k = rng.standard_normal((batch, seqlen, hkv, head_dim), dtype=np.float32)
     v = rng.standard_normal((batch, seqlen, hkv, head_dim), dtype=np.float32)
-    if std != 1.0:
-        q *= np.float32(std)
-        k *= np.float32(std)
-        v *= np.float32(std)
+    if qk_std != 1.0:
+        q *= np.float32(qk_std)
+        k *= np.float32(qk_std)
     do = rng.standard_normal((batch, seqlen, hq, head_dim), dtype=np.float32) if with_do else None
     if fp8:
         q8, dq = e4m3_quantize(q)
