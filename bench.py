@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Attention TFLOP/s for causal bf16 fwd+bwd at S=32768, D=128 on one MI355X.
+
+One step is the whole hot path on one batch of synthetic input that already
+sits in HBM: attn_fwd, then the three backward kernels (Delta, dK/dV, dQ)
+through attn_bwd_phases. That is the same work attn_bwd does, split so each
+kernel can be bracketed with HIP events on the stream it runs on.
+
+Workload (one GPU's Ulysses head share of a Qwen2.5-7B-shaped layer): B=1,
+Hq=28, Hkv=4, S=32768, D=128, causal, bf16 inputs drawn N(0, 1) from seed 3.
+
+FLOPs are algorithmic: only visible (i, j) pairs count, 4*D per pair for the
+forward (QK^T and PV) and 10*D per pair for the backward (QK^T, dO V^T,
+P^T dO, dS K, dS^T Q). The dQ kernel's second recompute of QK^T and dO V^T is
+not counted. Per kernel: fwd 4*D, dK/dV 8*D, dQ 2*D per pair.
+
+Prints one JSON line. The roofline object describes the kernel with the
+largest share of the step time. ``cpu_baseline`` times the fp64 oracle on a
+bounded sample of the same workload on the host cores.
+
+    python bench.py [--steps 20] [--warmup 3] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
+PEAK_HBM_GBS = 8000.0
+
+
+def _pairs(seqlen: int, causal: bool, cu=None) -> float:
+    if cu is not None:
+        lens = [int(b) - int(a) for a, b in zip(cu[:-1], cu[1:])]
+        return float(sum(L * (L + 1) // 2 if causal else L * L for L in lens))
+    return seqlen * (seqlen + 1) / 2.0 if causal else float(seqlen) * seqlen
+
+
+KERNEL_SOURCES = {
+    "attn_fwd_bf16_kernel": ("attn_fwd.hip", "attn_device.h", "attn_internal.h"),
+    "attn_bwd_dkdv_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h"),
+    "attn_bwd_dq_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h"),
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the source files a kernel is built from (counter records go stale when it changes)."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "long_context_exact_fwd_amd", "csrc", name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel: str):
+    """HBM bytes per launch from the committed counter record, if the kernel's sources are unchanged."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path, encoding="utf-8") as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if not k or k.get("source_hash") != kernel_source_hash(kernel):
+        return None
+    return k.get("bytes_per_launch")
+
+
+def cpu_baseline(w, x, sample_len: int):
+    """Oracle (fp64, numpy) fwd+bwd of one kv group over a causal prefix of the same inputs."""
+    import numpy as np
+    import oracle
+    workers = min(16, len(os.sched_getaffinity(0)))
+    L = min(sample_len, w.seqlen)
+    g = w.hq // w.hkv
+    q = x.values("q")[:, :L, :g]
+    k = x.values("k")[:, :L, :1]
+    v = x.values("v")[:, :L, :1]
+    do = x.values("do")[:, :L, :g]
+    t0 = time.perf_counter()
+    oracle.attention_bwd_group(q, k, v, do, b=0, kv_head=0, causal=w.causal, scale=w.scale, workers=workers)
+    dt = time.perf_counter() - t0
+    flops = 14.0 * w.head_dim * _pairs(L, w.causal) * g
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle fwd+bwd (attention_bwd_group) of one kv group ({g} query heads) over the "
+                   f"first {L} tokens of the same seeded inputs, causal; {dt:.1f} s on {workers} threads; "
+                   f"flops counted as for the GPU (14*D per visible pair)"),
+        "seconds": dt,
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gqa32k")
+    ap.add_argument("--cpu-sample-len", type=int, default=32768)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the timed region, run one plain device copy of this many MiB (counter calibration)")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py: only one GPU is supported by this build (got --gpus {a.gpus}); the kernels run one GPU's "
+              f"head share and no collectives are implemented", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import seeded_inputs as si
+    import long_context_exact_fwd_amd as lca
+
+    w = si.WORKLOADS[a.workload]
+    if w.fp8 or not w.backward:
+        print("bench.py: the headline step is bf16 fwd+bwd; pick a workload with a backward", file=sys.stderr)
+        return 2
+    lib = lca.load_library()
+    x = si.workload_inputs(w)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    up = lca.bf16_from_bits
+    q, k, v, do = up(x.q_bits), up(x.k_bits), up(x.v_bits), up(x.do_bits)
+    cu = torch.from_numpy(x.cu_seqlens).to(dev) if x.cu_seqlens is not None else None
+    B, S, Hq, Hkv, D = w.batch, w.seqlen, w.hq, w.hkv, w.head_dim
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(lca.bwd_workspace_bytes(B, Hq, S) // 4, dtype=torch.float32, device=dev)
+    kw = dict(causal=w.causal, cu_seqlens=cu, scale=w.scale)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        lca.fwd(q, k, v, out=o, lse=lse, **kw)
+        if ev is not None:
+            ev[1].record()
+        lca.bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, phases=lca.BWD_DELTA, **kw)
+        if ev is not None:
+            ev[2].record()
+        lca.bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, phases=lca.BWD_DKDV, **kw)
+        if ev is not None:
+            ev[3].record()
+        lca.bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, phases=lca.BWD_DQ, **kw)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"bench: warmup {a.warmup} done, timing {a.steps} steps", file=sys.stderr, flush=True)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(a.steps):
+        step(evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / a.steps
+    names = ["attn_fwd", "bwd_delta", "bwd_dkdv", "bwd_dq"]
+    per = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / a.steps for j, n in enumerate(names)}
+
+    pairs = _pairs(S, w.causal, x.cu_seqlens) * B * Hq
+    flops_k = {"attn_fwd": 4.0 * D * pairs, "bwd_delta": 0.0, "bwd_dkdv": 8.0 * D * pairs, "bwd_dq": 2.0 * D * pairs}
+    step_flops = 14.0 * D * pairs
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    dom = max(("attn_fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: per[n])
+    achieved = flops_k[dom] / (per[dom] * 1e-3) / 1e12
+    kernel_names = {"attn_fwd": "attn_fwd_bf16_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel",
+                    "bwd_dq": "attn_bwd_dq_kernel"}
+    roofline = {
+        "bound": "mfma",
+        "kernel": kernel_names[dom],
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": _traffic(kernel_names[dom]),
+        "avg_launch_ms": round(per[dom], 4),
+        "algorithmic_flops_per_launch": flops_k[dom],
+    }
+
+    if a.calib_copy_mib > 0:
+        n = a.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    result = {
+        "metric": "attention TFLOP/s fwd+bwd (causal bf16, S=32K, D=128) and % of MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} causal={w.causal} packed={w.packed}, "
+                        f"N(0,1) seed {w.seed}",
+            "batch": B, "hq": Hq, "hkv": Hkv, "seq_len": S, "head_dim": D, "causal": w.causal,
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "phases_ms": {n: round(t, 4) for n, t in per.items()},
+        "wall_s_timed": round(wall, 3),
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu_baseline:
+        print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, x, a.cpu_sample_len)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -116,6 +116,23 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      int causal, const int32_t* cu_seqlens, int num_seqs,
                      float scale, attn_stream_t stream);
 
+/* One or more of the three backward kernels, in the fixed order Delta, dK/dV,
+ * dQ: attn_bwd(...) is attn_bwd_phases(ATTN_BWD_ALL, ...). Running the
+ * phases as separate calls on one stream (Delta first) gives bitwise the
+ * same result. It exists so that callers and profilers can time or schedule
+ * each kernel on its own. Arguments as attn_bwd. dK/dV and dQ read the Delta
+ * that an earlier ATTN_BWD_DELTA call left in `workspace`.
+ * phases: nonzero bitmask of the values below; other bits are invalid. */
+#define ATTN_BWD_DELTA 1u
+#define ATTN_BWD_DKDV 2u
+#define ATTN_BWD_DQ 4u
+#define ATTN_BWD_ALL 7u
+attn_status attn_bwd_phases(unsigned phases, const void* q, const void* k, const void* v, const void* o,
+                            const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                            int batch, int hq, int hkv, int seqlen, int head_dim,
+                            int causal, const int32_t* cu_seqlens, int num_seqs,
+                            float scale, attn_stream_t stream);
+
 /* Static string naming a status code ("ATTN_OK", ...). Never NULL. */
 const char* attn_status_str(attn_status s);
 

@@ -49,6 +49,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_fwd_fp8.restype = i
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, f, st]
     lib.attn_bwd.restype = i
+    lib.attn_bwd_phases.argtypes = [ctypes.c_uint, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i,
+                                    f, st]
+    lib.attn_bwd_phases.restype = i
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_status_str.argtypes = [i]
@@ -60,8 +63,18 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     return lib
 
 
-EXPORTED = ("attn_fwd", "attn_fwd_fp8", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str",
-            "attn_last_hip_error")
+EXPORTED = ("attn_fwd", "attn_fwd_fp8", "attn_bwd", "attn_bwd_phases", "attn_bwd_workspace_bytes",
+            "attn_status_str", "attn_last_hip_error")
+
+BWD_DELTA, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
+
+
+def bf16_from_bits(bits, device="cuda"):
+    """Device bfloat16 tensor from a numpy array of bf16 bit patterns (uint16)."""
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(bits).view(np.int16)
+    return torch.from_numpy(a).view(torch.bfloat16).to(device)
 
 
 def _check(status: int, what: str) -> None:
@@ -143,8 +156,12 @@ def bwd_workspace_bytes(batch: int, hq: int, seqlen: int) -> int:
 
 
 def bwd(q, k, v, o, lse, do, *, causal: bool, cu_seqlens=None, scale: Optional[float] = None, workspace=None,
-        dq=None, dk=None, dv=None):
-    """Backward, bf16. Returns (dq, dk, dv) shaped like q, k, v."""
+        dq=None, dk=None, dv=None, phases: Optional[int] = None):
+    """Backward, bf16. Returns (dq, dk, dv) shaped like q, k, v.
+
+    ``phases`` (bitmask of BWD_DELTA, BWD_DKDV, BWD_DQ) runs only those kernels
+    through attn_bwd_phases; the default runs attn_bwd (all three).
+    """
     import torch
     _check_tensors(q, k, v, o, do, dtype=torch.bfloat16)
     _check_tensors(lse, dtype=torch.float32)
@@ -157,8 +174,10 @@ def bwd(q, k, v, o, lse, do, *, causal: bool, cu_seqlens=None, scale: Optional[f
     if workspace is None:
         nbytes = bwd_workspace_bytes(B, Hq, S)
         workspace = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=q.device)
-    st = load_library().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
-                                 _ptr(dv), _ptr(workspace), B, Hq, Hkv, S, D, int(bool(causal)), _ptr(cu_seqlens), n,
-                                 float(scale), _stream())
-    _check(st, "attn_bwd")
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+            B, Hq, Hkv, S, D, int(bool(causal)), _ptr(cu_seqlens), n, float(scale), _stream())
+    if phases is None:
+        _check(load_library().attn_bwd(*args), "attn_bwd")
+    else:
+        _check(load_library().attn_bwd_phases(int(phases), *args), "attn_bwd_phases")
     return dq, dk, dv

@@ -126,10 +126,11 @@ attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const f
   return launch_result(mi355attn::run_fwd_fp8(p, reinterpret_cast<hipStream_t>(stream)));
 }
 
-attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                     void* dq, void* dk, void* dv, void* workspace, int batch, int hq, int hkv, int seqlen,
-                     int head_dim, int causal, const int32_t* cu_seqlens, int num_seqs, float scale,
-                     attn_stream_t stream) {
+attn_status attn_bwd_phases(unsigned phases, const void* q, const void* k, const void* v, const void* o,
+                            const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                            int batch, int hq, int hkv, int seqlen, int head_dim, int causal,
+                            const int32_t* cu_seqlens, int num_seqs, float scale, attn_stream_t stream) {
+  if (phases == 0u || (phases & ~7u) != 0u) return ATTN_ERR_INVALID_ARGUMENT;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return ATTN_ERR_INVALID_ARGUMENT;
   const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, workspace};
   for (const void* ptr : ptrs)
@@ -158,7 +159,15 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
   p.causal = causal;
   p.scale = scale;
   p.scale_log2e = (float)((double)scale * 1.4426950408889634);
-  return launch_result(mi355attn::run_bwd(p, reinterpret_cast<hipStream_t>(stream)));
+  return launch_result(mi355attn::run_bwd(p, phases, reinterpret_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                     void* dq, void* dk, void* dv, void* workspace, int batch, int hq, int hkv, int seqlen,
+                     int head_dim, int causal, const int32_t* cu_seqlens, int num_seqs, float scale,
+                     attn_stream_t stream) {
+  return attn_bwd_phases(ATTN_BWD_ALL, q, k, v, o, lse, dout, dq, dk, dv, workspace, batch, hq, hkv, seqlen, head_dim,
+                         causal, cu_seqlens, num_seqs, scale, stream);
 }
 
 }  // extern "C"

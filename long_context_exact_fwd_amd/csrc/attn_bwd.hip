@@ -495,8 +495,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdParams p) {
 }
 
 template <int D, int NWK, int NWQ, bool CAUSAL>
-hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
-  {
+hipError_t launch_bwd(const BwdParams& p, unsigned phases, hipStream_t stream) {
+  if (phases & kBwdDelta) {
     constexpr int RPB = 256 / (D / 8);
     const long nrows = (long)p.batch * p.seqlen * p.hq;
     dim3 grid((unsigned)((nrows + RPB - 1) / RPB));
@@ -504,7 +504,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
+  if (phases & kBwdDkDv) {
     BwdParams q = p;
     q.num_blk = (p.seqlen + 32 * NWK - 1) / (32 * NWK);
     dim3 grid(p.batch * p.hkv, q.num_blk);
@@ -512,22 +512,25 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
+  if (phases & kBwdDq) {
     BwdParams q = p;
     q.num_blk = (p.seqlen + 32 * NWQ - 1) / (32 * NWQ);
     dim3 grid(p.batch * p.hq, q.num_blk);
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, NWQ, CAUSAL>), grid, dim3(NWQ * 64), 0, stream, q);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
+  return hipSuccess;
 }
 
 }  // namespace
 
-hipError_t run_bwd(const BwdParams& p, hipStream_t stream) {
+hipError_t run_bwd(const BwdParams& p, unsigned phases, hipStream_t stream) {
   if (p.head_dim == 128) {
-    return p.causal ? launch_bwd<128, 4, 4, true>(p, stream) : launch_bwd<128, 4, 4, false>(p, stream);
+    return p.causal ? launch_bwd<128, 4, 4, true>(p, phases, stream)
+                    : launch_bwd<128, 4, 4, false>(p, phases, stream);
   }
-  return p.causal ? launch_bwd<64, 4, 4, true>(p, stream) : launch_bwd<64, 4, 4, false>(p, stream);
+  return p.causal ? launch_bwd<64, 4, 4, true>(p, phases, stream) : launch_bwd<64, 4, 4, false>(p, phases, stream);
 }
 
 }  // namespace mi355attn

@@ -61,6 +61,7 @@ struct BwdParams {
 
 hipError_t run_fwd_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t run_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream);
-hipError_t run_bwd(const BwdParams& p, hipStream_t stream);
+constexpr unsigned kBwdDelta = 1u, kBwdDkDv = 2u, kBwdDq = 4u;
+hipError_t run_bwd(const BwdParams& p, unsigned phases, hipStream_t stream);
 
 }  // namespace mi355attn

@@ -3,8 +3,8 @@ import numpy as np
 
 
 def dev_bf16(bits: np.ndarray):
-    import torch
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    import long_context_exact_fwd_amd as lca
+    return lca.bf16_from_bits(bits, "cuda")
 
 
 def dev_u8(codes: np.ndarray):
