@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mi355attn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -49,6 +51,21 @@ __device__ __forceinline__ float wave_max_halves(float x) {
   // lanes l and l ^ 32 hold the same query column
   return fmaxf(x, __shfl_xor(x, 32));
 }
+
+// v_permlane32_swap exchanges the upper half of one copy of x with the lower
+// half of another, so the two results hold, lane by lane, x[l] and x[l ^ 32]
+// (in one order or the other). A commutative combination of the two is the
+// same in every lane of a pair, whichever way round the halves come back.
+__device__ __forceinline__ float max_lane_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_lane_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // Swap bits 2 and 3 of a row index in [0, 32): the K (or Q, dO) row a lane
 // loads for the score product, so that C-layout register r of lane half h
@@ -88,8 +105,8 @@ __device__ __forceinline__ int swz_b128(int row, int chunk) {
 template <int D>
 __device__ __forceinline__ int swz_tr_chunk(int row, int chunk) {
   // unit XOR table {0, 12, 24, 20} (8-byte units), halved to 16-byte chunks
-  const int t = row & 3;
-  int x = (t == 0) ? 0 : (t == 1) ? 6 : (t == 2) ? 12 : 10;
+  // {0, 6, 12, 10}, looked up by shifting a packed byte table (no branches)
+  int x = (0x0A0C0600 >> (8 * (row & 3))) & 0xFF;
   if constexpr (D == 64) x &= 7;
   return chunk ^ x;
 }
@@ -128,6 +145,37 @@ __device__ __forceinline__ bf16x8 tr_fragment(const __bf16* tile, int row0, int 
   out[4] = hi[0]; out[5] = hi[1]; out[6] = hi[2]; out[7] = hi[3];
   return out;
 }
+
+// Two transposing reads, 4 rows apart in a TR tile: elem_off is the first
+// read's offset and row_delta the element distance of the second.
+__device__ __forceinline__ bf16x8 tr_read_pair(const __bf16* tile, int elem_off, int row_delta) {
+  const bf16x4 lo = lds_read_tr(tile, elem_off);
+  const bf16x4 hi = lds_read_tr(tile, elem_off + row_delta);
+  bf16x8 out;
+  out[0] = lo[0]; out[1] = lo[1]; out[2] = lo[2]; out[3] = lo[3];
+  out[4] = hi[0]; out[5] = hi[1]; out[6] = hi[2]; out[7] = hi[3];
+  return out;
+}
+
+// Direct global -> LDS copy (global_load_lds_dwordx4): lane L of the wave
+// copies 16 bytes from g into lds_wave_base + 16 L. lds_wave_base must be the
+// same for every lane of the wave (it goes to M0). Completion is tracked by
+// vmcnt, so wait_dma() must precede the barrier after which the data is read.
+__device__ __forceinline__ void dma16(const void* g, const void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, LDS_PTR(void, const_cast<void*>(lds_wave_base)), 16, 0, 0);
+}
+// Buffer resource over [base, base + nbytes) (raw, stride 0): a load whose
+// per-lane offset is past nbytes returns zeros, which handles ragged tails.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
+}
+// buffer_load_dwordx4 ... lds: lane L copies 16 bytes at byte offset voff of
+// the buffer into lds_wave_base + 16 L (same M0 rule as dma16).
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, const void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, const_cast<void*>(lds_wave_base)), 16, voff, 0, 0, 0);
+}
+// s_waitcnt vmcnt(0), other counters left alone (expcnt 7, lgkmcnt 15).
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ u32x4 load16(const __bf16* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x4 load16_pred(const __bf16* p, bool ok) {

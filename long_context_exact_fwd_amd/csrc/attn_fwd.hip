@@ -7,16 +7,21 @@
 // log-sum-exp) reach global memory. The FA-2 paragraph of the same page names
 // double-buffered loads; here K and V tiles are double-buffered through LDS.
 //
-// Work split (one workgroup per (b, h_q, block of 32*NW queries)):
-//   * each wave owns 32 queries; its Q slice sits in VGPRs as the B operand
-//     of S^T = K Q^T (32 keys x 32 queries per MFMA block), so every lane owns
-//     one query column and the row statistics need no cross-lane work except
-//     one exchange between the two lane halves;
-//   * K rows are loaded through perm_rows, which puts the probabilities in
-//     exactly the register order the B operand of O^T += V^T P^T needs;
-//   * V^T fragments come from the transposing LDS read, so V stays row-major;
-//   * 64-key tiles; tiles entirely outside a wave's visible keys are skipped,
-//     tiles partly outside are masked per element.
+// Work split: one workgroup of 4 waves per (b, h_q, 128 queries), two
+// workgroups per CU (two waves per SIMD, so one wave's softmax overlaps the
+// other's MFMAs; at most 256 VGPRs each).
+//   * Each wave owns 32 queries. Its Q slice sits in VGPRs as the B operand of
+//     S^T = K Q^T, so every lane owns one query column and the row statistics
+//     need only one exchange between the two lane halves (v_permlane32_swap).
+//   * K rows are read through perm_rows, which leaves the probabilities in
+//     exactly the register order the B operand of O^T += V^T P^T needs.
+//   * V^T fragments come from the transposing LDS read; V stays row-major.
+//   * K/V tiles (64 keys) move from global memory straight into LDS
+//     (buffer_load_dwordx4 ... lds, no staging registers), double-buffered
+//     with one barrier per tile.
+//   * Tiles outside a wave's visible keys are skipped, tiles partly outside
+//     are masked per element. Every LDS address is a per-lane base computed
+//     once plus a compile-time offset, and every per-tile branch is scalar.
 #include "attn_device.h"
 #include "attn_internal.h"
 
@@ -24,53 +29,26 @@ namespace mi355attn {
 
 namespace {
 
-constexpr int kBN = 64;  // keys per tile
+constexpr int kBN = 64;    // keys per tile
+constexpr int kWaves = 4;  // waves per workgroup
+constexpr int kBM = 32 * kWaves;
 
-template <int D, int NW>
-struct FwdTileLoader {
-  static constexpr int kThreads = NW * 64;
-  static constexpr int kChunks = kBN * D / 8;  // 16-byte chunks per tile
-  static constexpr int kPer = kChunks / kThreads;
-  static_assert(kChunks % kThreads == 0, "tile chunks must divide evenly");
-  u32x4 k[kPer], v[kPer];
-
-  __device__ __forceinline__ void load(const __bf16* kg, const __bf16* vg, int row_stride, int t0, int seqlen,
-                                       int tid) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int idx = tid + i * kThreads;
-      const int row = idx / (D / 8);
-      const int ch = idx % (D / 8);
-      const int g = t0 + row;
-      const bool ok = g < seqlen;
-      const size_t off = (size_t)(ok ? g : 0) * row_stride + ch * 8;
-      k[i] = load16_pred(kg + off, ok);
-      v[i] = load16_pred(vg + off, ok);
-    }
-  }
-  __device__ __forceinline__ void store(__bf16* ks, __bf16* vs, int tid) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int idx = tid + i * kThreads;
-      const int row = idx / (D / 8);
-      const int ch = idx % (D / 8);
-      lds_store16(ks, off_b128<D>(row, ch), k[i]);
-      lds_store16(vs, off_tr<D>(row, ch), v[i]);
-    }
-  }
-};
-
-template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(FwdParams p) {
-  constexpr int BM = 32 * NW;
-  constexpr int KS = D / 16;  // k-steps of the score product
-  constexpr int DB = D / 32;  // 32-wide d blocks of the output
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][kBN * D];
-  __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][kBN * D];
-  __shared__ int red[4][NW];
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_bf16_kernel(FwdParams p) {
+  constexpr int KS = D / 16;     // k-steps of the score product
+  constexpr int DB = D / 32;     // 32-wide d blocks of the output
+  constexpr int TILE = kBN * D;  // elements of one K or V tile
+  constexpr int NI = TILE * 2 / (kWaves * 1024);  // DMA instructions per wave per tensor and tile
+  // The two buffers are separate objects so that alias analysis can tell the
+  // reads of one from the DMA writes into the other (no waits between them).
+  __shared__ __attribute__((aligned(1024))) __bf16 k_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 k_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_lds1[TILE];
+  __shared__ int red[2][kWaves];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int n = lane & 31;
   const int h = lane >> 5;
@@ -80,8 +58,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(FwdParams p) {
   const int hq = bh - b * p.hq;
   const int hk = hq / (p.hq / p.hkv);
   const int qblk = p.num_qblk - 1 - (int)blockIdx.y;  // heaviest blocks first
-  const int q0 = qblk * BM;
-  const int my_q = q0 + wave * 32 + n;
+  const int my_q = qblk * kBM + wave * 32 + n;
   const bool q_ok = my_q < p.seqlen;
 
   const int q_stride = p.hq * D;
@@ -98,10 +75,13 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(FwdParams p) {
     kstart = s0;
     kend = CAUSAL ? my_q + 1 : s1;
   }
-  const int lo_min = wave_min(q_ok ? kstart : INT32_MAX);
-  const int hi_max = wave_max(q_ok ? kend : INT32_MIN);
-  const int lo_max = wave_max(q_ok ? kstart : INT32_MIN);
-  const int hi_min = wave_min(q_ok ? kend : INT32_MAX);
+  // Wave bounds: a tile is skipped when it misses every visible range of the
+  // wave and unmasked when it lies inside all of them. The reductions are
+  // wave-uniform; readfirstlane says so, which keeps the tile branches scalar.
+  const int lo_min = __builtin_amdgcn_readfirstlane(wave_min(q_ok ? kstart : INT32_MAX));
+  const int hi_max = __builtin_amdgcn_readfirstlane(wave_max(q_ok ? kend : INT32_MIN));
+  const int lo_max = __builtin_amdgcn_readfirstlane(wave_max(q_ok ? kstart : INT32_MIN));
+  const int hi_min = __builtin_amdgcn_readfirstlane(wave_min(q_ok ? kend : INT32_MAX));
   if (lane == 0) {
     red[0][wave] = lo_min;
     red[1][wave] = hi_max;
@@ -109,20 +89,62 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(FwdParams p) {
   __syncthreads();
   int wg_lo = INT32_MAX, wg_hi = INT32_MIN;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
+  for (int w = 0; w < kWaves; ++w) {
     wg_lo = min(wg_lo, red[0][w]);
     wg_hi = max(wg_hi, red[1][w]);
   }
+  wg_lo = __builtin_amdgcn_readfirstlane(wg_lo);
+  wg_hi = __builtin_amdgcn_readfirstlane(wg_hi);
   const int tile_begin = wg_hi > wg_lo ? wg_lo / kBN : 0;
   const int tile_end = wg_hi > wg_lo ? (wg_hi + kBN - 1) / kBN : 0;
 
-  // Q slice of this wave as B operands: lane (n, h) holds Q[my_q][16t + 8h .. +7]
+  // Q slice as B operands: lane (n, h) holds Q[my_q][16t + 8h .. +7]
   bf16x8 qf[KS];
   {
-    const __bf16* qrow = qg + (size_t)(q_ok ? my_q : 0) * q_stride + 8 * h;
+    const __bf16* qrow = qg + (size_t)min(my_q, p.seqlen - 1) * q_stride + 8 * h;
 #pragma unroll
-    for (int t = 0; t < KS; ++t) qf[t] = as_bf16x8(load16_pred(qrow + 16 * t, q_ok));
+    for (int t = 0; t < KS; ++t) qf[t] = as_bf16x8(load16(qrow + 16 * t));
   }
+
+  // Per-lane LDS element offsets (tile-relative).
+  int koff[KS];  // K row perm_rows(n), chunk 2t + h: A operand of S^T, key block 0
+#pragma unroll
+  for (int t = 0; t < KS; ++t) koff[t] = off_b128<D>(perm_rows(n), 2 * t + h);
+  int voff[DB];  // first transposing read of the V^T fragment (key step 0, d block db)
+  {
+    const int r0 = 8 * h + ((lane & 15) >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) voff[db] = off_tr_unit<D>(r0, 8 * db + 4 * ((lane >> 4) & 1) + (lane & 3));
+  }
+
+  // DMA tile loader. Instruction i of wave w fills the 1 KiB of LDS at
+  // (4 i + w) KiB of the tile, lane L the 16 bytes at L * 16 of it: tile row
+  // `row`, physical chunk `pc`. The lane fetches the logical chunk that the
+  // swizzle puts there (both swizzles are XORs, hence involutions). The
+  // buffer resource starts at the tile's first row and ends at the last key,
+  // so rows past the end read as zeros (their keys are masked anyway).
+  uint32_t ld_koff[NI], ld_voff[NI];  // byte offsets within the tile
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int e = (i * kWaves + wave) * 512 + lane * 8;  // element offset in the tile
+    const int row = e / D;
+    const int pc = (e % D) / 8;
+    ld_koff[i] = (uint32_t)(row * kv_stride + swz_b128<D>(row, pc) * 8) * 2u;
+    ld_voff[i] = (uint32_t)(row * kv_stride + swz_tr_chunk<D>(row, pc) * 8) * 2u;
+  }
+  auto issue_tile = [&](int t0, auto buf_c) {
+    __bf16* kd = decltype(buf_c)::value ? k_lds1 : k_lds0;
+    __bf16* vd = decltype(buf_c)::value ? v_lds1 : v_lds0;
+    const uint32_t nbytes = (uint32_t)(p.seqlen - t0) * (uint32_t)kv_stride * 2u;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)t0 * kv_stride, nbytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)t0 * kv_stride, nbytes);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int lds_el = (i * kWaves + wave) * 512;
+      dma16_buf(rk, ld_koff[i], kd + lds_el);
+      dma16_buf(rv, ld_voff[i], vd + lds_el);
+    }
+  };
 
   f32x16 acc[DB];
 #pragma unroll
@@ -131,34 +153,25 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(FwdParams p) {
   float l_run = 0.f;       // partial row sum over this lane's keys
   const float c = p.scale_log2e;
 
-  FwdTileLoader<D, NW> ld;
-  if (tile_begin < tile_end) {
-    ld.load(kg, vg, kv_stride, tile_begin * kBN, p.seqlen, tid);
-    ld.store(k_lds[0], v_lds[0], tid);
-  }
+  if (tile_begin < tile_end) issue_tile(tile_begin * kBN, std::integral_constant<int, 0>{});
+  wait_dma();
   __syncthreads();
 
-  const int krow = perm_rows(n);
-  for (int it = tile_begin; it < tile_end; ++it) {
-    const int cur = (it - tile_begin) & 1;
+  auto tile_body = [&](int it, auto cur_c) {
+    constexpr int cur = decltype(cur_c)::value;
     const int t0 = it * kBN;
-    const bool more = it + 1 < tile_end;
-    if (more) ld.load(kg, vg, kv_stride, t0 + kBN, p.seqlen, tid);
+    if (it + 1 < tile_end) issue_tile(t0 + kBN, std::integral_constant<int, cur ^ 1>{});
 
-    const bool any = (t0 < hi_max) && (t0 + kBN > lo_min);
-    if (any) {
+    if ((t0 < hi_max) && (t0 + kBN > lo_min)) {
       const bool full = (t0 >= lo_max) && (t0 + kBN <= hi_min);
-      const __bf16* ks = k_lds[cur];
-      const __bf16* vs = v_lds[cur];
+      const __bf16* ks = cur ? k_lds1 : k_lds0;
+      const __bf16* vs = cur ? v_lds1 : v_lds0;
       f32x16 s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         s[kb] = f32x16{};
 #pragma unroll
-        for (int t = 0; t < KS; ++t) {
-          const bf16x8 a = lds_read_b128(ks, off_b128<D>(kb * 32 + krow, 2 * t + h));
-          s[kb] = mfma32(a, qf[t], s[kb]);
-        }
+        for (int t = 0; t < KS; ++t) s[kb] = mfma32(lds_read_b128(ks, koff[t] + kb * 32 * D), qf[t], s[kb]);
       }
       if (!full) {
 #pragma unroll
@@ -166,15 +179,13 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = t0 + kb * 32 + c_key(r, h);
-            if (key < kstart || key >= kend) s[kb][r] = -INFINITY;
+            s[kb][r] = (key < kstart || key >= kend) ? -INFINITY : s[kb][r];
           }
       }
-      float mx = s[0][0];
+      float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-      mx = wave_max_halves(mx);
+      for (int r = 1; r < 16; ++r) mx = max3f(mx, s[0][r], s[1][r]);
+      mx = max_lane_halves(mx);
       const float m_tile = mx * c;
       if (__any(m_tile > m_run + kRescaleThreshold)) {
         const float m_new = fmaxf(m_run, m_tile);
@@ -184,13 +195,14 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(FwdParams p) {
         for (int i = 0; i < DB; ++i) acc[i] *= alpha;
         m_run = m_new;
       }
+      const float neg_m = -m_run;
       bf16x8 pb[4];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float e[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          e[r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_run));
+          e[r] = fast_exp2(__builtin_fmaf(s[kb][r], c, neg_m));
           l_run += e[r];
         }
         pb[2 * kb] = pack_bf16(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
@@ -199,17 +211,20 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 a = tr_fragment<D>(vs, 16 * u, 32 * db, lane);
-          acc[db] = mfma32(a, pb[u], acc[db]);
-        }
+        for (int db = 0; db < DB; ++db)
+          acc[db] = mfma32(tr_read_pair(vs, voff[db] + 16 * u * D, 4 * D), pb[u], acc[db]);
     }
-    if (more) ld.store(k_lds[cur ^ 1], v_lds[cur ^ 1], tid);
+    wait_dma();
     __syncthreads();
+  };
+
+  for (int it = tile_begin; it < tile_end; it += 2) {
+    tile_body(it, std::integral_constant<int, 0>{});
+    if (it + 1 < tile_end) tile_body(it + 1, std::integral_constant<int, 1>{});
   }
 
   // epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = sum_lane_halves(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   if (q_ok) {
     __bf16* orow = p.o + ((size_t)b * p.seqlen + my_q) * q_stride + hq * D;
@@ -231,23 +246,22 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-template <int D, int NW, bool CAUSAL>
+template <int D, bool CAUSAL>
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
   FwdParams q = p;
-  q.num_qblk = (p.seqlen + 32 * NW - 1) / (32 * NW);
+  q.num_qblk = (p.seqlen + kBM - 1) / kBM;
   dim3 grid(p.batch * p.hq, q.num_qblk);
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, CAUSAL>), grid, dim3(NW * 64), 0, stream, q);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), grid, dim3(kWaves * 64), 0, stream, q);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t run_fwd_bf16(const FwdParams& p, hipStream_t stream) {
-  constexpr int NW = 8;
   if (p.head_dim == 128) {
-    return p.causal ? launch_fwd<128, NW, true>(p, stream) : launch_fwd<128, NW, false>(p, stream);
+    return p.causal ? launch_fwd<128, true>(p, stream) : launch_fwd<128, false>(p, stream);
   }
-  return p.causal ? launch_fwd<64, NW, true>(p, stream) : launch_fwd<64, NW, false>(p, stream);
+  return p.causal ? launch_fwd<64, true>(p, stream) : launch_fwd<64, false>(p, stream);
 }
 
 }  // namespace mi355attn
