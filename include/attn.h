@@ -98,8 +98,10 @@ attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                          int causal, const int32_t* cu_seqlens, int num_seqs,
                          float scale, attn_stream_t stream);
 
-/* Bytes of device workspace attn_bwd needs: 4 * batch * hq * seqlen (the
- * per-row Delta_i = dO_i . O_i in fp32). Returns 0 for non-positive sizes. */
+/* Bytes of device workspace attn_bwd needs: 8 * batch * hq * S64, with S64 =
+ * seqlen rounded up to a multiple of 64. It holds two fp32 per-row arrays of
+ * [batch, hq, S64]: Delta_i = dO_i . O_i and LSE_i * log2(e); the padding
+ * rows are written as zeros. Returns 0 for non-positive sizes. */
 size_t attn_bwd_workspace_bytes(int batch, int hq, int seqlen);
 
 /* Backward: dq, dk, dv from q, k, v, the forward's o and lse, and dout.

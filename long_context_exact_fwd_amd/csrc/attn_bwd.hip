@@ -9,12 +9,17 @@
 //   Delta_i = dO_i . O_i              dS_ij = P_ij (dP_ij - Delta_i)
 //   dQ_i = scale sum_j dS_ij K_j      dK_j = scale sum_i dS_ij Q_i
 // Split into two passes so that nothing is accumulated with atomics:
-//   * dK/dV: one workgroup per (b, h_kv, 32*NW keys); each wave keeps 32 keys
-//     of K and V in VGPRs and accumulates dK^T, dV^T over every query head of
-//     the GQA group and every visible Q tile (so the group sum needs no
-//     reduction across workgroups);
-//   * dQ: one workgroup per (b, h_q, 32*NW queries), the forward's layout:
+//   * dK/dV: one workgroup of 8 waves per (b, h_kv, 128 keys). Two waves share
+//     each 32 keys: wave A holds K, computes S and P and accumulates dV^T;
+//     wave B holds V, computes dP and, with A's P handed over through LDS,
+//     dS and dK^T. Each wave then needs one accumulator and one operand set,
+//     under 256 VGPRs, so two waves run per SIMD. The loop covers every query
+//     head of the GQA group and every visible 64-query tile, so the group sum
+//     needs no reduction across workgroups.
+//   * dQ: the forward's layout (4 waves of 32 queries, two workgroups per CU):
 //     Q and dO stay in VGPRs, K and V tiles stream through LDS.
+// Tiles reach LDS through buffer loads that write LDS directly; rows past the
+// sequence end read as zeros and are masked.
 #include "attn_device.h"
 #include "attn_internal.h"
 
@@ -22,134 +27,68 @@ namespace mi355attn {
 
 namespace {
 
-constexpr int kTile = 64;  // rows of the streamed tiles (queries or keys)
-
-// One layout for tiles read both with 16-byte reads (rows through perm_rows)
-// and with transposing reads (4 consecutive rows): the chunk XOR spreads
-// 16 consecutive rows over 16 chunks and 4 consecutive rows over 4 chunk groups.
-template <int D>
-__device__ __forceinline__ int swz_dual(int row, int chunk) {
-  if constexpr (D == 128) {
-    return chunk ^ (((row & 3) << 2) | ((row >> 2) & 3));
-  } else {
-    return chunk ^ (((row & 3) << 1) | ((row >> 2) & 1));
-  }
-}
-template <int D>
-__device__ __forceinline__ int off_dual(int row, int chunk) { return row * D + swz_dual<D>(row, chunk) * 8; }
-template <int D>
-__device__ __forceinline__ int off_dual_unit(int row, int unit) {
-  return row * D + swz_dual<D>(row, unit >> 1) * 8 + (unit & 1) * 4;
-}
-
-// X^T fragment from a dual-layout tile (see tr_fragment in attn_device.h).
-template <int D>
-__device__ __forceinline__ bf16x8 tr_fragment_dual(const __bf16* tile, int row0, int col0, int lane) {
-  const int r = row0 + 8 * (lane >> 5) + ((lane & 15) >> 2);
-  const int unit = (col0 >> 2) + 4 * ((lane >> 4) & 1) + (lane & 3);
-  const bf16x4 lo = lds_read_tr(tile, off_dual_unit<D>(r, unit));
-  const bf16x4 hi = lds_read_tr(tile, off_dual_unit<D>(r + 4, unit));
-  bf16x8 out;
-  out[0] = lo[0]; out[1] = lo[1]; out[2] = lo[2]; out[3] = lo[3];
-  out[4] = hi[0]; out[5] = hi[1]; out[6] = hi[2]; out[7] = hi[3];
-  return out;
-}
+constexpr int kQT = 64;  // queries per tile (dK/dV pass)
+constexpr int kKT = 64;  // keys per tile (dQ pass)
 
 // ---------------------------------------------------------------------------
-// Delta_i = dO_i . O_i (fp32), [B, Hq, S]
+// Delta_i = dO_i . O_i and LSE_i * log2(e), both fp32 [B, Hq, S]
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
   constexpr int LPR = D / 8;  // lanes per row
   constexpr int RPB = 256 / LPR;
   const int tid = threadIdx.x;
-  const long row = (long)blockIdx.x * RPB + tid / LPR;  // index into [B, S, Hq]
-  const long nrows = (long)p.batch * p.seqlen * p.hq;
+  const long r = (long)blockIdx.x * RPB + tid / LPR;  // index into [B, Hq, stat_stride]
+  const long nrows = (long)p.batch * p.hq * p.stat_stride;
   const int sub = tid % LPR;
+  const long i = r % p.stat_stride;
+  const bool real = r < nrows && i < p.seqlen;
   float acc = 0.f;
-  if (row < nrows) {
-    const u32x4 a = load16(p.o + row * D + sub * 8);
-    const u32x4 g = load16(p.dout + row * D + sub * 8);
-    const bf16x8 av = as_bf16x8(a), gv = as_bf16x8(g);
+  if (real) {
+    const long bh = r / p.stat_stride;
+    const long b = bh / p.hq;
+    const long hq = bh % p.hq;
+    const size_t off = ((size_t)(b * p.seqlen + i) * p.hq + hq) * D + sub * 8;
+    const bf16x8 av = as_bf16x8(load16(p.o + off));
+    const bf16x8 gv = as_bf16x8(load16(p.dout + off));
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc += (float)av[e] * (float)gv[e];
   }
 #pragma unroll
   for (int o = LPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-  if (row < nrows && sub == 0) {
-    const long hq = row % p.hq;
-    const long bs = row / p.hq;
-    const long i = bs % p.seqlen;
-    const long b = bs / p.seqlen;
-    p.delta[(b * p.hq + hq) * p.seqlen + i] = acc;
+  if (r < nrows && sub == 0) {
+    // padding rows get zeros: they are read by whole-tile copies and masked
+    const long bh = r / p.stat_stride;
+    p.delta[r] = acc;
+    p.lse2[r] = real ? p.lse[bh * p.seqlen + i] * kLog2e : 0.f;
   }
 }
 
 // ---------------------------------------------------------------------------
 // dK / dV
 // ---------------------------------------------------------------------------
-template <int D, int NW>
-struct QTileLoader {
-  static constexpr int kThreads = NW * 64;
-  static constexpr int kChunks = kTile * D / 8;
-  static constexpr int kPer = (kChunks + kThreads - 1) / kThreads;
-  u32x4 q[kPer], g[kPer];
-  float lse2, dlt;  // one row statistic per thread (threads < kTile)
-
-  __device__ __forceinline__ void load(const BwdParams& p, int b, int hq, int t0, int tid) {
-    const int q_stride = p.hq * D;
-    const __bf16* qg = p.q + (size_t)b * p.seqlen * q_stride + hq * D;
-    const __bf16* gg = p.dout + (size_t)b * p.seqlen * q_stride + hq * D;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int idx = tid + i * kThreads;
-      const int row = idx / (D / 8);
-      const int ch = idx % (D / 8);
-      const int r = t0 + row;
-      const bool ok = (idx < kChunks) && r < p.seqlen;
-      const size_t off = (size_t)(ok ? r : 0) * q_stride + ch * 8;
-      q[i] = load16_pred(qg + off, ok);
-      g[i] = load16_pred(gg + off, ok);
-    }
-    if (tid < kTile) {
-      const int r = t0 + tid;
-      const size_t so = ((size_t)b * p.hq + hq) * p.seqlen;
-      const bool ok = r < p.seqlen;
-      lse2 = ok ? p.lse[so + r] * kLog2e : INFINITY;
-      dlt = ok ? p.delta[so + r] : 0.f;
-    }
-  }
-  __device__ __forceinline__ void store(__bf16* qs, __bf16* gs, float* ls, float* ds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int idx = tid + i * kThreads;
-      if (idx < kChunks) {
-        const int row = idx / (D / 8);
-        const int ch = idx % (D / 8);
-        lds_store16(qs, off_dual<D>(row, ch), q[i]);
-        lds_store16(gs, off_dual<D>(row, ch), g[i]);
-      }
-    }
-    if (tid < kTile) {
-      ls[tid] = lse2;
-      ds[tid] = dlt;
-    }
-  }
-};
-
-template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdParams p) {
-  constexpr int BK = 32 * NW;  // keys per workgroup
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  __shared__ __attribute__((aligned(16))) __bf16 q_lds[2][kTile * D];
-  __shared__ __attribute__((aligned(16))) __bf16 g_lds[2][kTile * D];
-  __shared__ __attribute__((aligned(16))) float l_lds[2][kTile];
-  __shared__ __attribute__((aligned(16))) float d_lds[2][kTile];
-  __shared__ int red[2][NW];
+  constexpr int TILE = kQT * D;
+  constexpr int NI = TILE * 2 / (8 * 1024);  // DMA instructions per wave per tensor and tile
+  // Separate objects per buffer so that alias analysis keeps DMA writes into
+  // one buffer from forcing waits on reads of the other.
+  __shared__ __attribute__((aligned(1024))) __bf16 q_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 q_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 g_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 g_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) float st_lds0[2 * kQT];  // [LSE*log2e | Delta] of the tile
+  __shared__ __attribute__((aligned(1024))) float st_lds1[2 * kQT];
+  // P handed from wave A to wave B: [pair][query block][4][lane] x f32x4
+  __shared__ __attribute__((aligned(1024))) f32x4 xchg[4][2][4][64];
+  __shared__ int red[2][8];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave & 3;
+  const int role = wave >> 2;  // 0: S, P, dV   1: dP, dS, dK
   const int lane = tid & 63;
   const int n = lane & 31;
   const int h = lane >> 5;
@@ -158,11 +97,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdParams p) {
   const int b = bh / p.hkv;
   const int hk = bh - b * p.hkv;
   const int G = p.hq / p.hkv;
-  const int kblk = blockIdx.y;
-  const int k0 = kblk * BK;
-  const int my_k = k0 + wave * 32 + n;
+  const int k0 = blockIdx.y * 128;  // causal: the first key blocks see the most queries
+  const int my_k = k0 + pair * 32 + n;
   const bool k_ok = my_k < p.seqlen;
   const int kv_stride = p.hkv * D;
+  const int q_stride = p.hq * D;
 
   // queries that see this lane's key: [qlo, qhi)
   int qlo = 0, qhi = 0;
@@ -172,10 +111,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdParams p) {
     qlo = CAUSAL ? my_k : s0;
     qhi = s1;
   }
-  const int lo_min = wave_min(k_ok ? qlo : INT32_MAX);
-  const int hi_max = wave_max(k_ok ? qhi : INT32_MIN);
-  const int lo_max = wave_max(k_ok ? qlo : INT32_MIN);
-  const int hi_min = wave_min(k_ok ? qhi : INT32_MAX);
+  // Both waves of a pair hold the same keys and so take the same decisions.
+  const int lo_min = __builtin_amdgcn_readfirstlane(wave_min(k_ok ? qlo : INT32_MAX));
+  const int hi_max = __builtin_amdgcn_readfirstlane(wave_max(k_ok ? qhi : INT32_MIN));
+  const int lo_max = __builtin_amdgcn_readfirstlane(wave_max(k_ok ? qlo : INT32_MIN));
+  const int hi_min = __builtin_amdgcn_readfirstlane(wave_min(k_ok ? qhi : INT32_MAX));
   if (lane == 0) {
     red[0][wave] = lo_min;
     red[1][wave] = hi_max;
@@ -183,131 +123,209 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdParams p) {
   __syncthreads();
   int wg_lo = INT32_MAX, wg_hi = INT32_MIN;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
+  for (int w = 0; w < 8; ++w) {
     wg_lo = min(wg_lo, red[0][w]);
     wg_hi = max(wg_hi, red[1][w]);
   }
-  const int tile_begin = wg_hi > wg_lo ? wg_lo / kTile : 0;
-  const int tile_end = wg_hi > wg_lo ? (wg_hi + kTile - 1) / kTile : 0;
+  wg_lo = __builtin_amdgcn_readfirstlane(wg_lo);
+  wg_hi = __builtin_amdgcn_readfirstlane(wg_hi);
+  const int tile_begin = wg_hi > wg_lo ? wg_lo / kQT : 0;
+  const int tile_end = wg_hi > wg_lo ? (wg_hi + kQT - 1) / kQT : 0;
   const int ntiles = tile_end - tile_begin;
   const int nsteps = ntiles * G;
 
-  // K and V slices of this wave as B operands: lane (n, h) holds row my_k, d = 16t + 8h .. +7
-  bf16x8 kf[KS], vf[KS];
+  // This wave's operand (K for A, V for B) as B operands: lane (n, h) holds row my_k, d = 16t + 8h .. +7
+  bf16x8 xf[KS];
   {
-    const size_t off = ((size_t)b * p.seqlen + (k_ok ? my_k : 0)) * kv_stride + hk * D + 8 * h;
+    const __bf16* src = role == 0 ? p.k : p.v;
+    const size_t off = ((size_t)b * p.seqlen + min(my_k, p.seqlen - 1)) * kv_stride + hk * D + 8 * h;
 #pragma unroll
-    for (int t = 0; t < KS; ++t) {
-      kf[t] = as_bf16x8(load16_pred(p.k + off + 16 * t, k_ok));
-      vf[t] = as_bf16x8(load16_pred(p.v + off + 16 * t, k_ok));
+    for (int t = 0; t < KS; ++t) xf[t] = as_bf16x8(load16(src + off + 16 * t));
+  }
+
+  // LDS offsets: rows perm_rows(n) of a Q/dO tile (A operand of S and dP), and
+  // the two transposing reads of the Q^T / dO^T fragment of query step 0.
+  int qoff[KS];
+#pragma unroll
+  for (int t = 0; t < KS; ++t) qoff[t] = off_dual<D>(perm_rows(n), 2 * t + h);
+  int trlo[DB], trhi[DB];
+  {
+    const int r0 = 8 * h + ((lane & 15) >> 2);
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+      const int unit = 8 * d + 4 * ((lane >> 4) & 1) + (lane & 3);
+      trlo[d] = off_dual_unit<D>(r0, unit);
+      trhi[d] = off_dual_unit<D>(r0 + 4, unit);
     }
   }
-  f32x16 dk[DB], dv[DB];
+  // DMA: instruction i of wave w fills the 1 KiB at (8 i + w) KiB of a tile.
+  uint32_t ld_off[NI];
 #pragma unroll
-  for (int i = 0; i < DB; ++i) {
-    dk[i] = f32x16{};
-    dv[i] = f32x16{};
+  for (int i = 0; i < NI; ++i) {
+    const int e = (i * 8 + wave) * 512 + lane * 8;
+    const int row = e / D;
+    ld_off[i] = (uint32_t)(row * q_stride + swz_dual<D>(row, (e % D) / 8) * 8) * 2u;
   }
+  const size_t stat_b = (size_t)b * p.hq * p.stat_stride;
+  auto issue_step = [&](int step, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    const int g = step / ntiles;
+    const int t0 = (tile_begin + step - g * ntiles) * kQT;
+    const int hq = hk * G + g;
+    const size_t row0 = ((size_t)b * p.seqlen + t0) * q_stride + hq * D;
+    const uint32_t nbytes = (uint32_t)(p.seqlen - t0) * (uint32_t)q_stride * 2u;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + row0, nbytes);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.dout + row0, nbytes);
+    __bf16* qd = buf ? q_lds1 : q_lds0;
+    __bf16* gd = buf ? g_lds1 : g_lds0;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int el = (i * 8 + wave) * 512;
+      dma16_buf(rq, ld_off[i], qd + el);
+      dma16_buf(rg, ld_off[i], gd + el);
+    }
+    if (wave < 2 && lane < kQT / 4) {
+      // wave 0 copies LSE*log2e, wave 1 Delta: 4 floats per lane
+      const float* src = (wave == 0 ? p.lse2 : p.delta) + stat_b + (size_t)hq * p.stat_stride + t0;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)(p.stat_stride - t0) * 4u);
+      float* sd = (buf ? st_lds1 : st_lds0) + wave * kQT;
+      dma16_buf(rs, (uint32_t)lane * 16u, sd);
+    }
+  };
+
+  f32x16 acc[DB];  // dV^T (role A) or dK^T (role B)
+#pragma unroll
+  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
   const float c = p.scale_log2e;
 
-  QTileLoader<D, NW> ld;
-  if (nsteps > 0) {
-    ld.load(p, b, hk * G, tile_begin * kTile, tid);
-    ld.store(q_lds[0], g_lds[0], l_lds[0], d_lds[0], tid);
-  }
+  if (nsteps > 0) issue_step(0, std::integral_constant<int, 0>{});
+  wait_dma();
   __syncthreads();
 
-  const int qrow = perm_rows(n);
-  for (int step = 0; step < nsteps; ++step) {
-    const int cur = step & 1;
-    const int it = tile_begin + step % ntiles;
-    const int t0 = it * kTile;
-    const bool more = step + 1 < nsteps;
-    if (more) {
-      const int nstep = step + 1;
-      ld.load(p, b, hk * G + nstep / ntiles, (tile_begin + nstep % ntiles) * kTile, tid);
-    }
-    const bool any = (t0 < hi_max) && (t0 + kTile > lo_min);
-    if (any) {
-      const bool full = (t0 >= lo_max) && (t0 + kTile <= hi_min);
-      const __bf16* qs = q_lds[cur];
-      const __bf16* gs = g_lds[cur];
-      const float* ls = l_lds[cur];
-      const float* dsl = d_lds[cur];
-      bf16x8 pb[4], db[4];
+  // Every pair runs every step of the workgroup's range: a step that a pair
+  // cannot see is fully masked (P = 0). With 64-query tiles and 128-key
+  // workgroups that costs at most the first two steps of a causal range,
+  // and it keeps the loop free of per-wave branches around the barriers.
+  // Two barriers per step: after A has written P, and at the end of the step
+  // (next Q/dO tile in LDS).
+  if (role == 0) {
+    auto body_a = [&](int step, auto cur_c) {
+      constexpr int cur = decltype(cur_c)::value;
+      const int t0 = (tile_begin + step % ntiles) * kQT;
+      if (step + 1 < nsteps) issue_step(step + 1, std::integral_constant<int, cur ^ 1>{});
+      const bool full = (t0 >= lo_max) && (t0 + kQT <= hi_min);
+      const __bf16* qs = cur ? q_lds1 : q_lds0;
+      const __bf16* gs = cur ? g_lds1 : g_lds0;
+      const float* st = cur ? st_lds1 : st_lds0;
+      bf16x8 pb[4];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        f32x16 s = f32x16{}, dp = f32x16{};
+        f32x16 s = f32x16{};
 #pragma unroll
-        for (int t = 0; t < KS; ++t) {
-          const bf16x8 a = lds_read_b128(qs, off_dual<D>(qb * 32 + qrow, 2 * t + h));
-          s = mfma32(a, kf[t], s);
-        }
+        for (int t = 0; t < KS; ++t) s = mfma32(lds_read_b128(qs, qoff[t] + qb * 32 * D), xf[t], s);
+        // C rows of this lane: queries qb*32 + c_key(r, h), two runs of 8
+        const f32x4* l4 = reinterpret_cast<const f32x4*>(st + qb * 32 + 8 * h);
+        const f32x4 la = l4[0], lb = l4[1], lc = l4[4], ld = l4[5];
+        float pr[16];
 #pragma unroll
-        for (int t = 0; t < KS; ++t) {
-          const bf16x8 a = lds_read_b128(gs, off_dual<D>(qb * 32 + qrow, 2 * t + h));
-          dp = mfma32(a, vf[t], dp);
-        }
-        // rows of this lane: queries qb*32 + c_key(r, h): two runs of 8
-        const f32x4* l4 = reinterpret_cast<const f32x4*>(ls + qb * 32 + 8 * h);
-        const f32x4* d4 = reinterpret_cast<const f32x4*>(dsl + qb * 32 + 8 * h);
-        float pr[16], dsv[16];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const f32x4 la = l4[4 * half], lb = l4[4 * half + 1];
-          const f32x4 da = d4[4 * half], dd = d4[4 * half + 1];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r0 = 8 * half + e, r1 = 8 * half + 4 + e;
-            pr[r0] = fast_exp2(__builtin_fmaf(s[r0], c, -la[e]));
-            pr[r1] = fast_exp2(__builtin_fmaf(s[r1], c, -lb[e]));
-            dsv[r0] = pr[r0] * (dp[r0] - da[e]);
-            dsv[r1] = pr[r1] * (dp[r1] - dd[e]);
-          }
+        for (int e = 0; e < 4; ++e) {
+          pr[e] = fast_exp2(__builtin_fmaf(s[e], c, -la[e]));
+          pr[4 + e] = fast_exp2(__builtin_fmaf(s[4 + e], c, -lb[e]));
+          pr[8 + e] = fast_exp2(__builtin_fmaf(s[8 + e], c, -lc[e]));
+          pr[12 + e] = fast_exp2(__builtin_fmaf(s[12 + e], c, -ld[e]));
         }
         if (!full) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int qq = t0 + qb * 32 + c_key(r, h);
-            if (qq < qlo || qq >= qhi) {
-              pr[r] = 0.f;
-              dsv[r] = 0.f;
-            }
+            pr[r] = (qq < qlo || qq >= qhi) ? 0.f : pr[r];
           }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4 v = {pr[4 * j], pr[4 * j + 1], pr[4 * j + 2], pr[4 * j + 3]};
+          xchg[pair][qb][j][lane] = v;
         }
         pb[2 * qb] = pack_bf16(pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]);
         pb[2 * qb + 1] = pack_bf16(pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]);
+      }
+      __syncthreads();  // P of this step is in xchg
+      // dV^T += dO^T P (fragment reads kept one query step ahead at most)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int d = 0; d < DB; ++d)
+          acc[d] = mfma32(tr_read2(gs, trlo[d] + 16 * u * D, trhi[d] + 16 * u * D), pb[u], acc[d]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wait_dma();
+      __syncthreads();
+    };
+    for (int step = 0; step < nsteps; step += 2) {
+      body_a(step, std::integral_constant<int, 0>{});
+      if (step + 1 < nsteps) body_a(step + 1, std::integral_constant<int, 1>{});
+    }
+  } else {
+    auto body_b = [&](int step, auto cur_c) {
+      constexpr int cur = decltype(cur_c)::value;
+      if (step + 1 < nsteps) issue_step(step + 1, std::integral_constant<int, cur ^ 1>{});
+      const __bf16* qs = cur ? q_lds1 : q_lds0;
+      const __bf16* gs = cur ? g_lds1 : g_lds0;
+      const float* st = cur ? st_lds1 : st_lds0;
+      f32x16 dp[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        dp[qb] = f32x16{};
+#pragma unroll
+        for (int t = 0; t < KS; ++t) dp[qb] = mfma32(lds_read_b128(gs, qoff[t] + qb * 32 * D), xf[t], dp[qb]);
+      }
+      __syncthreads();  // P of this step is in xchg
+      bf16x8 db[4];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const f32x4* d4 = reinterpret_cast<const f32x4*>(st + kQT + qb * 32 + 8 * h);
+        const f32x4 da = d4[0], dd = d4[1], dc = d4[4], de = d4[5];
+        const f32x4 p0 = xchg[pair][qb][0][lane], p1 = xchg[pair][qb][1][lane];
+        const f32x4 p2 = xchg[pair][qb][2][lane], p3 = xchg[pair][qb][3][lane];
+        float dsv[16];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dsv[e] = p0[e] * (dp[qb][e] - da[e]);
+          dsv[4 + e] = p1[e] * (dp[qb][4 + e] - dd[e]);
+          dsv[8 + e] = p2[e] * (dp[qb][8 + e] - dc[e]);
+          dsv[12 + e] = p3[e] * (dp[qb][12 + e] - de[e]);
+        }
         db[2 * qb] = pack_bf16(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
         db[2 * qb + 1] = pack_bf16(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
       }
+      // dK^T += Q^T dS
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 4; ++u) {
 #pragma unroll
-        for (int d = 0; d < DB; ++d) {
-          const bf16x8 ag = tr_fragment_dual<D>(gs, 16 * u, 32 * d, lane);
-          dv[d] = mfma32(ag, pb[u], dv[d]);
-          const bf16x8 aq = tr_fragment_dual<D>(qs, 16 * u, 32 * d, lane);
-          dk[d] = mfma32(aq, db[u], dk[d]);
-        }
+        for (int d = 0; d < DB; ++d)
+          acc[d] = mfma32(tr_read2(qs, trlo[d] + 16 * u * D, trhi[d] + 16 * u * D), db[u], acc[d]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wait_dma();
+      __syncthreads();
+    };
+    for (int step = 0; step < nsteps; step += 2) {
+      body_b(step, std::integral_constant<int, 0>{});
+      if (step + 1 < nsteps) body_b(step + 1, std::integral_constant<int, 1>{});
     }
-    if (more) ld.store(q_lds[cur ^ 1], g_lds[cur ^ 1], l_lds[cur ^ 1], d_lds[cur ^ 1], tid);
-    __syncthreads();
   }
 
   if (k_ok) {
-    const size_t off = ((size_t)b * p.seqlen + my_k) * kv_stride + hk * D;
+    __bf16* dst = (role == 0 ? p.dv : p.dk) + ((size_t)b * p.seqlen + my_k) * kv_stride + hk * D;
+    const float mul = role == 0 ? 1.0f : p.scale;
 #pragma unroll
     for (int d = 0; d < DB; ++d)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        bf16x4 wk, wv;
+        bf16x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          wk[e] = (__bf16)(dk[d][4 * g + e] * p.scale);
-          wv[e] = (__bf16)(dv[d][4 * g + e]);
-        }
-        *reinterpret_cast<bf16x4*>(p.dk + off + 32 * d + 8 * g + 4 * h) = wk;
-        *reinterpret_cast<bf16x4*>(p.dv + off + 32 * d + 8 * g + 4 * h) = wv;
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[d][4 * g + e] * mul);
+        *reinterpret_cast<bf16x4*>(dst + 32 * d + 8 * g + 4 * h) = w;
       }
   }
 }
@@ -315,52 +333,20 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
-template <int D, int NW>
-struct KVTileLoader {
-  static constexpr int kThreads = NW * 64;
-  static constexpr int kChunks = kTile * D / 8;
-  static constexpr int kPer = (kChunks + kThreads - 1) / kThreads;
-  u32x4 k[kPer], v[kPer];
-
-  __device__ __forceinline__ void load(const __bf16* kg, const __bf16* vg, int row_stride, int t0, int seqlen,
-                                       int tid) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int idx = tid + i * kThreads;
-      const int row = idx / (D / 8);
-      const int ch = idx % (D / 8);
-      const int g = t0 + row;
-      const bool ok = (idx < kChunks) && g < seqlen;
-      const size_t off = (size_t)(ok ? g : 0) * row_stride + ch * 8;
-      k[i] = load16_pred(kg + off, ok);
-      v[i] = load16_pred(vg + off, ok);
-    }
-  }
-  __device__ __forceinline__ void store(__bf16* ks, __bf16* vs, int tid) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int idx = tid + i * kThreads;
-      if (idx < kChunks) {
-        const int row = idx / (D / 8);
-        const int ch = idx % (D / 8);
-        lds_store16(ks, off_dual<D>(row, ch), k[i]);
-        lds_store16(vs, off_b128<D>(row, ch), v[i]);
-      }
-    }
-  }
-};
-
-template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdParams p) {
-  constexpr int BM = 32 * NW;
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][kTile * D];
-  __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][kTile * D];
-  __shared__ int red[2][NW];
+  constexpr int TILE = kKT * D;
+  constexpr int NI = TILE * 2 / (4 * 1024);
+  __shared__ __attribute__((aligned(1024))) __bf16 k_lds0[TILE];  // dual layout: rows and K^T reads
+  __shared__ __attribute__((aligned(1024))) __bf16 k_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_lds0[TILE];  // row reads only
+  __shared__ __attribute__((aligned(1024))) __bf16 v_lds1[TILE];
+  __shared__ int red[2][4];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int n = lane & 31;
   const int h = lane >> 5;
@@ -369,8 +355,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdParams p) {
   const int b = bh / p.hq;
   const int hq = bh - b * p.hq;
   const int hk = hq / (p.hq / p.hkv);
-  const int qblk = p.num_blk - 1 - (int)blockIdx.y;
-  const int my_q = qblk * BM + wave * 32 + n;
+  const int qblk = p.num_blk - 1 - (int)blockIdx.y;  // heaviest blocks first
+  const int my_q = qblk * 128 + wave * 32 + n;
   const bool q_ok = my_q < p.seqlen;
   const int q_stride = p.hq * D;
   const int kv_stride = p.hkv * D;
@@ -384,10 +370,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdParams p) {
     kstart = s0;
     kend = CAUSAL ? my_q + 1 : s1;
   }
-  const int lo_min = wave_min(q_ok ? kstart : INT32_MAX);
-  const int hi_max = wave_max(q_ok ? kend : INT32_MIN);
-  const int lo_max = wave_max(q_ok ? kstart : INT32_MIN);
-  const int hi_min = wave_min(q_ok ? kend : INT32_MAX);
+  const int lo_min = __builtin_amdgcn_readfirstlane(wave_min(q_ok ? kstart : INT32_MAX));
+  const int hi_max = __builtin_amdgcn_readfirstlane(wave_max(q_ok ? kend : INT32_MIN));
+  const int lo_max = __builtin_amdgcn_readfirstlane(wave_max(q_ok ? kstart : INT32_MIN));
+  const int hi_min = __builtin_amdgcn_readfirstlane(wave_min(q_ok ? kend : INT32_MAX));
   if (lane == 0) {
     red[0][wave] = lo_min;
     red[1][wave] = hi_max;
@@ -395,63 +381,92 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdParams p) {
   __syncthreads();
   int wg_lo = INT32_MAX, wg_hi = INT32_MIN;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
+  for (int w = 0; w < 4; ++w) {
     wg_lo = min(wg_lo, red[0][w]);
     wg_hi = max(wg_hi, red[1][w]);
   }
-  const int tile_begin = wg_hi > wg_lo ? wg_lo / kTile : 0;
-  const int tile_end = wg_hi > wg_lo ? (wg_hi + kTile - 1) / kTile : 0;
+  wg_lo = __builtin_amdgcn_readfirstlane(wg_lo);
+  wg_hi = __builtin_amdgcn_readfirstlane(wg_hi);
+  const int tile_begin = wg_hi > wg_lo ? wg_lo / kKT : 0;
+  const int tile_end = wg_hi > wg_lo ? (wg_hi + kKT - 1) / kKT : 0;
 
   bf16x8 qf[KS], gf[KS];
   {
-    const size_t off = ((size_t)b * p.seqlen + (q_ok ? my_q : 0)) * q_stride + hq * D + 8 * h;
+    const size_t off = ((size_t)b * p.seqlen + min(my_q, p.seqlen - 1)) * q_stride + hq * D + 8 * h;
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
-      qf[t] = as_bf16x8(load16_pred(p.q + off + 16 * t, q_ok));
-      gf[t] = as_bf16x8(load16_pred(p.dout + off + 16 * t, q_ok));
+      qf[t] = as_bf16x8(load16(p.q + off + 16 * t));
+      gf[t] = as_bf16x8(load16(p.dout + off + 16 * t));
     }
   }
-  const size_t so = ((size_t)b * p.hq + hq) * p.seqlen;
-  const float lse2 = q_ok ? p.lse[so + my_q] * kLog2e : INFINITY;
+  const size_t so = ((size_t)b * p.hq + hq) * p.stat_stride;
+  // rows past the end: P = exp2(-inf) = 0, so nothing from them is non-finite
+  const float lse2 = q_ok ? p.lse2[so + my_q] : INFINITY;
   const float dlt = q_ok ? p.delta[so + my_q] : 0.f;
+
+  int koff[KS], voff[KS];
+#pragma unroll
+  for (int t = 0; t < KS; ++t) {
+    koff[t] = off_dual<D>(perm_rows(n), 2 * t + h);
+    voff[t] = off_b128<D>(perm_rows(n), 2 * t + h);
+  }
+  int ktlo[DB], kthi[DB];  // K^T fragment of key step 0
+  {
+    const int r0 = 8 * h + ((lane & 15) >> 2);
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+      const int unit = 8 * d + 4 * ((lane >> 4) & 1) + (lane & 3);
+      ktlo[d] = off_dual_unit<D>(r0, unit);
+      kthi[d] = off_dual_unit<D>(r0 + 4, unit);
+    }
+  }
+  uint32_t ld_koff[NI], ld_voff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int e = (i * 4 + wave) * 512 + lane * 8;
+    const int row = e / D;
+    const int pc = (e % D) / 8;
+    ld_koff[i] = (uint32_t)(row * kv_stride + swz_dual<D>(row, pc) * 8) * 2u;
+    ld_voff[i] = (uint32_t)(row * kv_stride + swz_b128<D>(row, pc) * 8) * 2u;
+  }
+  auto issue_tile = [&](int t0, auto buf_c) {
+    __bf16* kd = decltype(buf_c)::value ? k_lds1 : k_lds0;
+    __bf16* vd = decltype(buf_c)::value ? v_lds1 : v_lds0;
+    const uint32_t nbytes = (uint32_t)(p.seqlen - t0) * (uint32_t)kv_stride * 2u;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)t0 * kv_stride, nbytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)t0 * kv_stride, nbytes);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int el = (i * 4 + wave) * 512;
+      dma16_buf(rk, ld_koff[i], kd + el);
+      dma16_buf(rv, ld_voff[i], vd + el);
+    }
+  };
 
   f32x16 acc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
   const float c = p.scale_log2e;
 
-  KVTileLoader<D, NW> ld;
-  if (tile_begin < tile_end) {
-    ld.load(kg, vg, kv_stride, tile_begin * kTile, p.seqlen, tid);
-    ld.store(k_lds[0], v_lds[0], tid);
-  }
+  if (tile_begin < tile_end) issue_tile(tile_begin * kKT, std::integral_constant<int, 0>{});
+  wait_dma();
   __syncthreads();
 
-  const int krow = perm_rows(n);
-  for (int it = tile_begin; it < tile_end; ++it) {
-    const int cur = (it - tile_begin) & 1;
-    const int t0 = it * kTile;
-    const bool more = it + 1 < tile_end;
-    if (more) ld.load(kg, vg, kv_stride, t0 + kTile, p.seqlen, tid);
-    const bool any = (t0 < hi_max) && (t0 + kTile > lo_min);
-    if (any) {
-      const bool full = (t0 >= lo_max) && (t0 + kTile <= hi_min);
-      const __bf16* ks = k_lds[cur];
-      const __bf16* vs = v_lds[cur];
-      bf16x8 db[4];
+  auto tile_body = [&](int it, auto cur_c) {
+    constexpr int cur = decltype(cur_c)::value;
+    const int t0 = it * kKT;
+    if (it + 1 < tile_end) issue_tile(t0 + kKT, std::integral_constant<int, cur ^ 1>{});
+    if ((t0 < hi_max) && (t0 + kKT > lo_min)) {
+      const bool full = (t0 >= lo_max) && (t0 + kKT <= hi_min);
+      const __bf16* ks = cur ? k_lds1 : k_lds0;
+      const __bf16* vs = cur ? v_lds1 : v_lds0;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int t = 0; t < KS; ++t) {
-          const bf16x8 a = lds_read_b128(ks, off_dual<D>(kb * 32 + krow, 2 * t + h));
-          s = mfma32(a, qf[t], s);
-        }
+        for (int t = 0; t < KS; ++t) s = mfma32(lds_read_b128(ks, koff[t] + kb * 32 * D), qf[t], s);
 #pragma unroll
-        for (int t = 0; t < KS; ++t) {
-          const bf16x8 a = lds_read_b128(vs, off_b128<D>(kb * 32 + krow, 2 * t + h));
-          dp = mfma32(a, gf[t], dp);
-        }
+        for (int t = 0; t < KS; ++t) dp = mfma32(lds_read_b128(vs, voff[t] + kb * 32 * D), gf[t], dp);
         float dsv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -462,22 +477,27 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = t0 + kb * 32 + c_key(r, h);
-            if (key < kstart || key >= kend) dsv[r] = 0.f;
+            dsv[r] = (key < kstart || key >= kend) ? 0.f : dsv[r];
           }
         }
-        db[2 * kb] = pack_bf16(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
-        db[2 * kb + 1] = pack_bf16(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
+        const bf16x8 d0 = pack_bf16(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+        const bf16x8 d1 = pack_bf16(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
+        // dQ^T += K^T dS^T
 #pragma unroll
         for (int d = 0; d < DB; ++d) {
-          const bf16x8 a = tr_fragment_dual<D>(ks, 16 * u, 32 * d, lane);
-          acc[d] = mfma32(a, db[u], acc[d]);
+          const int o = (kb * 32) * D;
+          acc[d] = mfma32(tr_read2(ks, ktlo[d] + o, kthi[d] + o), d0, acc[d]);
+          acc[d] = mfma32(tr_read2(ks, ktlo[d] + o + 16 * D, kthi[d] + o + 16 * D), d1, acc[d]);
         }
+      }
     }
-    if (more) ld.store(k_lds[cur ^ 1], v_lds[cur ^ 1], tid);
+    wait_dma();
     __syncthreads();
+  };
+
+  for (int it = tile_begin; it < tile_end; it += 2) {
+    tile_body(it, std::integral_constant<int, 0>{});
+    if (it + 1 < tile_end) tile_body(it + 1, std::integral_constant<int, 1>{});
   }
 
   if (q_ok) {
@@ -494,11 +514,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(BwdParams p) {
   }
 }
 
-template <int D, int NWK, int NWQ, bool CAUSAL>
+template <int D, bool CAUSAL>
 hipError_t launch_bwd(const BwdParams& p, unsigned phases, hipStream_t stream) {
   if (phases & kBwdDelta) {
     constexpr int RPB = 256 / (D / 8);
-    const long nrows = (long)p.batch * p.seqlen * p.hq;
+    const long nrows = (long)p.batch * p.hq * p.stat_stride;
     dim3 grid((unsigned)((nrows + RPB - 1) / RPB));
     hipLaunchKernelGGL((attn_bwd_delta_kernel<D>), grid, dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
@@ -506,17 +526,17 @@ hipError_t launch_bwd(const BwdParams& p, unsigned phases, hipStream_t stream) {
   }
   if (phases & kBwdDkDv) {
     BwdParams q = p;
-    q.num_blk = (p.seqlen + 32 * NWK - 1) / (32 * NWK);
+    q.num_blk = (p.seqlen + 127) / 128;
     dim3 grid(p.batch * p.hkv, q.num_blk);
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, NWK, CAUSAL>), grid, dim3(NWK * 64), 0, stream, q);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL>), grid, dim3(512), 0, stream, q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (phases & kBwdDq) {
     BwdParams q = p;
-    q.num_blk = (p.seqlen + 32 * NWQ - 1) / (32 * NWQ);
+    q.num_blk = (p.seqlen + 127) / 128;
     dim3 grid(p.batch * p.hq, q.num_blk);
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, NWQ, CAUSAL>), grid, dim3(NWQ * 64), 0, stream, q);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), grid, dim3(256), 0, stream, q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -527,10 +547,9 @@ hipError_t launch_bwd(const BwdParams& p, unsigned phases, hipStream_t stream) {
 
 hipError_t run_bwd(const BwdParams& p, unsigned phases, hipStream_t stream) {
   if (p.head_dim == 128) {
-    return p.causal ? launch_bwd<128, 4, 4, true>(p, phases, stream)
-                    : launch_bwd<128, 4, 4, false>(p, phases, stream);
+    return p.causal ? launch_bwd<128, true>(p, phases, stream) : launch_bwd<128, false>(p, phases, stream);
   }
-  return p.causal ? launch_bwd<64, 4, 4, true>(p, phases, stream) : launch_bwd<64, 4, 4, false>(p, phases, stream);
+  return p.causal ? launch_bwd<64, true>(p, phases, stream) : launch_bwd<64, false>(p, phases, stream);
 }
 
 }  // namespace mi355attn

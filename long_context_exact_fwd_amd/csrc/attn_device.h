@@ -177,6 +177,35 @@ __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t vof
 // s_waitcnt vmcnt(0), other counters left alone (expcnt 7, lgkmcnt 15).
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// One layout for tiles read both with 16-byte reads (rows through perm_rows)
+// and with transposing reads (4 consecutive rows): the chunk XOR spreads 16
+// consecutive rows over 16 chunks and 4 consecutive rows over 4 chunk groups.
+template <int D>
+__device__ __forceinline__ int swz_dual(int row, int chunk) {
+  if constexpr (D == 128) {
+    return chunk ^ (((row & 3) << 2) | ((row >> 2) & 3));
+  } else {
+    return chunk ^ (((row & 3) << 1) | ((row >> 2) & 1));
+  }
+}
+template <int D>
+__device__ __forceinline__ int off_dual(int row, int chunk) { return row * D + swz_dual<D>(row, chunk) * 8; }
+template <int D>
+__device__ __forceinline__ int off_dual_unit(int row, int unit) {
+  return row * D + swz_dual<D>(row, unit >> 1) * 8 + (unit & 1) * 4;
+}
+
+// Two transposing reads at independent offsets (dual tiles: the swizzle of
+// row r + 4 differs from that of row r).
+__device__ __forceinline__ bf16x8 tr_read2(const __bf16* tile, int off_lo, int off_hi) {
+  const bf16x4 lo = lds_read_tr(tile, off_lo);
+  const bf16x4 hi = lds_read_tr(tile, off_hi);
+  bf16x8 out;
+  out[0] = lo[0]; out[1] = lo[1]; out[2] = lo[2]; out[3] = lo[3];
+  out[4] = hi[0]; out[5] = hi[1]; out[6] = hi[2]; out[7] = hi[3];
+  return out;
+}
+
 __device__ __forceinline__ u32x4 load16(const __bf16* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x4 load16_pred(const __bf16* p, bool ok) {
   u32x4 z = {0u, 0u, 0u, 0u};

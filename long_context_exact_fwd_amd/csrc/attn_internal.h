@@ -49,7 +49,9 @@ struct BwdParams {
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
-  float* delta;  // workspace [B, Hq, S]
+  float* delta;  // workspace [B, Hq, stat_stride]: Delta_i = dO_i . O_i
+  float* lse2;   // workspace [B, Hq, stat_stride]: LSE_i * log2(e)
+  int stat_stride;  // seqlen rounded up to kStatAlign; the padding holds zeros
   const int32_t* cu_seqlens;
   int num_seqs;
   int batch, hq, hkv, seqlen, head_dim;
@@ -58,6 +60,10 @@ struct BwdParams {
   float scale_log2e;
   int num_blk;  // set by the launchers
 };
+
+// Row length of the backward's per-row statistics in the workspace.
+constexpr int kStatAlign = 64;
+inline int stat_stride_for(int seqlen) { return (seqlen + kStatAlign - 1) / kStatAlign * kStatAlign; }
 
 hipError_t run_fwd_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t run_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream);

@@ -42,8 +42,10 @@ def test_status_strings():
 
 def test_workspace_bytes():
     lib = lca.load_library()
-    assert lib.attn_bwd_workspace_bytes(1, 28, 32768) == 4 * 28 * 32768
-    assert lib.attn_bwd_workspace_bytes(2, 3, 5) == 120
+    # two fp32 arrays [B, Hq, S rounded up to 64]
+    assert lib.attn_bwd_workspace_bytes(1, 28, 32768) == 8 * 28 * 32768
+    assert lib.attn_bwd_workspace_bytes(2, 3, 5) == 8 * 2 * 3 * 64
+    assert lib.attn_bwd_workspace_bytes(1, 1, 65) == 8 * 128
     assert lib.attn_bwd_workspace_bytes(0, 3, 5) == 0
     assert lib.attn_bwd_workspace_bytes(1, -1, 5) == 0
 
