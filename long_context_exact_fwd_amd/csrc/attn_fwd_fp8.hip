@@ -1,8 +1,306 @@
-// FP8 E4M3 forward kernel for gfx950 (placeholder until the kernel lands).
+// FP8 (OCP E4M3FN) forward kernel for gfx950.
+//
+// Same tiled online-softmax method as the bf16 forward ("ms-swift集成FlashAttention
+// 2/3，长文本训练更高效", section "FlashAttention 如何破局"), with the FP8 datatype
+// that the same page's FA-3 paragraph names and per-tensor scaling of E4M3 data
+// as in the Q-Galore section of "ms-swift支持GPU显存碎片整理提升利用率":
+//   S = (Q8 K8^T) * descale_q * descale_k * scale, online softmax in fp32,
+//   P rounded to E4M3 for the PV product, O = (P8 V8) * descale_v / l,
+//   l summed from the fp32 probabilities.
+//
+// Both products run on v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 operands, unit
+// block scales, fp32 accumulate). Work split as in the bf16 kernel: 4 waves of
+// 32 queries per workgroup, two workgroups per CU, 64-key K/V tiles copied
+// into LDS by buffer loads, double-buffered.
+//   * S^T = K Q^T: lane (n, h) supplies bytes [64t + 32h, +32) of its row for
+//     both operands (the lane-to-k order of an MFMA is the same for A and B,
+//     so any common byte choice contracts every d exactly once).
+//   * P^T as the B operand of O^T += V^T P^T: byte 8q + e of lane (n, h) is the
+//     probability of key 16q + 8h + e, which is where the score C layout of
+//     the perm_rows key order already puts it (register 8(q & 1) + e of key
+//     block q / 2).
+//   * V^T fragments come from ds_read_b64_tr_b8: in each 16-lane group,
+//     destination lane t gets byte t % 8 of the 8-byte segments addressed by
+//     source lanes t / 8 + 2e (e = 0..7), so source lane s points at key row
+//     16q + 8h + s / 2, column half s % 2 of the lane group's 16 d-columns.
+//   * v_cvt_pk_fp8_f32 rounds to nearest even and turns values above 464
+//     into NaN. The exponent offset keeps P at most 2^8.5: the running maximum
+//     used for exponentiation is at most 0.5 (log2 units) stale, and 8 is
+//     subtracted so that small probabilities keep E4M3 precision instead of
+//     flushing to zero; the offset cancels in O = acc / l and is added back
+//     in the LSE.
+#include "attn_device.h"
 #include "attn_internal.h"
 
 namespace mi355attn {
 
-hipError_t run_fwd_fp8(const Fp8FwdParams&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kD = 128;       // head dim (bytes per fp8 row)
+constexpr int kBN = 64;       // keys per tile
+constexpr int kWaves = 4;
+constexpr int kBM = 32 * kWaves;
+constexpr int kTileBytes = kBN * kD;
+constexpr float kP8Offset = 8.0f;       // log2 units subtracted from the running maximum
+constexpr float kP8Threshold = 0.5f;    // lazy rescale threshold for the fp8 path
+
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  // formats 0/0 = E4M3 for A and B; E8M0 block scales 127 = 1.0
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// K tile: 64 rows x 8 chunks of 16 bytes; chunk c of row r at c ^ fK(r), where
+// fK spreads the 8 rows perm_rows reads together over 8 chunk positions.
+__device__ __forceinline__ int fk_swz(int row) { return (row & 3) | ((row >> 1) & 4); }
+// V tile: chunk c of row r at c ^ (r & 7): the 8 rows of one transposing read
+// then cover all 32 banks.
+__device__ __forceinline__ int fv_swz(int row) { return row & 7; }
+
+__device__ __forceinline__ uint32_t lds_read_u32x4_as(const uint8_t* base, int byte_off, int which) {
+  return (*LDS_PTR(const u32x4, base + byte_off))[which];
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_fp8_kernel(Fp8FwdParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[kTileBytes];
+  __shared__ int red[2][kWaves];
+  constexpr int NI = kTileBytes / (kWaves * 1024);  // DMA instructions per wave per tensor and tile
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 31;
+  const int h = lane >> 5;
+
+  const int bh = blockIdx.x;
+  const int b = bh / p.hq;
+  const int hq = bh - b * p.hq;
+  const int hk = hq / (p.hq / p.hkv);
+  const int qblk = p.num_qblk - 1 - (int)blockIdx.y;
+  const int my_q = qblk * kBM + wave * 32 + n;
+  const bool q_ok = my_q < p.seqlen;
+
+  const int q_stride = p.hq * kD;  // bytes
+  const int kv_stride = p.hkv * kD;
+  const uint8_t* qg = p.q + (size_t)b * p.seqlen * q_stride + hq * kD;
+  const uint8_t* kg = p.k + (size_t)b * p.seqlen * kv_stride + hk * kD;
+  const uint8_t* vg = p.v + (size_t)b * p.seqlen * kv_stride + hk * kD;
+
+  int kstart = 0, kend = 0;
+  if (q_ok) {
+    int s0, s1;
+    segment_of(p.cu_seqlens, p.num_seqs, p.seqlen, my_q, s0, s1);
+    kstart = s0;
+    kend = CAUSAL ? my_q + 1 : s1;
+  }
+  const int lo_min = __builtin_amdgcn_readfirstlane(wave_min(q_ok ? kstart : INT32_MAX));
+  const int hi_max = __builtin_amdgcn_readfirstlane(wave_max(q_ok ? kend : INT32_MIN));
+  const int lo_max = __builtin_amdgcn_readfirstlane(wave_max(q_ok ? kstart : INT32_MIN));
+  const int hi_min = __builtin_amdgcn_readfirstlane(wave_min(q_ok ? kend : INT32_MAX));
+  if (lane == 0) {
+    red[0][wave] = lo_min;
+    red[1][wave] = hi_max;
+  }
+  __syncthreads();
+  int wg_lo = INT32_MAX, wg_hi = INT32_MIN;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    wg_lo = min(wg_lo, red[0][w]);
+    wg_hi = max(wg_hi, red[1][w]);
+  }
+  wg_lo = __builtin_amdgcn_readfirstlane(wg_lo);
+  wg_hi = __builtin_amdgcn_readfirstlane(wg_hi);
+  const int tile_begin = wg_hi > wg_lo ? wg_lo / kBN : 0;
+  const int tile_end = wg_hi > wg_lo ? (wg_hi + kBN - 1) / kBN : 0;
+
+  // Q as B operands: k-step t, bytes [64t + 32h, +32) of the lane's query row.
+  i32x8 qf[2];
+  {
+    const uint8_t* qrow = qg + (size_t)min(my_q, p.seqlen - 1) * q_stride + 32 * h;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(qrow + 64 * t);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(qrow + 64 * t + 16);
+      qf[t] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+  }
+
+  // LDS byte offsets (tile-relative).
+  const int krow = perm_rows(n);
+  int koff[2][2];  // [t][half of the 32 bytes]: K row krow, chunk 4t + 2h + i
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) koff[t][i] = krow * kD + ((4 * t + 2 * h + i) ^ fk_swz(krow)) * 16;
+  int voff[4];  // V^T source address of key step q = 0 for d block db
+  {
+    const int g = (lane >> 4) & 1;  // which 16 d-columns of the 32-wide block this lane group covers
+    const int s = lane & 15;
+    const int row = 8 * h + (s >> 1);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) voff[db] = row * kD + ((2 * db + g) ^ fv_swz(row)) * 16 + 8 * (s & 1);
+  }
+  uint32_t ld_koff[NI], ld_voff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int off = (i * kWaves + wave) * 1024 + lane * 16;
+    const int row = off / kD;
+    const int pc = (off % kD) / 16;
+    ld_koff[i] = (uint32_t)(row * kv_stride + (pc ^ fk_swz(row)) * 16);
+    ld_voff[i] = (uint32_t)(row * kv_stride + (pc ^ fv_swz(row)) * 16);
+  }
+  auto issue_tile = [&](int t0, auto buf_c) {
+    uint8_t* kd = decltype(buf_c)::value ? k_lds1 : k_lds0;
+    uint8_t* vd = decltype(buf_c)::value ? v_lds1 : v_lds0;
+    const uint32_t nbytes = (uint32_t)(p.seqlen - t0) * (uint32_t)kv_stride;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)t0 * kv_stride, nbytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)t0 * kv_stride, nbytes);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int el = (i * kWaves + wave) * 1024;
+      dma16_buf(rk, ld_koff[i], kd + el);
+      dma16_buf(rv, ld_voff[i], vd + el);
+    }
+  };
+
+  const float dq = p.descale_q[0], dk = p.descale_k[0], dv = p.descale_v[0];
+  const float c = p.scale * dq * dk * kLog2e;  // raw fp8 dot product -> log2 units
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+  float m_run = kMaxInit;
+  float l_run = 0.f;
+
+  if (tile_begin < tile_end) issue_tile(tile_begin * kBN, std::integral_constant<int, 0>{});
+  wait_dma();
+  __syncthreads();
+
+  auto tile_body = [&](int it, auto cur_c) {
+    constexpr int cur = decltype(cur_c)::value;
+    const int t0 = it * kBN;
+    if (it + 1 < tile_end) issue_tile(t0 + kBN, std::integral_constant<int, cur ^ 1>{});
+    if ((t0 < hi_max) && (t0 + kBN > lo_min)) {
+      const bool full = (t0 >= lo_max) && (t0 + kBN <= hi_min);
+      const uint8_t* ks = cur ? k_lds1 : k_lds0;
+      const uint8_t* vs = cur ? v_lds1 : v_lds0;
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const u32x4 lo = *LDS_PTR(const u32x4, ks + koff[t][0] + kb * 32 * kD);
+          const u32x4 hi = *LDS_PTR(const u32x4, ks + koff[t][1] + kb * 32 * kD);
+          const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          s[kb] = mfma_fp8(a, qf[t], s[kb]);
+        }
+      }
+      if (!full) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = t0 + kb * 32 + c_key(r, h);
+            s[kb][r] = (key < kstart || key >= kend) ? -INFINITY : s[kb][r];
+          }
+      }
+      float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = max3f(mx, s[0][r], s[1][r]);
+      mx = max_lane_halves(mx);
+      const float m_tile = mx * c;
+      if (__any(m_tile > m_run + kP8Threshold)) {
+        const float m_new = fmaxf(m_run, m_tile);
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] *= alpha;
+        m_run = m_new;
+      }
+      const float neg_m = kP8Offset - m_run;
+      // P^T bytes: byte 8q + e = key 16q + 8h + e = register 8(q & 1) + e of key block q / 2
+      i32x8 pf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float e[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          e[r] = fast_exp2(__builtin_fmaf(s[kb][r], c, neg_m));
+          l_run += e[r];
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w], e[4 * w + 1], 0, false);
+          word = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w + 2], e[4 * w + 3], word, true);
+          pf[4 * kb + w] = word;
+        }
+      }
+      // O^T += V^T P^T
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        i32x8 a;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              LDS_PTR(i32x2, const_cast<uint8_t*>(vs) + voff[db] + q * 16 * kD));
+          a[2 * q] = t[0];
+          a[2 * q + 1] = t[1];
+        }
+        acc[db] = mfma_fp8(a, pf, acc[db]);
+      }
+    }
+    wait_dma();
+    __syncthreads();
+  };
+
+  for (int it = tile_begin; it < tile_end; it += 2) {
+    tile_body(it, std::integral_constant<int, 0>{});
+    if (it + 1 < tile_end) tile_body(it + 1, std::integral_constant<int, 1>{});
+  }
+
+  // O = acc * descale_v / l; LSE = (m - offset + log2 l) * ln 2
+  const float l_tot = sum_lane_halves(l_run);
+  const float inv = l_tot > 0.f ? dv / l_tot : 0.f;
+  if (q_ok) {
+    __bf16* orow = p.o + ((size_t)b * p.seqlen + my_q) * (size_t)(p.hq * kD) + hq * kD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 w;
+        w[0] = (__bf16)(acc[db][4 * g + 0] * inv);
+        w[1] = (__bf16)(acc[db][4 * g + 1] * inv);
+        w[2] = (__bf16)(acc[db][4 * g + 2] * inv);
+        w[3] = (__bf16)(acc[db][4 * g + 3] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * g + 4 * h) = w;
+      }
+    if (h == 0) {
+      p.lse[((size_t)b * p.hq + hq) * p.seqlen + my_q] =
+          l_tot > 0.f ? (m_run - kP8Offset + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+template <bool CAUSAL>
+hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream) {
+  Fp8FwdParams q = p;
+  q.num_qblk = (p.seqlen + kBM - 1) / kBM;
+  dim3 grid(p.batch * p.hq, q.num_qblk);
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL>), grid, dim3(kWaves * 64), 0, stream, q);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t run_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream) {
+  return p.causal ? launch_fwd_fp8<true>(p, stream) : launch_fwd_fp8<false>(p, stream);
+}
 
 }  // namespace mi355attn
