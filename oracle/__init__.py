@@ -17,5 +17,6 @@ from .attention import (  # noqa: F401
     attention_bwd,
     attention_bwd_group,
     attention_dq_rows,
+    attention_dkdv_rows,
     e4m3_decode,
 )

@@ -323,6 +323,50 @@ def attention_dq_rows(q, k, v, do, picks: Iterable[tuple[int, int, int]], *, cau
     return out
 
 
+def attention_dkdv_rows(q, k, v, do, picks: Iterable[tuple[int, int, int]], *, causal: bool, scale: float,
+                        cu_seqlens=None, workers: Optional[int] = None):
+    """dK and dV for selected (b, kv_head, j) key rows: returns (dK rows [n, D], dV rows [n, D]).
+
+    Key j collects a term from every query row i that sees it, in each of the
+    G query heads of its group: dV_j = sum_h sum_i P_ij dO_i and
+    dK_j = scale sum_h sum_i P_ij (dO_i . V_j - Delta_i) Q_i, with
+    P_ij = exp(s_ij - LSE_i) and Delta_i = dO_i . O_i. Those need LSE_i and O_i
+    of every such row, so the group's full forward (attention_fwd on its query
+    heads) runs first; the per-key sums then follow the definition directly.
+    """
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = _group_size(Hq, Hkv)
+    seg_start, seg_end = segment_bounds(S, cu_seqlens)
+    picks = list(picks)
+    stats = {}
+    for b, kvh in sorted({(int(b), int(kvh)) for b, kvh, _ in picks}):
+        qg = np.asarray(q[b:b + 1, :, kvh * G:(kvh + 1) * G], dtype=np.float64)
+        kg = np.asarray(k[b:b + 1, :, kvh:kvh + 1], dtype=np.float64)
+        vg = np.asarray(v[b:b + 1, :, kvh:kvh + 1], dtype=np.float64)
+        dog = np.asarray(do[b:b + 1, :, kvh * G:(kvh + 1) * G], dtype=np.float64)
+        o, lse = attention_fwd(qg, kg, vg, causal=causal, scale=scale, cu_seqlens=cu_seqlens, workers=workers)
+        delta = np.sum(dog[0] * o[0], axis=-1)  # [S, G]
+        stats[(b, kvh)] = (qg[0], dog[0], lse[0], delta)
+    dk = np.zeros((len(picks), D), dtype=np.float64)
+    dv = np.zeros((len(picks), D), dtype=np.float64)
+    for n, (b, kvh, j) in enumerate(picks):
+        qg, dog, lse, delta = stats[(int(b), int(kvh))]
+        # queries that see key j: same segment, and not before j when causal
+        lo = j if causal else int(seg_start[j])
+        hi = int(seg_end[j])
+        kj = np.asarray(k[b, j, kvh], dtype=np.float64)
+        vj = np.asarray(v[b, j, kvh], dtype=np.float64)
+        for h in range(G):
+            qi = qg[lo:hi, h]
+            doi = dog[lo:hi, h]
+            p = np.exp(scale * (qi @ kj) - lse[h, lo:hi])
+            dv[n] += p @ doi
+            ds = p * (doi @ vj - delta[lo:hi, h])
+            dk[n] += scale * (ds @ qi)
+    return dk, dv
+
+
 # ---------------------------------------------------------------------------
 # FP8 E4M3FN decoding (OCP 8-bit floating point, E4M3 variant)
 # ---------------------------------------------------------------------------

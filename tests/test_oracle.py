@@ -362,6 +362,22 @@ def test_group_backward_and_row_dq_match_full_backward(lengths, monkeypatch):
     np.testing.assert_allclose(rq, np.array([dq[0, i, h] for _, h, i in picks]), atol=1e-13)
 
 
+@pytest.mark.parametrize("causal,lengths", [(True, None), (False, None), (True, [9, 20, 11]), (False, [9, 20, 11])])
+def test_key_row_dkdv_match_full_backward(causal, lengths):
+    S, D, Hq, Hkv = 40, 8, 6, 2
+    q, k, v, do = (_rand((2, S, Hq, D), 80), _rand((2, S, Hkv, D), 81), _rand((2, S, Hkv, D), 82),
+                   _rand((2, S, Hq, D), 83))
+    cu = None
+    if lengths is not None:
+        q, k, v, do = q[:1], k[:1], v[:1], do[:1]
+        cu = cu_seqlens_from_lengths(lengths)
+    _, dk, dv = oracle.attention_bwd(q, k, v, do, causal=causal, scale=0.3, cu_seqlens=cu, workers=2)
+    picks = [(b, kv, j) for b in range(q.shape[0]) for kv in range(Hkv) for j in (0, 1, 8, 9, 28, 39)]
+    rk, rv = oracle.attention_dkdv_rows(q, k, v, do, picks, causal=causal, scale=0.3, cu_seqlens=cu, workers=2)
+    np.testing.assert_allclose(rk, np.array([dk[b, j, kv] for b, kv, j in picks]), atol=1e-13)
+    np.testing.assert_allclose(rv, np.array([dv[b, j, kv] for b, kv, j in picks]), atol=1e-13)
+
+
 # ------------------------------------------------------------------- fp8 -----
 
 def test_e4m3_decoder_matches_torch_for_all_codes():

@@ -1,0 +1,152 @@
+"""GPU parity at the full workload sizes, in the launch configuration bench.py times.
+
+The kernels run on the whole seeded inputs of each workload (mid, gqa32k,
+packed32k, fp8_64k). The fp64 oracle checks a seeded sample of outputs that it
+can compute one by one: forward rows (O and LSE), dQ rows, and dK/dV rows of
+one kv group (the oracle runs that group's full forward for the LSE and Delta
+of every query row). Gradient sums that hold over whole tensors are checked
+on the full GPU outputs: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i per kv
+head and segment (summed over the group's query heads).
+
+Tolerances as in the small-shape tests, applied to the sampled sets: O
+|err| <= max(1e-2, ulp) and rel-L2 <= 5e-3, LSE <= 1e-3, gradients rel-L2
+<= 1e-2 per tensor, fp8 O rel-L2 <= 5e-2.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+from tests.gpu_helpers import (TOL_FP8_REL, TOL_GRAD_REL, TOL_LSE, check_fwd, dev_i32, dev_u8, host, max_abs,
+                               rel_l2)
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_rows(w, cu, seed, count):
+    """Query/key rows: 0, 1, S-1, each segment's first and last row, plus seeded uniform rows."""
+    must = [0, 1, w.seqlen - 1]
+    if cu is not None:
+        for a, b in zip(cu[:-1], cu[1:]):
+            must += [int(a), int(b) - 1]
+    return si.sample_indices(seed, w.seqlen, count, must=must)
+
+
+def _sample_heads(n, seed):
+    return si.sample_indices(seed + 7, n, 2, must=[0, n - 1])
+
+
+def _upload(x):
+    import long_context_exact_fwd_amd as lca
+    return [lca.bf16_from_bits(bits, "cuda") for bits in (x.q_bits, x.k_bits, x.v_bits)]
+
+
+def _forward_rows_check(w, x, o, lse, picks, tag):
+    qv, kv, vv = x.values("q"), x.values("k"), x.values("v")
+    ro, rl = oracle.attention_fwd_rows(qv, kv, vv, picks, causal=w.causal, scale=w.scale, cu_seqlens=x.cu_seqlens)
+    go = np.stack([o[b, i, h] for b, h, i in picks])
+    gl = np.array([lse[b, h, i] for b, h, i in picks])
+    check_fwd(go, gl, ro, rl, tag=tag)
+    return qv, kv, vv
+
+
+def _run_fwd_bwd(name, backward):
+    import torch
+    import long_context_exact_fwd_amd as lca
+    w = si.WORKLOADS[name]
+    print(f"full-size case {name}: B={w.batch} Hq={w.hq} Hkv={w.hkv} S={w.seqlen} D={w.head_dim} causal={w.causal} "
+          f"packed={w.packed} seed={w.seed} backward={backward}", flush=True)
+    x = si.workload_inputs(w, with_do=backward)
+    q, k, v = _upload(x)
+    cu = dev_i32(x.cu_seqlens) if x.cu_seqlens is not None else None
+    kw = dict(causal=w.causal, cu_seqlens=cu, scale=w.scale)
+    o, lse = lca.fwd(q, k, v, **kw)
+    if backward:
+        do = lca.bf16_from_bits(x.do_bits, "cuda")
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(lca.bwd_workspace_bytes(w.batch, w.hq, w.seqlen) // 4, dtype=torch.float32, device="cuda")
+        for ph in (lca.BWD_DELTA, lca.BWD_DKDV, lca.BWD_DQ):  # as bench.py launches them
+            lca.bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, phases=ph, **kw)
+    torch.cuda.synchronize()
+    print(f"{name}: GPU done", flush=True)
+    o_h, lse_h = host(o), host(lse)
+    rows = _sample_rows(w, x.cu_seqlens, w.seed, 128)
+    heads = _sample_heads(w.hq, w.seed)
+    picks = [(b, int(h), int(i)) for b in range(w.batch) for h in heads for i in rows]
+    qv, kv, vv = _forward_rows_check(w, x, o_h, lse_h, picks, tag=f"{name} fwd ({len(picks)} rows)")
+    if not backward:
+        return
+    dov = x.values("do")
+    dq_h, dk_h, dv_h = host(dq), host(dk), host(dv)
+    rq = oracle.attention_dq_rows(qv, kv, vv, dov, picks, causal=w.causal, scale=w.scale, cu_seqlens=x.cu_seqlens)
+    gq = np.stack([dq_h[b, i, h] for b, h, i in picks])
+    e_q = rel_l2(gq, rq)
+    kvh = int(si.sample_indices(w.seed + 11, w.hkv, 1)[0])
+    keys = _sample_rows(w, x.cu_seqlens, w.seed + 13, 128)
+    kpicks = [(0, kvh, int(j)) for j in keys]
+    rk, rv = oracle.attention_dkdv_rows(qv, kv, vv, dov, kpicks, causal=w.causal, scale=w.scale,
+                                        cu_seqlens=x.cu_seqlens)
+    gk = np.stack([dk_h[b, j, h] for b, h, j in kpicks])
+    gv = np.stack([dv_h[b, j, h] for b, h, j in kpicks])
+    e_k, e_v = rel_l2(gk, rk), rel_l2(gv, rv)
+    print(f"{name} bwd sampled: dQ relL2={e_q:.3e} ({len(picks)} rows) dK relL2={e_k:.3e} dV relL2={e_v:.3e} "
+          f"({len(kpicks)} keys of kv head {kvh})", flush=True)
+    assert np.all(np.isfinite(dq_h)) and np.all(np.isfinite(dk_h)) and np.all(np.isfinite(dv_h))
+    assert max(e_q, e_k, e_v) <= TOL_GRAD_REL
+    # whole-tensor identities per kv head and segment
+    G = w.hq // w.hkv
+    bounds = list(zip(x.cu_seqlens[:-1], x.cu_seqlens[1:])) if x.cu_seqlens is not None else [(0, w.seqlen)]
+    worst_k = worst_v = 0.0
+    for b in range(w.batch):
+        for h in range(w.hkv):
+            for a, e in bounds:
+                sk = dk_h[b, a:e, h].sum(axis=0)
+                worst_k = max(worst_k, float(np.linalg.norm(sk) / np.linalg.norm(dk_h[b, a:e, h])))
+                sv = dv_h[b, a:e, h].sum(axis=0)
+                ref = dov[b, a:e, h * G:(h + 1) * G].sum(axis=(0, 1))
+                worst_v = max(worst_v, rel_l2(sv, ref))
+    print(f"{name} sums: |sum dK| / |dK| <= {worst_k:.3e}, sum dV vs sum dO relL2 <= {worst_v:.3e}", flush=True)
+    # sum_j dK_j = 0 exactly; bf16 rounding of each row leaves noise far below the norm of dK itself
+    assert worst_k <= 1e-2 and worst_v <= 1e-2
+
+
+def test_mid_full_forward_sampled():
+    """B=2, H=32, S=8192, D=128 causal forward."""
+    _run_fwd_bwd("mid", backward=False)
+
+
+def test_gqa32k_full_forward_backward_sampled():
+    """B=1, Hq=28, Hkv=4, S=32768, D=128 causal forward + backward (the bench workload)."""
+    _run_fwd_bwd("gqa32k", backward=True)
+
+
+def test_packed32k_full_forward_backward_sampled():
+    """B=1, Hq=14, Hkv=2, S=32768 packed (seed-4 lengths), D=128 causal forward + backward."""
+    _run_fwd_bwd("packed32k", backward=True)
+
+
+def test_fp8_64k_full_forward_sampled():
+    """B=1, Hq=8, Hkv=1, S=65536, D=128 causal fp8 forward, O bf16 and LSE fp32."""
+    import torch
+    import long_context_exact_fwd_amd as lca
+    w = si.WORKLOADS["fp8_64k"]
+    print(f"full-size case fp8_64k: Hq={w.hq} Hkv={w.hkv} S={w.seqlen} seed={w.seed}", flush=True)
+    x = si.workload_inputs(w)
+    q8, k8, v8 = dev_u8(x.q_bits), dev_u8(x.k_bits), dev_u8(x.v_bits)
+    ds = [torch.tensor([float(d)], dtype=torch.float32, device="cuda") for d in x.descale]
+    o, lse = lca.fwd_fp8(q8, k8, v8, *ds, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    o_h, lse_h = host(o), host(lse)
+    rows = _sample_rows(w, None, w.seed, 128)
+    heads = _sample_heads(w.hq, w.seed)
+    picks = [(0, int(h), int(i)) for h in heads for i in rows]
+    qv = oracle.e4m3_decode(x.q_bits) * float(x.descale[0])
+    kv = oracle.e4m3_decode(x.k_bits) * float(x.descale[1])
+    vv = oracle.e4m3_decode(x.v_bits) * float(x.descale[2])
+    ro, rl = oracle.attention_fwd_rows(qv, kv, vv, picks, causal=True, scale=w.scale)
+    go = np.stack([o_h[0, i, h] for _, h, i in picks])
+    gl = np.array([lse_h[0, h, i] for _, h, i in picks])
+    rr, rlse = rel_l2(go, ro), max_abs(gl, rl)
+    print(f"fp8_64k sampled ({len(picks)} rows): O relL2={rr:.3e} LSE maxabs={rlse:.3e}", flush=True)
+    assert np.all(np.isfinite(o_h)) and np.all(np.isfinite(lse_h))
+    assert rr <= TOL_FP8_REL and rlse <= TOL_LSE
