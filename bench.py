@@ -4,10 +4,12 @@
 One step is the whole hot path on one batch of synthetic input that already
 sits in HBM: attn_fwd, then the three backward kernels (Delta, dK/dV, dQ)
 through attn_bwd_phases. That is the same work attn_bwd does, split so each
-kernel can be bracketed with HIP events on the stream it runs on.
+kernel can be bracketed with HIP events on the stream it runs on (the
+binding launches on torch's current stream, which the events record on).
 
-Workload (one GPU's Ulysses head share of a Qwen2.5-7B-shaped layer): B=1,
-Hq=28, Hkv=4, S=32768, D=128, causal, bf16 inputs drawn N(0, 1) from seed 3.
+Headline workload (one GPU's Ulysses head share of a Qwen2.5-7B-shaped layer):
+B=1, Hq=28, Hkv=4, S=32768, D=128, causal, bf16 inputs drawn N(0, 1) from
+seed 3.
 
 FLOPs are algorithmic: only visible (i, j) pairs count, 4*D per pair for the
 forward (QK^T and PV) and 10*D per pair for the backward (QK^T, dO V^T,
@@ -16,16 +18,17 @@ not counted. Per kernel: fwd 4*D, dK/dV 8*D, dQ 2*D per pair.
 
 Prints one JSON line. The roofline object describes the kernel with the
 largest share of the step time. ``cpu_baseline`` times the fp64 oracle on a
-bounded sample of the same workload on the host cores.
+bounded sample of the same workload on the host cores. ``workloads`` holds
+the other configurations measured the same way (mid: bf16 forward; packed32k:
+packed fwd+bwd; fp8_64k: fp8 forward against the fp8 dense peak).
 
-    python bench.py [--steps 20] [--warmup 3] [--gpus 1]
+    python bench.py [--steps 20] [--warmup 3] [--gpus 1] [--no-secondary]
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -35,10 +38,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA peak
 PEAK_HBM_GBS = 8000.0
 
 
 def _pairs(seqlen: int, causal: bool, cu=None) -> float:
+    """Visible (query, key) pairs of one (batch, head)."""
     if cu is not None:
         lens = [int(b) - int(a) for a, b in zip(cu[:-1], cu[1:])]
         return float(sum(L * (L + 1) // 2 if causal else L * L for L in lens))
@@ -49,7 +54,11 @@ KERNEL_SOURCES = {
     "attn_fwd_bf16_kernel": ("attn_fwd.hip", "attn_device.h", "attn_internal.h"),
     "attn_bwd_dkdv_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h"),
     "attn_bwd_dq_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h"),
+    "attn_bwd_delta_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h"),
+    "attn_fwd_fp8_kernel": ("attn_fwd_fp8.hip", "attn_device.h", "attn_internal.h"),
 }
+KERNEL_OF_PHASE = {"attn_fwd": "attn_fwd_bf16_kernel", "bwd_delta": "attn_bwd_delta_kernel",
+                   "bwd_dkdv": "attn_bwd_dkdv_kernel", "bwd_dq": "attn_bwd_dq_kernel"}
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -78,7 +87,6 @@ def _traffic(kernel: str):
 
 def cpu_baseline(w, x, sample_len: int):
     """Oracle (fp64, numpy) fwd+bwd of one kv group over a causal prefix of the same inputs."""
-    import numpy as np
     import oracle
     workers = min(16, len(os.sched_getaffinity(0)))
     L = min(sample_len, w.seqlen)
@@ -103,14 +111,118 @@ def cpu_baseline(w, x, sample_len: int):
     }
 
 
+class Timer:
+    """HIP events around each named phase of a step, on torch's current stream."""
+
+    def __init__(self, names, steps):
+        import torch
+        self.names = names
+        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+
+    def mark(self, step, j):
+        self.ev[step][j].record()
+
+    def per_phase_ms(self):
+        n = len(self.ev)
+        return {name: sum(e[j].elapsed_time(e[j + 1]) for e in self.ev) / n for j, name in enumerate(self.names)}
+
+
+def run_steps(step, names, steps, warmup):
+    """Warm up, then time exactly `steps` steps between two synchronisations; returns (ms/step, per-phase ms)."""
+    import torch
+    for _ in range(warmup):
+        step(None, 0)
+    torch.cuda.synchronize()
+    tm = Timer(names, steps)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        step(tm, i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps, tm.per_phase_ms()
+
+
+def bf16_case(w, x, dev):
+    """Device buffers and a step function (fwd, then Delta, dK/dV, dQ if the workload has a backward)."""
+    import torch
+    import long_context_exact_fwd_amd as lca
+    up = lca.bf16_from_bits
+    q, k, v = up(x.q_bits, dev), up(x.k_bits, dev), up(x.v_bits, dev)
+    cu = torch.from_numpy(x.cu_seqlens).to(dev) if x.cu_seqlens is not None else None
+    B, S, Hq = w.batch, w.seqlen, w.hq
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    kw = dict(causal=w.causal, cu_seqlens=cu, scale=w.scale)
+    names = ["attn_fwd"]
+    if w.backward:
+        do = up(x.do_bits, dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(lca.bwd_workspace_bytes(B, Hq, S) // 4, dtype=torch.float32, device=dev)
+        names += ["bwd_delta", "bwd_dkdv", "bwd_dq"]
+
+    def step(tm, i):
+        if tm is not None:
+            tm.mark(i, 0)
+        lca.fwd(q, k, v, out=o, lse=lse, **kw)
+        if tm is not None:
+            tm.mark(i, 1)
+        if w.backward:
+            for j, ph in enumerate((lca.BWD_DELTA, lca.BWD_DKDV, lca.BWD_DQ)):
+                lca.bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, phases=ph, **kw)
+                if tm is not None:
+                    tm.mark(i, j + 2)
+
+    return step, names
+
+
+def fp8_case(w, x, dev):
+    import torch
+    import long_context_exact_fwd_amd as lca
+    q8, k8, v8 = (torch.from_numpy(b).to(dev) for b in (x.q_bits, x.k_bits, x.v_bits))
+    ds = [torch.tensor([float(d)], dtype=torch.float32, device=dev) for d in x.descale]
+    o = torch.empty((w.batch, w.seqlen, w.hq, w.head_dim), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, w.hq, w.seqlen), dtype=torch.float32, device=dev)
+
+    def step(tm, i):
+        if tm is not None:
+            tm.mark(i, 0)
+        lca.fwd_fp8(q8, k8, v8, *ds, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        if tm is not None:
+            tm.mark(i, 1)
+
+    return step, ["attn_fwd_fp8"]
+
+
+def secondary(name, steps, warmup, dev):
+    """Time one of the other workloads the same way; returns a dict for the `workloads` object."""
+    import seeded_inputs as si
+    w = si.WORKLOADS[name]
+    x = si.workload_inputs(w)
+    step, names = (fp8_case if w.fp8 else bf16_case)(w, x, dev)
+    ms, per = run_steps(step, names, steps, warmup)
+    pairs = _pairs(w.seqlen, w.causal, x.cu_seqlens) * w.batch * w.hq
+    flops = (14.0 if w.backward else 4.0) * w.head_dim * pairs
+    peak = PEAK_FP8_TFLOPS if w.fp8 else PEAK_BF16_TFLOPS
+    tf = flops / (ms * 1e-3) / 1e12
+    return {
+        "config": f"B={w.batch} Hq={w.hq} Hkv={w.hkv} S={w.seqlen} D={w.head_dim} causal={w.causal} "
+                  f"packed={w.packed} {'fp8 e4m3' if w.fp8 else 'bf16'} {'fwd+bwd' if w.backward else 'fwd'}, "
+                  f"N(0,1) seed {w.seed}",
+        "tflops": round(tf, 2), "pct_of_peak": round(100.0 * tf / peak, 2), "peak_tflops": peak,
+        "ms_per_step": round(ms, 4), "steps": steps, "phases_ms": {n: round(t, 4) for n, t in per.items()},
+    }
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="gqa32k")
     ap.add_argument("--cpu-sample-len", type=int, default=32768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the mid / packed32k / fp8_64k measurements")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB (counter calibration)")
     a = ap.parse_args(argv)
@@ -119,82 +231,36 @@ def main(argv=None) -> int:
               f"head share and no collectives are implemented", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
     import seeded_inputs as si
     import long_context_exact_fwd_amd as lca
 
-    w = si.WORKLOADS[a.workload]
-    if w.fp8 or not w.backward:
-        print("bench.py: the headline step is bf16 fwd+bwd; pick a workload with a backward", file=sys.stderr)
-        return 2
-    lib = lca.load_library()
+    lca.load_library()
+    w = si.WORKLOADS["gqa32k"]
     x = si.workload_inputs(w)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    up = lca.bf16_from_bits
-    q, k, v, do = up(x.q_bits), up(x.k_bits), up(x.v_bits), up(x.do_bits)
-    cu = torch.from_numpy(x.cu_seqlens).to(dev) if x.cu_seqlens is not None else None
-    B, S, Hq, Hkv, D = w.batch, w.seqlen, w.hq, w.hkv, w.head_dim
-    o = torch.empty_like(q)
-    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(lca.bwd_workspace_bytes(B, Hq, S) // 4, dtype=torch.float32, device=dev)
-    kw = dict(causal=w.causal, cu_seqlens=cu, scale=w.scale)
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        lca.fwd(q, k, v, out=o, lse=lse, **kw)
-        if ev is not None:
-            ev[1].record()
-        lca.bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, phases=lca.BWD_DELTA, **kw)
-        if ev is not None:
-            ev[2].record()
-        lca.bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, phases=lca.BWD_DKDV, **kw)
-        if ev is not None:
-            ev[3].record()
-        lca.bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, phases=lca.BWD_DQ, **kw)
-        if ev is not None:
-            ev[4].record()
-
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    print(f"bench: warmup {a.warmup} done, timing {a.steps} steps", file=sys.stderr, flush=True)
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    step, names = bf16_case(w, x, dev)
     t0 = time.perf_counter()
-    start.record()
-    for i in range(a.steps):
-        step(evs[i])
-    end.record()
-    torch.cuda.synchronize()
+    ms_per_step, per = run_steps(step, names, a.steps, a.warmup)
     wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / a.steps
-    names = ["attn_fwd", "bwd_delta", "bwd_dkdv", "bwd_dq"]
-    per = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / a.steps for j, n in enumerate(names)}
+    print(f"bench: {a.steps} timed steps done", file=sys.stderr, flush=True)
 
-    pairs = _pairs(S, w.causal, x.cu_seqlens) * B * Hq
+    D, Hq = w.head_dim, w.hq
+    pairs = _pairs(w.seqlen, w.causal, x.cu_seqlens) * w.batch * Hq
     flops_k = {"attn_fwd": 4.0 * D * pairs, "bwd_delta": 0.0, "bwd_dkdv": 8.0 * D * pairs, "bwd_dq": 2.0 * D * pairs}
-    step_flops = 14.0 * D * pairs
-    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    value = 14.0 * D * pairs / (ms_per_step * 1e-3) / 1e12
 
     dom = max(("attn_fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: per[n])
     achieved = flops_k[dom] / (per[dom] * 1e-3) / 1e12
-    kernel_names = {"attn_fwd": "attn_fwd_bf16_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel",
-                    "bwd_dq": "attn_bwd_dq_kernel"}
     roofline = {
         "bound": "mfma",
-        "kernel": kernel_names[dom],
+        "kernel": KERNEL_OF_PHASE[dom],
         "achieved": round(achieved, 2),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-        "traffic": _traffic(kernel_names[dom]),
+        "traffic": _traffic(KERNEL_OF_PHASE[dom]),
         "avg_launch_ms": round(per[dom], 4),
         "algorithmic_flops_per_launch": flops_k[dom],
     }
@@ -222,16 +288,25 @@ def main(argv=None) -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{w.name}: B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} causal={w.causal} packed={w.packed}, "
-                        f"N(0,1) seed {w.seed}",
-            "batch": B, "hq": Hq, "hkv": Hkv, "seq_len": S, "head_dim": D, "causal": w.causal,
+            "workload": f"gqa32k: B={w.batch} Hq={Hq} Hkv={w.hkv} S={w.seqlen} D={D} causal={w.causal} "
+                        f"packed={w.packed}, N(0,1) seed {w.seed}",
+            "batch": w.batch, "hq": Hq, "hkv": w.hkv, "seq_len": w.seqlen, "head_dim": D, "causal": w.causal,
         },
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "phases_ms": {n: round(t, 4) for n, t in per.items()},
         "wall_s_timed": round(wall, 3),
         "roofline": roofline,
         "cpu_baseline": None,
+        "workloads": None,
     }
+    if not a.no_secondary:
+        del step
+        torch.cuda.empty_cache()
+        sec_steps = max(3, min(10, a.steps))
+        result["workloads"] = {}
+        for name in ("mid", "packed32k", "fp8_64k"):
+            result["workloads"][name] = secondary(name, sec_steps, min(2, a.warmup), dev)
+            print(f"bench: {name} done", file=sys.stderr, flush=True)
     if not a.no_cpu_baseline:
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, x, a.cpu_sample_len)
