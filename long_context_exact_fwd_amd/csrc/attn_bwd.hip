@@ -93,11 +93,15 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   const int n = lane & 31;
   const int h = lane >> 5;
 
+  // Launch order: kv heads fastest, then key blocks (causal: the first key
+  // blocks see the most queries, so the heaviest start first). Workgroups are
+  // dealt round-robin to the 8 XCDs, so with up to 8 kv heads each XCD keeps
+  // working on the same kv head and shares its Q/dO tiles in its L2.
   const int bh = blockIdx.x;
   const int b = bh / p.hkv;
   const int hk = bh - b * p.hkv;
   const int G = p.hq / p.hkv;
-  const int k0 = blockIdx.y * 128;  // causal: the first key blocks see the most queries
+  const int k0 = blockIdx.y * 128;
   const int my_k = k0 + pair * 32 + n;
   const bool k_ok = my_k < p.seqlen;
   const int kv_stride = p.hkv * D;
@@ -167,10 +171,21 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
     ld_off[i] = (uint32_t)(row * q_stride + swz_dual<D>(row, (e % D) / 8) * 8) * 2u;
   }
   const size_t stat_b = (size_t)b * p.hq * p.stat_stride;
-  auto issue_step = [&](int step, auto buf_c) {
+  // Step order: query tiles from the last one down, the G heads of the group
+  // innermost. Every workgroup of a kv head starts on the same tile, so the
+  // ones running together on an XCD read the same Q/dO tiles at the same time.
+  // (g, ti) of a step are carried as scalars and advanced by one per step:
+  // no integer division in the loop.
+  auto advance = [&](int& g, int& ti) {
+    ++g;
+    if (g == G) {
+      g = 0;
+      --ti;
+    }
+  };
+  auto issue_step = [&](int g, int ti, auto buf_c) {
     constexpr int buf = decltype(buf_c)::value;
-    const int g = step / ntiles;
-    const int t0 = (tile_begin + step - g * ntiles) * kQT;
+    const int t0 = ti * kQT;
     const int hq = hk * G + g;
     const size_t row0 = ((size_t)b * p.seqlen + t0) * q_stride + hq * D;
     const uint32_t nbytes = (uint32_t)(p.seqlen - t0) * (uint32_t)q_stride * 2u;
@@ -198,7 +213,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
   const float c = p.scale_log2e;
 
-  if (nsteps > 0) issue_step(0, std::integral_constant<int, 0>{});
+  int cur_g = 0, cur_ti = tile_end - 1;  // head and query tile of the current step
+  if (nsteps > 0) issue_step(cur_g, cur_ti, std::integral_constant<int, 0>{});
   wait_dma();
   __syncthreads();
 
@@ -211,8 +227,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   if (role == 0) {
     auto body_a = [&](int step, auto cur_c) {
       constexpr int cur = decltype(cur_c)::value;
-      const int t0 = (tile_begin + step % ntiles) * kQT;
-      if (step + 1 < nsteps) issue_step(step + 1, std::integral_constant<int, cur ^ 1>{});
+      int nxt_g = cur_g, nxt_ti = cur_ti;
+      advance(nxt_g, nxt_ti);
+      const int t0 = cur_ti * kQT;
+      if (step + 1 < nsteps) issue_step(nxt_g, nxt_ti, std::integral_constant<int, cur ^ 1>{});
       const bool full = (t0 >= lo_max) && (t0 + kQT <= hi_min);
       const __bf16* qs = cur ? q_lds1 : q_lds0;
       const __bf16* gs = cur ? g_lds1 : g_lds0;
@@ -258,6 +276,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
           acc[d] = mfma32(tr_read2(gs, trlo[d] + 16 * u * D, trhi[d] + 16 * u * D), pb[u], acc[d]);
         __builtin_amdgcn_sched_barrier(0);
       }
+      cur_g = nxt_g;
+      cur_ti = nxt_ti;
       wait_dma();
       __syncthreads();
     };
@@ -268,7 +288,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   } else {
     auto body_b = [&](int step, auto cur_c) {
       constexpr int cur = decltype(cur_c)::value;
-      if (step + 1 < nsteps) issue_step(step + 1, std::integral_constant<int, cur ^ 1>{});
+      int nxt_g = cur_g, nxt_ti = cur_ti;
+      advance(nxt_g, nxt_ti);
+      if (step + 1 < nsteps) issue_step(nxt_g, nxt_ti, std::integral_constant<int, cur ^ 1>{});
       const __bf16* qs = cur ? q_lds1 : q_lds0;
       const __bf16* gs = cur ? g_lds1 : g_lds0;
       const float* st = cur ? st_lds1 : st_lds0;
@@ -306,6 +328,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
           acc[d] = mfma32(tr_read2(qs, trlo[d] + 16 * u * D, trhi[d] + 16 * u * D), db[u], acc[d]);
         __builtin_amdgcn_sched_barrier(0);
       }
+      cur_g = nxt_g;
+      cur_ti = nxt_ti;
       wait_dma();
       __syncthreads();
     };

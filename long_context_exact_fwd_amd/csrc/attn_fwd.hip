@@ -19,9 +19,12 @@
 //   * K/V tiles (64 keys) move from global memory straight into LDS
 //     (buffer_load_dwordx4 ... lds, no staging registers), double-buffered
 //     with one barrier per tile.
-//   * Tiles outside a wave's visible keys are skipped, tiles partly outside
-//     are masked per element. Every LDS address is a per-lane base computed
-//     once plus a compile-time offset, and every per-tile branch is scalar.
+//   * Software pipeline: the scores of tile j + 1 are computed in the same
+//     straight block as the exp/sum/pack of tile j, so their MFMAs interleave
+//     with the softmax VALU work; K is kept one tile ahead of V.
+//   * Tiles partly (or wholly) outside a wave's visible keys are masked per
+//     element. Every LDS address is a per-lane base computed once plus a
+//     compile-time offset, and every per-tile branch is scalar.
 #include "attn_device.h"
 #include "attn_internal.h"
 
@@ -132,18 +135,28 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_bf16_kernel(FwdParams
     ld_koff[i] = (uint32_t)(row * kv_stride + swz_b128<D>(row, pc) * 8) * 2u;
     ld_voff[i] = (uint32_t)(row * kv_stride + swz_tr_chunk<D>(row, pc) * 8) * 2u;
   }
-  auto issue_tile = [&](int t0, auto buf_c) {
+  auto issue_k = [&](int t0, auto buf_c) {
     __bf16* kd = decltype(buf_c)::value ? k_lds1 : k_lds0;
-    __bf16* vd = decltype(buf_c)::value ? v_lds1 : v_lds0;
     const uint32_t nbytes = (uint32_t)(p.seqlen - t0) * (uint32_t)kv_stride * 2u;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + (size_t)t0 * kv_stride, nbytes);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma16_buf(rk, ld_koff[i], kd + (i * kWaves + wave) * 512);
+  };
+  auto issue_v = [&](int t0, auto buf_c) {
+    __bf16* vd = decltype(buf_c)::value ? v_lds1 : v_lds0;
+    const uint32_t nbytes = (uint32_t)(p.seqlen - t0) * (uint32_t)kv_stride * 2u;
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)t0 * kv_stride, nbytes);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int lds_el = (i * kWaves + wave) * 512;
-      dma16_buf(rk, ld_koff[i], kd + lds_el);
-      dma16_buf(rv, ld_voff[i], vd + lds_el);
-    }
+    for (int i = 0; i < NI; ++i) dma16_buf(rv, ld_voff[i], vd + (i * kWaves + wave) * 512);
+  };
+  // S^T of a 64-key tile in two 32-key blocks
+  auto scores = [&](const __bf16* ks, f32x16 (&s)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < KS; ++t)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(lds_read_b128(ks, koff[t] + kb * 32 * D), qf[t], s[kb]);
   };
 
   f32x16 acc[DB];
@@ -153,74 +166,83 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_bf16_kernel(FwdParams
   float l_run = 0.f;       // partial row sum over this lane's keys
   const float c = p.scale_log2e;
 
-  if (tile_begin < tile_end) issue_tile(tile_begin * kBN, std::integral_constant<int, 0>{});
+  // Software pipeline: the scores of tile j + 1 are computed while the
+  // softmax of tile j runs, so K is kept one tile ahead of V. Tile
+  // tile_begin + i has its K in buffer i & 1 and its V in buffer i & 1.
+  const int ntile = tile_end - tile_begin;
+  f32x16 s_cur[2];
+  if (ntile > 0) {
+    issue_k(tile_begin * kBN, std::integral_constant<int, 0>{});
+    issue_v(tile_begin * kBN, std::integral_constant<int, 0>{});
+    if (ntile > 1) issue_k((tile_begin + 1) * kBN, std::integral_constant<int, 1>{});
+  }
   wait_dma();
   __syncthreads();
+  if (ntile > 0) scores(k_lds0, s_cur);
+  __syncthreads();  // K of the first tile is read before its buffer is refilled
 
-  auto tile_body = [&](int it, auto cur_c) {
-    constexpr int cur = decltype(cur_c)::value;
-    const int t0 = it * kBN;
-    if (it + 1 < tile_end) issue_tile(t0 + kBN, std::integral_constant<int, cur ^ 1>{});
-
-    if ((t0 < hi_max) && (t0 + kBN > lo_min)) {
-      const bool full = (t0 >= lo_max) && (t0 + kBN <= hi_min);
-      const __bf16* ks = cur ? k_lds1 : k_lds0;
-      const __bf16* vs = cur ? v_lds1 : v_lds0;
-      f32x16 s[2];
+  auto body = [&](int i, auto par_c) {
+    constexpr int par = decltype(par_c)::value;
+    const int t0 = (tile_begin + i) * kBN;
+    if (i + 2 < ntile) issue_k(t0 + 2 * kBN, std::integral_constant<int, par>{});
+    if (i + 1 < ntile) issue_v(t0 + kBN, std::integral_constant<int, par ^ 1>{});
+    // Tiles a wave cannot see at all are fully masked (no per-wave skipping,
+    // which keeps the loop body one straight block for the scheduler).
+    const bool full = (t0 >= lo_max) && (t0 + kBN <= hi_min);
+    if (!full) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-#pragma unroll
-        for (int t = 0; t < KS; ++t) s[kb] = mfma32(lds_read_b128(ks, koff[t] + kb * 32 * D), qf[t], s[kb]);
-      }
-      if (!full) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = t0 + kb * 32 + c_key(r, h);
-            s[kb][r] = (key < kstart || key >= kend) ? -INFINITY : s[kb][r];
-          }
-      }
-      float mx = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = max3f(mx, s[0][r], s[1][r]);
-      mx = max_lane_halves(mx);
-      const float m_tile = mx * c;
-      if (__any(m_tile > m_run + kRescaleThreshold)) {
-        const float m_new = fmaxf(m_run, m_tile);
-        const float alpha = fast_exp2(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < DB; ++i) acc[i] *= alpha;
-        m_run = m_new;
-      }
-      const float neg_m = -m_run;
-      bf16x8 pb[4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float e[16];
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          e[r] = fast_exp2(__builtin_fmaf(s[kb][r], c, neg_m));
-          l_run += e[r];
+          const int key = t0 + kb * 32 + c_key(r, h);
+          s_cur[kb][r] = (key < kstart || key >= kend) ? -INFINITY : s_cur[kb][r];
         }
-        pb[2 * kb] = pack_bf16(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-        pb[2 * kb + 1] = pack_bf16(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          acc[db] = mfma32(tr_read_pair(vs, voff[db] + 16 * u * D, 4 * D), pb[u], acc[db]);
     }
+    float mx = fmaxf(s_cur[0][0], s_cur[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = max3f(mx, s_cur[0][r], s_cur[1][r]);
+    mx = max_lane_halves(mx);
+    const float m_tile = mx * c;
+    if (__any(m_tile > m_run + kRescaleThreshold)) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int k = 0; k < DB; ++k) acc[k] *= alpha;
+      m_run = m_new;
+    }
+    // scores of the next tile (its K is already in LDS); on the last tile
+    // this reads a stale buffer and the result is dropped
+    f32x16 s_nxt[2];
+    scores(par ? k_lds0 : k_lds1, s_nxt);
+    const float neg_m = -m_run;
+    bf16x8 pb[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float e[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        e[r] = fast_exp2(__builtin_fmaf(s_cur[kb][r], c, neg_m));
+        l_run += e[r];
+      }
+      pb[2 * kb] = pack_bf16(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+      pb[2 * kb + 1] = pack_bf16(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
+    }
+    const __bf16* vs = par ? v_lds1 : v_lds0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        acc[db] = mfma32(tr_read_pair(vs, voff[db] + 16 * u * D, 4 * D), pb[u], acc[db]);
+    s_cur[0] = s_nxt[0];
+    s_cur[1] = s_nxt[1];
     wait_dma();
     __syncthreads();
   };
 
-  for (int it = tile_begin; it < tile_end; it += 2) {
-    tile_body(it, std::integral_constant<int, 0>{});
-    if (it + 1 < tile_end) tile_body(it + 1, std::integral_constant<int, 1>{});
+  for (int i = 0; i < ntile; i += 2) {
+    body(i, std::integral_constant<int, 0>{});
+    if (i + 1 < ntile) body(i + 1, std::integral_constant<int, 1>{});
   }
 
   // epilogue: O = acc / l, LSE = (m + log2 l) * ln 2

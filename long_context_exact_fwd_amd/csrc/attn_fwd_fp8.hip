@@ -59,10 +59,6 @@ __device__ __forceinline__ int fk_swz(int row) { return (row & 3) | ((row >> 1) 
 // then cover all 32 banks.
 __device__ __forceinline__ int fv_swz(int row) { return row & 7; }
 
-__device__ __forceinline__ uint32_t lds_read_u32x4_as(const uint8_t* base, int byte_off, int which) {
-  return (*LDS_PTR(const u32x4, base + byte_off))[which];
-}
-
 template <bool CAUSAL>
 __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_fp8_kernel(Fp8FwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[kTileBytes];
