@@ -13,9 +13,11 @@
 //     each 32 keys: wave A holds K, computes S and P and accumulates dV^T;
 //     wave B holds V, computes dP and, with A's P handed over through LDS,
 //     dS and dK^T. Each wave then needs one accumulator and one operand set,
-//     under 256 VGPRs, so two waves run per SIMD. The loop covers every query
-//     head of the GQA group and every visible 64-query tile, so the group sum
-//     needs no reduction across workgroups.
+//     under 256 VGPRs, so two waves run per SIMD. B runs one step behind A,
+//     so within a step the two are independent and each one's VALU work can
+//     hide under the other's MFMAs. The loop covers every query head of the
+//     GQA group and every visible 64-query tile, so the group sum needs no
+//     reduction across workgroups.
 //   * dQ: the forward's layout (4 waves of 32 queries, two workgroups per CU):
 //     Q and dO stay in VGPRs, K and V tiles stream through LDS.
 // Tiles reach LDS through buffer loads that write LDS directly; rows past the
@@ -77,12 +79,15 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   // one buffer from forcing waits on reads of the other.
   __shared__ __attribute__((aligned(1024))) __bf16 q_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 q_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 q_lds2[TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 g_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 g_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 g_lds2[TILE];
   __shared__ __attribute__((aligned(1024))) float st_lds0[2 * kQT];  // [LSE*log2e | Delta] of the tile
   __shared__ __attribute__((aligned(1024))) float st_lds1[2 * kQT];
-  // P handed from wave A to wave B: [pair][query block][4][lane] x f32x4
-  __shared__ __attribute__((aligned(1024))) f32x4 xchg[4][2][4][64];
+  __shared__ __attribute__((aligned(1024))) float st_lds2[2 * kQT];
+  // P (bf16) handed from wave A to wave B: [step parity][pair][query block][2][lane] x 8 bf16
+  __shared__ __attribute__((aligned(1024))) u32x4 xchg[2][4][2][2][64];
   __shared__ int red[2][8];
 
   const int tid = threadIdx.x;
@@ -183,16 +188,23 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
       --ti;
     }
   };
-  auto issue_step = [&](int g, int ti, auto buf_c) {
-    constexpr int buf = decltype(buf_c)::value;
+  auto slot_ptrs = [&](auto slot_c, __bf16*& qd, __bf16*& gd, float*& sd) {
+    constexpr int sl = decltype(slot_c)::value;
+    qd = sl == 0 ? q_lds0 : (sl == 1 ? q_lds1 : q_lds2);
+    gd = sl == 0 ? g_lds0 : (sl == 1 ? g_lds1 : g_lds2);
+    sd = sl == 0 ? st_lds0 : (sl == 1 ? st_lds1 : st_lds2);
+  };
+  // DMA of one step's Q and dO tiles and row statistics into buffer slot sl
+  auto issue_step = [&](int g, int ti, auto slot_c) {
     const int t0 = ti * kQT;
     const int hq = hk * G + g;
     const size_t row0 = ((size_t)b * p.seqlen + t0) * q_stride + hq * D;
     const uint32_t nbytes = (uint32_t)(p.seqlen - t0) * (uint32_t)q_stride * 2u;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + row0, nbytes);
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.dout + row0, nbytes);
-    __bf16* qd = buf ? q_lds1 : q_lds0;
-    __bf16* gd = buf ? g_lds1 : g_lds0;
+    __bf16 *qd, *gd;
+    float* sd;
+    slot_ptrs(slot_c, qd, gd, sd);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int el = (i * 8 + wave) * 512;
@@ -203,8 +215,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
       // wave 0 copies LSE*log2e, wave 1 Delta: 4 floats per lane
       const float* src = (wave == 0 ? p.lse2 : p.delta) + stat_b + (size_t)hq * p.stat_stride + t0;
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)(p.stat_stride - t0) * 4u);
-      float* sd = (buf ? st_lds1 : st_lds0) + wave * kQT;
-      dma16_buf(rs, (uint32_t)lane * 16u, sd);
+      dma16_buf(rs, (uint32_t)lane * 16u, sd + wave * kQT);
     }
   };
 
@@ -213,8 +224,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
   const float c = p.scale_log2e;
 
-  int cur_g = 0, cur_ti = tile_end - 1;  // head and query tile of the current step
-  if (nsteps > 0) issue_step(cur_g, cur_ti, std::integral_constant<int, 0>{});
+  int nx_g = 0, nx_ti = tile_end - 1;  // head and query tile of the next step to load
+  if (nsteps > 0) {
+    issue_step(nx_g, nx_ti, std::integral_constant<int, 0>{});
+    advance(nx_g, nx_ti);
+  }
   wait_dma();
   __syncthreads();
 
@@ -222,121 +236,140 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   // cannot see is fully masked (P = 0). With 64-query tiles and 128-key
   // workgroups that costs at most the first two steps of a causal range,
   // and it keeps the loop free of per-wave branches around the barriers.
-  // Two barriers per step: after A has written P, and at the end of the step
-  // (next Q/dO tile in LDS).
+  //
+  // Wave B runs one step behind wave A, so the two are independent within a
+  // step and one barrier per step suffices:
+  //   step j: A: S(j) = Q(j) K^T, P(j) -> exchange slot j % 2, dV^T += dO(j)^T P(j)
+  //           B: dP(j-1) = dO(j-1) V^T, dS(j-1) with P(j-1), dK^T += Q(j-1)^T dS(j-1)
+  // Tiles therefore live for two steps (three buffer slots; the next step's
+  // tiles load into the third), the exchange for two (two slots). P goes
+  // through LDS as bf16; dS is rounded to bf16 for its MFMA anyway. Slots are
+  // compile-time: the loop over the nsteps + 1 barrier steps is unrolled by 6.
+  const int nbar = nsteps > 0 ? nsteps + 1 : 0;
+  auto steps6 = [&](auto body) {
+    for (int s0 = 0; s0 < nbar; s0 += 6) {
+      body(s0, std::integral_constant<int, 0>{});
+      if (s0 + 1 < nbar) body(s0 + 1, std::integral_constant<int, 1>{});
+      if (s0 + 2 < nbar) body(s0 + 2, std::integral_constant<int, 2>{});
+      if (s0 + 3 < nbar) body(s0 + 3, std::integral_constant<int, 3>{});
+      if (s0 + 4 < nbar) body(s0 + 4, std::integral_constant<int, 4>{});
+      if (s0 + 5 < nbar) body(s0 + 5, std::integral_constant<int, 5>{});
+    }
+  };
+  auto prefetch = [&](int step, auto r_c) {
+    constexpr int r = decltype(r_c)::value;
+    if (step + 1 < nsteps) {
+      issue_step(nx_g, nx_ti, std::integral_constant<int, (r + 1) % 3>{});
+      advance(nx_g, nx_ti);
+    }
+  };
   if (role == 0) {
-    auto body_a = [&](int step, auto cur_c) {
-      constexpr int cur = decltype(cur_c)::value;
-      int nxt_g = cur_g, nxt_ti = cur_ti;
-      advance(nxt_g, nxt_ti);
-      const int t0 = cur_ti * kQT;
-      if (step + 1 < nsteps) issue_step(nxt_g, nxt_ti, std::integral_constant<int, cur ^ 1>{});
-      const bool full = (t0 >= lo_max) && (t0 + kQT <= hi_min);
-      const __bf16* qs = cur ? q_lds1 : q_lds0;
-      const __bf16* gs = cur ? g_lds1 : g_lds0;
-      const float* st = cur ? st_lds1 : st_lds0;
-      bf16x8 pb[4];
+    int cur_g = 0, cur_ti = tile_end - 1;
+    auto body_a = [&](int step, auto r_c) {
+      constexpr int r = decltype(r_c)::value;
+      prefetch(step, r_c);
+      if (step < nsteps) {
+        const int t0 = cur_ti * kQT;
+        const bool full = (t0 >= lo_max) && (t0 + kQT <= hi_min);
+        __bf16 *qs, *gs;
+        float* st;
+        slot_ptrs(std::integral_constant<int, r % 3>{}, qs, gs, st);
+        bf16x8 pb[4];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x16 s = f32x16{};
+        for (int qb = 0; qb < 2; ++qb) {
+          f32x16 s = f32x16{};
 #pragma unroll
-        for (int t = 0; t < KS; ++t) s = mfma32(lds_read_b128(qs, qoff[t] + qb * 32 * D), xf[t], s);
-        // C rows of this lane: queries qb*32 + c_key(r, h), two runs of 8
-        const f32x4* l4 = reinterpret_cast<const f32x4*>(st + qb * 32 + 8 * h);
-        const f32x4 la = l4[0], lb = l4[1], lc = l4[4], ld = l4[5];
-        float pr[16];
+          for (int t = 0; t < KS; ++t) s = mfma32(lds_read_b128(qs, qoff[t] + qb * 32 * D), xf[t], s);
+          // C rows of this lane: queries qb*32 + c_key(r, h), two runs of 8
+          const f32x4* l4 = reinterpret_cast<const f32x4*>(st + qb * 32 + 8 * h);
+          const f32x4 la = l4[0], lb = l4[1], lc = l4[4], ld = l4[5];
+          float pr[16];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pr[e] = fast_exp2(__builtin_fmaf(s[e], c, -la[e]));
-          pr[4 + e] = fast_exp2(__builtin_fmaf(s[4 + e], c, -lb[e]));
-          pr[8 + e] = fast_exp2(__builtin_fmaf(s[8 + e], c, -lc[e]));
-          pr[12 + e] = fast_exp2(__builtin_fmaf(s[12 + e], c, -ld[e]));
-        }
-        if (!full) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qq = t0 + qb * 32 + c_key(r, h);
-            pr[r] = (qq < qlo || qq >= qhi) ? 0.f : pr[r];
+          for (int e = 0; e < 4; ++e) {
+            pr[e] = fast_exp2(__builtin_fmaf(s[e], c, -la[e]));
+            pr[4 + e] = fast_exp2(__builtin_fmaf(s[4 + e], c, -lb[e]));
+            pr[8 + e] = fast_exp2(__builtin_fmaf(s[8 + e], c, -lc[e]));
+            pr[12 + e] = fast_exp2(__builtin_fmaf(s[12 + e], c, -ld[e]));
           }
+          if (!full) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+              const int qq = t0 + qb * 32 + c_key(rr, h);
+              pr[rr] = (qq < qlo || qq >= qhi) ? 0.f : pr[rr];
+            }
+          }
+          pb[2 * qb] = pack_bf16(pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]);
+          pb[2 * qb + 1] = pack_bf16(pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]);
+          xchg[r % 2][pair][qb][0][lane] = __builtin_bit_cast(u32x4, pb[2 * qb]);
+          xchg[r % 2][pair][qb][1][lane] = __builtin_bit_cast(u32x4, pb[2 * qb + 1]);
         }
+        // dV^T += dO^T P (fragment reads kept one query step ahead at most)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          f32x4 v = {pr[4 * j], pr[4 * j + 1], pr[4 * j + 2], pr[4 * j + 3]};
-          xchg[pair][qb][j][lane] = v;
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+          for (int d = 0; d < DB; ++d)
+            acc[d] = mfma32(tr_read2(gs, trlo[d] + 16 * u * D, trhi[d] + 16 * u * D), pb[u], acc[d]);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        pb[2 * qb] = pack_bf16(pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]);
-        pb[2 * qb + 1] = pack_bf16(pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]);
+        advance(cur_g, cur_ti);
       }
-      __syncthreads();  // P of this step is in xchg
-      // dV^T += dO^T P (fragment reads kept one query step ahead at most)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-#pragma unroll
-        for (int d = 0; d < DB; ++d)
-          acc[d] = mfma32(tr_read2(gs, trlo[d] + 16 * u * D, trhi[d] + 16 * u * D), pb[u], acc[d]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      cur_g = nxt_g;
-      cur_ti = nxt_ti;
       wait_dma();
       __syncthreads();
     };
-    for (int step = 0; step < nsteps; step += 2) {
-      body_a(step, std::integral_constant<int, 0>{});
-      if (step + 1 < nsteps) body_a(step + 1, std::integral_constant<int, 1>{});
-    }
+    steps6(body_a);
   } else {
-    auto body_b = [&](int step, auto cur_c) {
-      constexpr int cur = decltype(cur_c)::value;
-      int nxt_g = cur_g, nxt_ti = cur_ti;
-      advance(nxt_g, nxt_ti);
-      if (step + 1 < nsteps) issue_step(nxt_g, nxt_ti, std::integral_constant<int, cur ^ 1>{});
-      const __bf16* qs = cur ? q_lds1 : q_lds0;
-      const __bf16* gs = cur ? g_lds1 : g_lds0;
-      const float* st = cur ? st_lds1 : st_lds0;
-      f32x16 dp[2];
+    auto body_b = [&](int step, auto r_c) {
+      constexpr int r = decltype(r_c)::value;
+      prefetch(step, r_c);
+      if (step > 0) {
+        // tiles and exchange slot of step - 1
+        __bf16 *qs, *gs;
+        float* st;
+        slot_ptrs(std::integral_constant<int, (r + 2) % 3>{}, qs, gs, st);
+        constexpr int xs = (r + 1) % 2;
+        f32x16 dp[2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        dp[qb] = f32x16{};
+        for (int qb = 0; qb < 2; ++qb) {
+          dp[qb] = f32x16{};
 #pragma unroll
-        for (int t = 0; t < KS; ++t) dp[qb] = mfma32(lds_read_b128(gs, qoff[t] + qb * 32 * D), xf[t], dp[qb]);
-      }
-      __syncthreads();  // P of this step is in xchg
-      bf16x8 db[4];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const f32x4* d4 = reinterpret_cast<const f32x4*>(st + kQT + qb * 32 + 8 * h);
-        const f32x4 da = d4[0], dd = d4[1], dc = d4[4], de = d4[5];
-        const f32x4 p0 = xchg[pair][qb][0][lane], p1 = xchg[pair][qb][1][lane];
-        const f32x4 p2 = xchg[pair][qb][2][lane], p3 = xchg[pair][qb][3][lane];
-        float dsv[16];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          dsv[e] = p0[e] * (dp[qb][e] - da[e]);
-          dsv[4 + e] = p1[e] * (dp[qb][4 + e] - dd[e]);
-          dsv[8 + e] = p2[e] * (dp[qb][8 + e] - dc[e]);
-          dsv[12 + e] = p3[e] * (dp[qb][12 + e] - de[e]);
+          for (int t = 0; t < KS; ++t) dp[qb] = mfma32(lds_read_b128(gs, qoff[t] + qb * 32 * D), xf[t], dp[qb]);
         }
-        db[2 * qb] = pack_bf16(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
-        db[2 * qb + 1] = pack_bf16(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
-      }
-      // dK^T += Q^T dS
+        bf16x8 db[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+        for (int qb = 0; qb < 2; ++qb) {
+          const f32x4* d4 = reinterpret_cast<const f32x4*>(st + kQT + qb * 32 + 8 * h);
+          const f32x4 da = d4[0], dd = d4[1], dc = d4[4], de = d4[5];
+          const u32x4 w0 = xchg[xs][pair][qb][0][lane], w1 = xchg[xs][pair][qb][1][lane];
+          auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
+          auto hi = [](uint32_t w) { return __uint_as_float(w & 0xffff0000u); };
+          float dsv[16];
 #pragma unroll
-        for (int d = 0; d < DB; ++d)
-          acc[d] = mfma32(tr_read2(qs, trlo[d] + 16 * u * D, trhi[d] + 16 * u * D), db[u], acc[d]);
-        __builtin_amdgcn_sched_barrier(0);
+          for (int e = 0; e < 2; ++e) {
+            dsv[2 * e] = lo(w0[e]) * (dp[qb][2 * e] - da[2 * e]);
+            dsv[2 * e + 1] = hi(w0[e]) * (dp[qb][2 * e + 1] - da[2 * e + 1]);
+            dsv[4 + 2 * e] = lo(w0[2 + e]) * (dp[qb][4 + 2 * e] - dd[2 * e]);
+            dsv[5 + 2 * e] = hi(w0[2 + e]) * (dp[qb][5 + 2 * e] - dd[2 * e + 1]);
+            dsv[8 + 2 * e] = lo(w1[e]) * (dp[qb][8 + 2 * e] - dc[2 * e]);
+            dsv[9 + 2 * e] = hi(w1[e]) * (dp[qb][9 + 2 * e] - dc[2 * e + 1]);
+            dsv[12 + 2 * e] = lo(w1[2 + e]) * (dp[qb][12 + 2 * e] - de[2 * e]);
+            dsv[13 + 2 * e] = hi(w1[2 + e]) * (dp[qb][13 + 2 * e] - de[2 * e + 1]);
+          }
+          db[2 * qb] = pack_bf16(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+          db[2 * qb + 1] = pack_bf16(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
+        }
+        // dK^T += Q^T dS
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+          for (int d = 0; d < DB; ++d)
+            acc[d] = mfma32(tr_read2(qs, trlo[d] + 16 * u * D, trhi[d] + 16 * u * D), db[u], acc[d]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-      cur_g = nxt_g;
-      cur_ti = nxt_ti;
       wait_dma();
       __syncthreads();
     };
-    for (int step = 0; step < nsteps; step += 2) {
-      body_b(step, std::integral_constant<int, 0>{});
-      if (step + 1 < nsteps) body_b(step + 1, std::integral_constant<int, 1>{});
-    }
+    steps6(body_b);
   }
 
   if (k_ok) {
