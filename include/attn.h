@@ -98,10 +98,13 @@ attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                          int causal, const int32_t* cu_seqlens, int num_seqs,
                          float scale, attn_stream_t stream);
 
-/* Bytes of device workspace attn_bwd needs: 8 * batch * hq * S64, with S64 =
- * seqlen rounded up to a multiple of 64. It holds two fp32 per-row arrays of
- * [batch, hq, S64]: Delta_i = dO_i . O_i and LSE_i * log2(e); the padding
- * rows are written as zeros. Returns 0 for non-positive sizes. */
+/* Bytes of device workspace attn_bwd needs: 8 * batch * hq * S64 + 8 * NB,
+ * with S64 = seqlen rounded up to a multiple of 64 and NB = ceil(seqlen / 128).
+ * It holds two fp32 per-row arrays of [batch, hq, S64], Delta_i = dO_i . O_i
+ * and LSE_i * log2(e) (the padding rows are written as zeros), then two int32
+ * arrays of NB entries: the order in which the dK/dV and the dQ kernels take
+ * their 128-row blocks, heaviest first under the mask. Returns 0 for
+ * non-positive sizes. */
 size_t attn_bwd_workspace_bytes(int batch, int hq, int seqlen);
 
 /* Backward: dq, dk, dv from q, k, v, the forward's o and lse, and dout.
@@ -123,7 +126,7 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
  * phases as separate calls on one stream (Delta first) gives bitwise the
  * same result. It exists so that callers and profilers can time or schedule
  * each kernel on its own. Arguments as attn_bwd. dK/dV and dQ read the Delta
- * that an earlier ATTN_BWD_DELTA call left in `workspace`.
+ * and the block order that an earlier ATTN_BWD_DELTA call left in `workspace`.
  * phases: nonzero bitmask of the values below; other bits are invalid. */
 #define ATTN_BWD_DELTA 1u
 #define ATTN_BWD_DKDV 2u

@@ -171,9 +171,12 @@ def bwd(q, k, v, o, lse, do, *, causal: bool, cu_seqlens=None, scale: Optional[f
     dq = dq if dq is not None else torch.empty_like(q)
     dk = dk if dk is not None else torch.empty_like(k)
     dv = dv if dv is not None else torch.empty_like(v)
+    nbytes = bwd_workspace_bytes(B, Hq, S)
     if workspace is None:
-        nbytes = bwd_workspace_bytes(B, Hq, S)
         workspace = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=q.device)
+    elif not (workspace.is_contiguous() and workspace.numel() * workspace.element_size() >= nbytes
+              and workspace.device == q.device):
+        raise ValueError(f"workspace must be a contiguous tensor of at least {nbytes} bytes on {q.device}")
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
             B, Hq, Hkv, S, D, int(bool(causal)), _ptr(cu_seqlens), n, float(scale), _stream())
     if phases is None:

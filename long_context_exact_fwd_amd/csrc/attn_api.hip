@@ -61,7 +61,8 @@ int attn_last_hip_error(void) { return g_last_hip_error; }
 
 size_t attn_bwd_workspace_bytes(int batch, int hq, int seqlen) {
   if (batch <= 0 || hq <= 0 || seqlen <= 0) return 0;
-  return (size_t)8 * (size_t)batch * (size_t)hq * (size_t)mi355attn::stat_stride_for(seqlen);
+  const size_t nblk = ((size_t)seqlen + 127) / 128;
+  return (size_t)8 * (size_t)batch * (size_t)hq * (size_t)mi355attn::stat_stride_for(seqlen) + 8 * nblk;
 }
 
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
@@ -151,6 +152,7 @@ attn_status attn_bwd_phases(unsigned phases, const void* q, const void* k, const
   p.stat_stride = mi355attn::stat_stride_for(seqlen);
   p.delta = static_cast<float*>(workspace);
   p.lse2 = p.delta + (size_t)batch * hq * p.stat_stride;
+  p.order = reinterpret_cast<int*>(p.lse2 + (size_t)batch * hq * p.stat_stride);
   p.cu_seqlens = cu_seqlens;
   p.num_seqs = num_seqs;
   p.batch = batch;

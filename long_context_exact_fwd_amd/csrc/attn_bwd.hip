@@ -33,12 +33,68 @@ constexpr int kQT = 64;  // queries per tile (dK/dV pass)
 constexpr int kKT = 64;  // keys per tile (dQ pass)
 
 // ---------------------------------------------------------------------------
-// Delta_i = dO_i . O_i and LSE_i * log2(e), both fp32 [B, Hq, S]
+// Work order. The dK/dV and dQ passes each run one workgroup per 128-row
+// block, and a block's cost is the number of 64-row tiles of the other
+// operand it visits. Under a causal or packed mask the costs differ by up to
+// the longest segment over the tile size, and with about two blocks per CU
+// the launch order decides the makespan: both passes launch their blocks
+// heaviest first (longest-processing-time order). For a single causal
+// sequence this is key blocks from the start and query blocks from the end.
 // ---------------------------------------------------------------------------
-template <int D>
+template <bool CAUSAL>
+__device__ int block_cost(const BwdParams& p, int pass, int blk) {
+  const int r0 = blk * 128;
+  const int r1 = min(r0 + 128, p.seqlen) - 1;
+  int s0a, s1a, s0b, s1b;
+  segment_of(p.cu_seqlens, p.num_seqs, p.seqlen, r0, s0a, s1a);
+  segment_of(p.cu_seqlens, p.num_seqs, p.seqlen, r1, s0b, s1b);
+  // pass 0: keys r0..r1 see queries [lo, hi); pass 1: queries r0..r1 see keys [lo, hi)
+  const int lo = (pass == 0 && CAUSAL) ? r0 : s0a;
+  const int hi = (pass == 1 && CAUSAL) ? r1 + 1 : s1b;
+  return (hi + 63) / 64 - lo / 64;
+}
+
+// Rank of each block by descending cost, ties by index; order[rank] = block.
+// Each thread ranks one block against all of them, 256 at a time through LDS.
+template <bool CAUSAL>
+__device__ void block_order(const BwdParams& p, int wg) {
+  __shared__ int cost[256];
+  const int nblk = p.num_blk;
+  const int per_pass = (nblk + 255) / 256;
+  const int pass = wg / per_pass;
+  const int i = (wg - pass * per_pass) * 256 + (int)threadIdx.x;
+  const int mine = i < nblk ? block_cost<CAUSAL>(p, pass, i) : 0;
+  int rank = 0;
+  for (int c = 0; c < nblk; c += 256) {
+    const int j = c + (int)threadIdx.x;
+    __syncthreads();
+    cost[threadIdx.x] = j < nblk ? block_cost<CAUSAL>(p, pass, j) : INT32_MIN;
+    __syncthreads();
+    const int m = min(256, nblk - c);
+    for (int t = 0; t < m; ++t) {
+      const int cj = cost[t];
+      rank += (cj > mine) || (cj == mine && c + t < i);
+    }
+  }
+  if (i < nblk) p.order[pass * nblk + rank] = i;
+}
+
+// ---------------------------------------------------------------------------
+// Delta_i = dO_i . O_i and LSE_i * log2(e), both fp32 [B, Hq, S]; the last
+// 2 * ceil(num_blk / 256) workgroups write the work order instead.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
   constexpr int LPR = D / 8;  // lanes per row
   constexpr int RPB = 256 / LPR;
+  {
+    const long nrows = (long)p.batch * p.hq * p.stat_stride;
+    const int nstat = (int)((nrows + RPB - 1) / RPB);
+    if ((int)blockIdx.x >= nstat) {
+      block_order<CAUSAL>(p, (int)blockIdx.x - nstat);
+      return;
+    }
+  }
   const int tid = threadIdx.x;
   const long r = (long)blockIdx.x * RPB + tid / LPR;  // index into [B, Hq, stat_stride]
   const long nrows = (long)p.batch * p.hq * p.stat_stride;
@@ -98,15 +154,16 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   const int n = lane & 31;
   const int h = lane >> 5;
 
-  // Launch order: kv heads fastest, then key blocks (causal: the first key
-  // blocks see the most queries, so the heaviest start first). Workgroups are
+  // Launch order: kv heads fastest, then key blocks in the heaviest-first
+  // order that the Delta pass wrote to the workspace. Workgroups are
   // dealt round-robin to the 8 XCDs, so with up to 8 kv heads each XCD keeps
   // working on the same kv head and shares its Q/dO tiles in its L2.
   const int bh = blockIdx.x;
   const int b = bh / p.hkv;
   const int hk = bh - b * p.hkv;
   const int G = p.hq / p.hkv;
-  const int k0 = blockIdx.y * 128;
+  // clamped, so that a workspace without a Delta pass gives wrong sums, never a stray address
+  const int k0 = (int)min((unsigned)p.order[blockIdx.y], (unsigned)(p.num_blk - 1)) * 128;
   const int my_k = k0 + pair * 32 + n;
   const bool k_ok = my_k < p.seqlen;
   const int kv_stride = p.hkv * D;
@@ -412,7 +469,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   const int b = bh / p.hq;
   const int hq = bh - b * p.hq;
   const int hk = hq / (p.hq / p.hkv);
-  const int qblk = p.num_blk - 1 - (int)blockIdx.y;  // heaviest blocks first
+  const int qblk = (int)min((unsigned)p.order[p.num_blk + blockIdx.y], (unsigned)(p.num_blk - 1));
   const int my_q = qblk * 128 + wave * 32 + n;
   const bool q_ok = my_q < p.seqlen;
   const int q_stride = p.hq * D;
@@ -572,27 +629,27 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_bwd(const BwdParams& p, unsigned phases, hipStream_t stream) {
+hipError_t launch_bwd(const BwdParams& p_in, unsigned phases, hipStream_t stream) {
+  BwdParams q = p_in;
+  q.num_blk = (q.seqlen + 127) / 128;
   if (phases & kBwdDelta) {
     constexpr int RPB = 256 / (D / 8);
-    const long nrows = (long)p.batch * p.hq * p.stat_stride;
-    dim3 grid((unsigned)((nrows + RPB - 1) / RPB));
-    hipLaunchKernelGGL((attn_bwd_delta_kernel<D>), grid, dim3(256), 0, stream, p);
+    const long nrows = (long)q.batch * q.hq * q.stat_stride;
+    const long nstat = (nrows + RPB - 1) / RPB;
+    const long norder = 2L * ((q.num_blk + 255) / 256);
+    dim3 grid((unsigned)(nstat + norder));
+    hipLaunchKernelGGL((attn_bwd_delta_kernel<D, CAUSAL>), grid, dim3(256), 0, stream, q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (phases & kBwdDkDv) {
-    BwdParams q = p;
-    q.num_blk = (p.seqlen + 127) / 128;
-    dim3 grid(p.batch * p.hkv, q.num_blk);
+    dim3 grid(q.batch * q.hkv, q.num_blk);
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL>), grid, dim3(512), 0, stream, q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (phases & kBwdDq) {
-    BwdParams q = p;
-    q.num_blk = (p.seqlen + 127) / 128;
-    dim3 grid(p.batch * p.hq, q.num_blk);
+    dim3 grid(q.batch * q.hq, q.num_blk);
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), grid, dim3(256), 0, stream, q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

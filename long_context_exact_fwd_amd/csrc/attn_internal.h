@@ -52,13 +52,14 @@ struct BwdParams {
   float* delta;  // workspace [B, Hq, stat_stride]: Delta_i = dO_i . O_i
   float* lse2;   // workspace [B, Hq, stat_stride]: LSE_i * log2(e)
   int stat_stride;  // seqlen rounded up to kStatAlign; the padding holds zeros
+  int* order;       // workspace [2, num_blk]: block order of the dK/dV pass, then of the dQ pass
   const int32_t* cu_seqlens;
   int num_seqs;
   int batch, hq, hkv, seqlen, head_dim;
   int causal;
   float scale;
   float scale_log2e;
-  int num_blk;  // set by the launchers
+  int num_blk;  // 128-row blocks along the sequence; set by the launcher
 };
 
 // Row length of the backward's per-row statistics in the workspace.

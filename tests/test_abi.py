@@ -42,10 +42,11 @@ def test_status_strings():
 
 def test_workspace_bytes():
     lib = lca.load_library()
-    # two fp32 arrays [B, Hq, S rounded up to 64]
-    assert lib.attn_bwd_workspace_bytes(1, 28, 32768) == 8 * 28 * 32768
-    assert lib.attn_bwd_workspace_bytes(2, 3, 5) == 8 * 2 * 3 * 64
-    assert lib.attn_bwd_workspace_bytes(1, 1, 65) == 8 * 128
+    # two fp32 arrays [B, Hq, S rounded up to 64], two int32 arrays [ceil(S / 128)]
+    assert lib.attn_bwd_workspace_bytes(1, 28, 32768) == 8 * 28 * 32768 + 8 * 256
+    assert lib.attn_bwd_workspace_bytes(2, 3, 5) == 8 * 2 * 3 * 64 + 8
+    assert lib.attn_bwd_workspace_bytes(1, 1, 65) == 8 * 128 + 8
+    assert lib.attn_bwd_workspace_bytes(1, 1, 129) == 8 * 192 + 16
     assert lib.attn_bwd_workspace_bytes(0, 3, 5) == 0
     assert lib.attn_bwd_workspace_bytes(1, -1, 5) == 0
 

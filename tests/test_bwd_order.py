@@ -1,0 +1,68 @@
+"""The backward's work order (GPU): the Delta phase writes, for the dK/dV and
+the dQ kernels, the order in which they take their 128-row blocks. Each list
+must be a permutation of the blocks (or some block would be computed twice and
+another never), sorted by cost, heaviest first, ties by block index.
+
+A block's cost is the number of 64-row tiles of the other operand that the
+mask lets it see: under a causal mask key j sees queries j.. of its segment and
+query i sees keys up to i; with packing only its own segment; otherwise the
+whole sequence.
+"""
+import numpy as np
+import pytest
+
+import seeded_inputs as si
+from tests.gpu_helpers import dev_i32
+
+pytestmark = pytest.mark.gpu
+
+
+def _segment(cu, i):
+    s = int(np.searchsorted(cu, i, side="right")) - 1
+    return int(cu[s]), int(cu[s + 1])
+
+
+def _cost(cu, S, causal, pass_, blk):
+    first, last = blk * 128, min(blk * 128 + 128, S) - 1
+    if pass_ == 0:  # keys first..last: the union of the queries they see
+        lo = first if causal else _segment(cu, first)[0]
+        hi = _segment(cu, last)[1]
+    else:  # queries first..last: the union of the keys they see
+        lo = _segment(cu, first)[0]
+        hi = last + 1 if causal else _segment(cu, last)[1]
+    return -(-hi // 64) - lo // 64
+
+
+CASES = [
+    (65, True, None),
+    (300, False, None),
+    (1000, True, [200, 13, 300, 487]),
+    (4096, True, None),
+    (32768, True, si.packed_lengths(np.random.default_rng(4))),
+    (32768, False, si.packed_lengths(np.random.default_rng(7))),
+    (70000, True, None),
+]
+
+
+@pytest.mark.parametrize("S,causal,lengths", CASES)
+def test_block_order(S, causal, lengths):
+    import torch
+    import long_context_exact_fwd_amd as lca
+    print(f"order S={S} causal={causal} lengths={lengths}", flush=True)
+    B, Hq, Hkv, D = 1, 2, 1, 128
+    z = torch.zeros((B, S, Hq, D), dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros((B, S, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((B, Hq, S), dtype=torch.float32, device="cuda")
+    cu_h = si.cu_seqlens_from_lengths(lengths) if lengths else np.array([0, S], dtype=np.int32)
+    cu = dev_i32(cu_h) if lengths else None
+    nbytes = lca.bwd_workspace_bytes(B, Hq, S)
+    ws = torch.full((nbytes // 4,), -7, dtype=torch.int32, device="cuda")
+    lca.bwd(z, kv, kv, z, lse, z, causal=causal, cu_seqlens=cu, workspace=ws, phases=lca.BWD_DELTA)
+    torch.cuda.synchronize()
+    nblk = -(-S // 128)
+    order = ws[-2 * nblk:].cpu().numpy().reshape(2, nblk)
+    for pass_ in (0, 1):
+        got = order[pass_]
+        assert sorted(got.tolist()) == list(range(nblk)), f"pass {pass_}: not a permutation"
+        keys = [(-_cost(cu_h, S, causal, pass_, int(b)), int(b)) for b in got]
+        assert keys == sorted(keys), f"pass {pass_}: not heaviest first"
