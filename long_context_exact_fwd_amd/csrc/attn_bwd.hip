@@ -320,6 +320,26 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
       advance(nx_g, nx_ti);
     }
   };
+  // out[qb] += (rows qb*32 .. qb*32+31 of a Q or dO tile) x (this wave's K or
+  // V)^T. The two 32-row chains alternate, and the LDS operands of step t + 2
+  // are read before the MFMAs of step t, so the read latency overlaps MFMAs.
+  auto rows_times_x = [&](const __bf16* tile, f32x16 (&out)[2]) {
+    bf16x8 a[3][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) a[t][qb] = lds_read_b128(tile, qoff[t] + qb * 32 * D);
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      if (t + 2 < KS) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) a[(t + 2) % 3][qb] = lds_read_b128(tile, qoff[t + 2] + qb * 32 * D);
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) out[qb] = mfma32(a[t % 3][qb], xf[t], out[qb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   if (role == 0) {
     int cur_g = 0, cur_ti = tile_end - 1;
     auto body_a = [&](int step, auto r_c) {
@@ -331,12 +351,12 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
         __bf16 *qs, *gs;
         float* st;
         slot_ptrs(std::integral_constant<int, r % 3>{}, qs, gs, st);
+        f32x16 sc[2] = {f32x16{}, f32x16{}};
+        rows_times_x(qs, sc);
         bf16x8 pb[4];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          f32x16 s = f32x16{};
-#pragma unroll
-          for (int t = 0; t < KS; ++t) s = mfma32(lds_read_b128(qs, qoff[t] + qb * 32 * D), xf[t], s);
+          const f32x16& s = sc[qb];
           // C rows of this lane: queries qb*32 + c_key(r, h), two runs of 8
           const f32x4* l4 = reinterpret_cast<const f32x4*>(st + qb * 32 + 8 * h);
           const f32x4 la = l4[0], lb = l4[1], lc = l4[4], ld = l4[5];
@@ -360,12 +380,20 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
           xchg[r % 2][pair][qb][0][lane] = __builtin_bit_cast(u32x4, pb[2 * qb]);
           xchg[r % 2][pair][qb][1][lane] = __builtin_bit_cast(u32x4, pb[2 * qb + 1]);
         }
-        // dV^T += dO^T P (fragment reads kept one query step ahead at most)
+        // dV^T += dO^T P; the fragments of query step u + 1 are read before
+        // the MFMAs of step u.
+        bf16x8 fr[2][DB];
+#pragma unroll
+        for (int d = 0; d < DB; ++d) fr[0][d] = tr_read2(gs, trlo[d], trhi[d]);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
+          if (u < 3) {
 #pragma unroll
-          for (int d = 0; d < DB; ++d)
-            acc[d] = mfma32(tr_read2(gs, trlo[d] + 16 * u * D, trhi[d] + 16 * u * D), pb[u], acc[d]);
+            for (int d = 0; d < DB; ++d)
+              fr[(u + 1) & 1][d] = tr_read2(gs, trlo[d] + 16 * (u + 1) * D, trhi[d] + 16 * (u + 1) * D);
+          }
+#pragma unroll
+          for (int d = 0; d < DB; ++d) acc[d] = mfma32(fr[u & 1][d], pb[u], acc[d]);
           __builtin_amdgcn_sched_barrier(0);
         }
         advance(cur_g, cur_ti);
@@ -384,16 +412,12 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
         float* st;
         slot_ptrs(std::integral_constant<int, (r + 2) % 3>{}, qs, gs, st);
         constexpr int xs = (r + 1) % 2;
-        f32x16 dp[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          dp[qb] = f32x16{};
-#pragma unroll
-          for (int t = 0; t < KS; ++t) dp[qb] = mfma32(lds_read_b128(gs, qoff[t] + qb * 32 * D), xf[t], dp[qb]);
-        }
+        f32x16 dp[2] = {f32x16{}, f32x16{}};
+        rows_times_x(gs, dp);
         bf16x8 db[4];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
+          // dS = P (dP - Delta), P widened from the bf16 exchange
           const f32x4* d4 = reinterpret_cast<const f32x4*>(st + kQT + qb * 32 + 8 * h);
           const f32x4 da = d4[0], dd = d4[1], dc = d4[4], de = d4[5];
           const u32x4 w0 = xchg[xs][pair][qb][0][lane], w1 = xchg[xs][pair][qb][1][lane];
@@ -414,12 +438,19 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
           db[2 * qb] = pack_bf16(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
           db[2 * qb + 1] = pack_bf16(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
         }
-        // dK^T += Q^T dS
+        // dK^T += Q^T dS, fragments read one query step ahead
+        bf16x8 fr[2][DB];
+#pragma unroll
+        for (int d = 0; d < DB; ++d) fr[0][d] = tr_read2(qs, trlo[d], trhi[d]);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
+          if (u < 3) {
 #pragma unroll
-          for (int d = 0; d < DB; ++d)
-            acc[d] = mfma32(tr_read2(qs, trlo[d] + 16 * u * D, trhi[d] + 16 * u * D), db[u], acc[d]);
+            for (int d = 0; d < DB; ++d)
+              fr[(u + 1) & 1][d] = tr_read2(qs, trlo[d] + 16 * (u + 1) * D, trhi[d] + 16 * (u + 1) * D);
+          }
+#pragma unroll
+          for (int d = 0; d < DB; ++d) acc[d] = mfma32(fr[u & 1][d], db[u], acc[d]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -576,11 +607,31 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
       const __bf16* vs = cur ? v_lds1 : v_lds0;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        // S and dP chains alternate; LDS operands are read two steps ahead
         f32x16 s = f32x16{}, dp = f32x16{};
+        {
+          bf16x8 ka[3], va[3];
 #pragma unroll
-        for (int t = 0; t < KS; ++t) s = mfma32(lds_read_b128(ks, koff[t] + kb * 32 * D), qf[t], s);
+          for (int t = 0; t < 2; ++t) {
+            ka[t] = lds_read_b128(ks, koff[t] + kb * 32 * D);
+            va[t] = lds_read_b128(vs, voff[t] + kb * 32 * D);
+          }
 #pragma unroll
-        for (int t = 0; t < KS; ++t) dp = mfma32(lds_read_b128(vs, voff[t] + kb * 32 * D), gf[t], dp);
+          for (int t = 0; t < KS; ++t) {
+            if (t + 2 < KS) {
+              ka[(t + 2) % 3] = lds_read_b128(ks, koff[t + 2] + kb * 32 * D);
+              va[(t + 2) % 3] = lds_read_b128(vs, voff[t + 2] + kb * 32 * D);
+            }
+            s = mfma32(ka[t % 3], qf[t], s);
+            dp = mfma32(va[t % 3], gf[t], dp);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        // K^T fragments of the first 16 keys, read while the exponentials run
+        const int o = (kb * 32) * D;
+        bf16x8 f0[DB], f1[DB];
+#pragma unroll
+        for (int d = 0; d < DB; ++d) f0[d] = tr_read2(ks, ktlo[d] + o, kthi[d] + o);
         float dsv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -598,11 +649,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
         const bf16x8 d1 = pack_bf16(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
         // dQ^T += K^T dS^T
 #pragma unroll
-        for (int d = 0; d < DB; ++d) {
-          const int o = (kb * 32) * D;
-          acc[d] = mfma32(tr_read2(ks, ktlo[d] + o, kthi[d] + o), d0, acc[d]);
-          acc[d] = mfma32(tr_read2(ks, ktlo[d] + o + 16 * D, kthi[d] + o + 16 * D), d1, acc[d]);
-        }
+        for (int d = 0; d < DB; ++d) f1[d] = tr_read2(ks, ktlo[d] + o + 16 * D, kthi[d] + o + 16 * D);
+#pragma unroll
+        for (int d = 0; d < DB; ++d) acc[d] = mfma32(f0[d], d0, acc[d]);
+#pragma unroll
+        for (int d = 0; d < DB; ++d) acc[d] = mfma32(f1[d], d1, acc[d]);
       }
     }
     wait_dma();

@@ -150,13 +150,26 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_bf16_kernel(FwdParams
     for (int i = 0; i < NI; ++i) dma16_buf(rv, ld_voff[i], vd + (i * kWaves + wave) * 512);
   };
   // S^T of a 64-key tile in two 32-key blocks
+  // S^T of one tile: the two 32-key chains alternate, and the K operands of
+  // step t + 2 are read before the MFMAs of step t, so the LDS latency
+  // overlaps MFMAs instead of stalling each one.
   auto scores = [&](const __bf16* ks, f32x16 (&s)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) s[kb] = f32x16{};
+    bf16x8 a[3][2];
 #pragma unroll
-    for (int t = 0; t < KS; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(lds_read_b128(ks, koff[t] + kb * 32 * D), qf[t], s[kb]);
+      for (int kb = 0; kb < 2; ++kb) a[t][kb] = lds_read_b128(ks, koff[t] + kb * 32 * D);
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      if (t + 2 < KS) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) a[(t + 2) % 3][kb] = lds_read_b128(ks, koff[t + 2] + kb * 32 * D);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(a[t % 3][kb], qf[t], s[kb]);
+    }
   };
 
   f32x16 acc[DB];
@@ -217,17 +230,19 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_bf16_kernel(FwdParams
     scores(par ? k_lds0 : k_lds1, s_nxt);
     const float neg_m = -m_run;
     bf16x8 pb[4];
+    float lp[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: no serial chain of adds
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float e[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         e[r] = fast_exp2(__builtin_fmaf(s_cur[kb][r], c, neg_m));
-        l_run += e[r];
+        lp[r & 3] += e[r];
       }
       pb[2 * kb] = pack_bf16(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
       pb[2 * kb + 1] = pack_bf16(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
     }
+    l_run += (lp[0] + lp[1]) + (lp[2] + lp[3]);
     const __bf16* vs = par ? v_lds1 : v_lds0;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
