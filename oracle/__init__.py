@@ -18,5 +18,6 @@ from .attention import (  # noqa: F401
     attention_bwd_group,
     attention_dq_rows,
     attention_dkdv_rows,
+    merge_partials,
     e4m3_decode,
 )

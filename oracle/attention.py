@@ -37,6 +37,10 @@ What is computed (all in float64, every input upcast exactly):
   intermediates again (its memory section), and the forward keeps only O and
   the log-sum-exp. Here P is simply recomputed from the scores.
 
+* Merging: attention over two disjoint key sets combines into attention
+  over their union (``merge_partials``), the step Ring-Attention repeats as
+  K/V blocks travel around the ring.
+
 Layout: Q, O, dO, dQ are [B, S, Hq, D]; K, V, dK, dV are [B, S, Hkv, D];
 LSE is [B, Hq, S].
 """
@@ -365,6 +369,44 @@ def attention_dkdv_rows(q, k, v, do, picks: Iterable[tuple[int, int, int]], *, c
             ds = p * (doi @ vj - delta[lo:hi, h])
             dk[n] += scale * (ds @ qi)
     return dk, dv
+
+
+# ---------------------------------------------------------------------------
+# merging attention over disjoint key sets (Ring-Attention partials)
+# ---------------------------------------------------------------------------
+
+
+def merge_partials(o1, lse1, o2, lse2):
+    """Attention over the union of two disjoint key sets from the two parts.
+
+    Ring-Attention passes K/V blocks around a ring and accumulates partial
+    attention results locally until every device has seen the whole context
+    (FlashAttention page, sequence-parallel section, Ring-Attention
+    paragraph; "ms-swift支持GPU显存碎片整理提升利用率", section on
+    Ring-Attention). The pages give no formula. From the definition: row i's
+    softmax denominator over A ∪ B is e^{LSE_A} + e^{LSE_B}, and its output is
+    the denominator-weighted mean of the two partial outputs:
+        LSE = ln(e^{LSE_A} + e^{LSE_B}),
+        O = (e^{LSE_A} O_A + e^{LSE_B} O_B) / e^{LSE}.
+    Computed with the larger LSE factored out. A part with no visible key has
+    LSE = -inf and weight 0; if both are empty, O = 0 and LSE = -inf.
+    O [B, S, H, D], LSE [B, H, S]; returns (O, LSE) in float64.
+    """
+    o1 = np.asarray(o1, dtype=np.float64)
+    o2 = np.asarray(o2, dtype=np.float64)
+    l1 = np.asarray(lse1, dtype=np.float64)
+    l2 = np.asarray(lse2, dtype=np.float64)
+    m = np.maximum(l1, l2)
+    empty = np.isneginf(m)
+    m_safe = np.where(empty, 0.0, m)
+    w1 = np.where(np.isneginf(l1), 0.0, np.exp(l1 - m_safe))
+    w2 = np.where(np.isneginf(l2), 0.0, np.exp(l2 - m_safe))
+    tot = w1 + w2
+    lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, tot)))
+    # weights are [B, H, S]; outputs [B, S, H, D]
+    a1 = np.transpose(np.where(empty, 0.0, w1 / np.where(empty, 1.0, tot)), (0, 2, 1))[..., None]
+    a2 = np.transpose(np.where(empty, 0.0, w2 / np.where(empty, 1.0, tot)), (0, 2, 1))[..., None]
+    return a1 * o1 + a2 * o2, lse
 
 
 # ---------------------------------------------------------------------------

@@ -390,3 +390,75 @@ def test_e4m3_decoder_matches_torch_for_all_codes():
     assert np.array_equal(ours[ok], ref[ok])
     assert np.nanmax(ours) == 448.0 and np.nanmin(ours) == -448.0
     assert ours[1] == 2.0 ** -9  # smallest subnormal
+
+
+# ----------------------------------------------------------- merging -----
+
+@pytest.mark.parametrize("nchunk,hq,hkv", [(2, 1, 1), (3, 2, 1), (4, 4, 2)])
+def test_merge_of_key_chunks_equals_full_attention(nchunk, hq, hkv):
+    # non-causal attention over all keys = merge of attention over each key chunk
+    S, D = 8, 5
+    q, k, v = _rand((1, S, hq, D), 50), _rand((1, S, hkv, D), 51), _rand((1, S, hkv, D), 52)
+    ro, rl = oracle.attention_fwd(q, k, v, causal=False, scale=0.4)
+    bounds = np.linspace(0, S, nchunk + 1).astype(int)
+    o, l_ = None, None
+    for c0, c1 in zip(bounds[:-1], bounds[1:]):
+        # attention of every query over the keys c0 .. c1-1 only, written out here
+        po = np.zeros_like(q); pl = np.zeros((1, hq, S))
+        for h in range(hq):
+            kv = h // (hq // hkv)
+            s = 0.4 * q[0, :, h] @ k[0, c0:c1, kv].T
+            m = s.max(axis=1, keepdims=True)
+            w = np.exp(s - m)
+            po[0, :, h] = (w / w.sum(axis=1, keepdims=True)) @ v[0, c0:c1, kv]
+            pl[0, h] = m[:, 0] + np.log(w.sum(axis=1))
+        o, l_ = (po, pl) if o is None else oracle.merge_partials(o, l_, po, pl)
+    np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l_, rl, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("nchunk", [2, 4])
+def test_ring_layout_causal(nchunk):
+    # query chunk r: non-causal against key chunks c < r, causal against c = r,
+    # merged in ring order = rows of chunk r of the full causal attention
+    S, D, H = 12, 4, 2
+    q, k, v = _rand((1, S, H, D), 60), _rand((1, S, H, D), 61), _rand((1, S, H, D), 62)
+    ro, rl = oracle.attention_fwd(q, k, v, causal=True, scale=0.5)
+    L = S // nchunk
+    for r in range(nchunk):
+        qs = slice(r * L, (r + 1) * L)
+        o, l_ = None, None
+        for c in range(r + 1):
+            ks = slice(c * L, (c + 1) * L)
+            po, pl = oracle.attention_fwd(q[:, qs], k[:, ks], v[:, ks], causal=(c == r), scale=0.5)
+            o, l_ = (po, pl) if o is None else oracle.merge_partials(o, l_, po, pl)
+        np.testing.assert_allclose(o, ro[:, qs], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l_, rl[:, :, qs], rtol=0, atol=1e-12)
+
+
+def test_merge_with_empty_part_and_commutes():
+    o1, l1 = _rand((2, 5, 3, 4), 70), _rand((2, 3, 5), 71)
+    o2, l2 = _rand((2, 5, 3, 4), 72), _rand((2, 3, 5), 73)
+    empty_l = np.full_like(l1, -np.inf)
+    o, l_ = oracle.merge_partials(o1, l1, np.zeros_like(o1), empty_l)
+    np.testing.assert_array_equal(l_, l1)
+    np.testing.assert_allclose(o, o1, rtol=0, atol=1e-15)
+    o, l_ = oracle.merge_partials(np.zeros_like(o1), empty_l, np.zeros_like(o1), empty_l)
+    assert np.all(np.isneginf(l_)) and np.all(o == 0)
+    oa, la = oracle.merge_partials(o1, l1, o2, l2)
+    ob, lb = oracle.merge_partials(o2, l2, o1, l1)
+    np.testing.assert_allclose(oa, ob, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(la, lb, rtol=0, atol=1e-14)
+
+
+def test_merge_brute_force_two_rows():
+    # LSE = log(e^a + e^b) and O = (e^a x + e^b y) / (e^a + e^b), by math.fsum on scalars
+    rng = np.random.default_rng(80)
+    for _ in range(20):
+        a, b = rng.uniform(-30, 30, 2)
+        x, y = rng.standard_normal(2)
+        o, l_ = oracle.merge_partials(np.full((1, 1, 1, 1), x), np.full((1, 1, 1), a),
+                                      np.full((1, 1, 1, 1), y), np.full((1, 1, 1), b))
+        ea, eb = math.exp(a), math.exp(b)
+        assert abs(l_[0, 0, 0] - math.log(math.fsum([ea, eb]))) <= 1e-12 * max(1.0, abs(a), abs(b))
+        assert abs(o[0, 0, 0, 0] - math.fsum([ea * x, eb * y]) / math.fsum([ea, eb])) <= 1e-12

@@ -116,3 +116,40 @@ def test_backward_mutations_are_caught(kind, monkeypatch):
 
     monkeypatch.setattr(A, "_bwd_rows_block", mutated)
     assert _fd_fails()
+
+
+def _merge_pins_fail():
+    from tests import test_oracle as T
+    for fn, args in ((T.test_merge_of_key_chunks_equals_full_attention, (3, 2, 1)),
+                     (T.test_ring_layout_causal, (4,)), (T.test_merge_brute_force_two_rows, ())):
+        try:
+            with np.errstate(all="ignore"):
+                fn(*args)
+        except AssertionError:
+            return True
+    return False
+
+
+@pytest.mark.parametrize("kind", ["unnormalised", "swapped_weights", "lse_is_max", "weight_sign"])
+def test_merge_mutations_are_caught(kind, monkeypatch):
+    real = A.merge_partials
+
+    def mutated(o1, l1, o2, l2):
+        o1, o2 = np.asarray(o1, dtype=np.float64), np.asarray(o2, dtype=np.float64)
+        l1, l2 = np.asarray(l1, dtype=np.float64), np.asarray(l2, dtype=np.float64)
+        if kind == "lse_is_max":
+            o, _ = real(o1, l1, o2, l2)
+            return o, np.maximum(l1, l2)
+        m = np.maximum(l1, l2)
+        sgn = -1.0 if kind == "weight_sign" else 1.0
+        w1, w2 = np.exp(sgn * (l1 - m)), np.exp(sgn * (l2 - m))
+        if kind == "swapped_weights":
+            w1, w2 = w2, w1
+        tot = w1 + w2
+        norm = 1.0 if kind == "unnormalised" else tot
+        a1 = np.transpose(w1 / norm, (0, 2, 1))[..., None]
+        a2 = np.transpose(w2 / norm, (0, 2, 1))[..., None]
+        return a1 * o1 + a2 * o2, m + np.log(tot)
+
+    monkeypatch.setattr(oracle, "merge_partials", mutated)
+    assert _merge_pins_fail()
