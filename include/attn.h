@@ -138,6 +138,27 @@ attn_status attn_bwd_phases(unsigned phases, const void* q, const void* k, const
                             int causal, const int32_t* cu_seqlens, int num_seqs,
                             float scale, attn_stream_t stream);
 
+/* Ring-Attention step: merge one partial attention result into a running one.
+ * Ring-Attention passes K/V blocks around a ring and accumulates partial
+ * attention results locally (FlashAttention page, sequence-parallel section,
+ * Ring-Attention paragraph; Ring-Attention section of
+ * "ms-swift支持GPU显存碎片整理提升利用率"). Attention over two disjoint key
+ * sets combines exactly into attention over their union:
+ *   M = max(LSE_acc, LSE_part), w = e^(LSE - M) for each,
+ *   O = (w_acc O_acc + w_part O_part) / (w_acc + w_part),
+ *   LSE = M + ln(w_acc + w_part);
+ * a part with LSE = -inf has weight 0; if both do, O = 0 and LSE = -inf.
+ * o_acc: float32 [B,S,H,D] (read if accumulate, then overwritten with the
+ * merged O). lse_acc: float32 [B,H,S] (same). accumulate = 0 treats the
+ * running result as empty (first ring step: the merge copies the part).
+ * o_part: bfloat16 [B,S,H,D] and lse_part float32 [B,H,S], e.g. attn_fwd's
+ * outputs for one K/V block. o_out: bfloat16 [B,S,H,D] copy of the merged O
+ * (nearest-even), or NULL. The four arrays must not overlap. Each element is
+ * read and written by one thread, so o_acc/lse_acc are updated in place.
+ * head_dim 64 or 128; o_acc, o_part, o_out 16-byte aligned. */
+attn_status attn_merge(float* o_acc, float* lse_acc, const void* o_part, const float* lse_part, void* o_out,
+                       int batch, int seqlen, int heads, int head_dim, int accumulate, attn_stream_t stream);
+
 /* Static string naming a status code ("ATTN_OK", ...). Never NULL. */
 const char* attn_status_str(attn_status s);
 

@@ -52,6 +52,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_bwd_phases.argtypes = [ctypes.c_uint, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i,
                                     f, st]
     lib.attn_bwd_phases.restype = i
+    lib.attn_merge.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, st]
+    lib.attn_merge.restype = i
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_status_str.argtypes = [i]
@@ -64,7 +66,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
 
 
 EXPORTED = ("attn_fwd", "attn_fwd_fp8", "attn_bwd", "attn_bwd_phases", "attn_bwd_workspace_bytes",
-            "attn_status_str", "attn_last_hip_error")
+            "attn_merge", "attn_status_str", "attn_last_hip_error")
 
 BWD_DELTA, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 
@@ -149,6 +151,32 @@ def fwd_fp8(q8, k8, v8, descale_q, descale_k, descale_v, *, causal: bool, cu_seq
                                      _ptr(cu_seqlens), n, float(scale), _stream())
     _check(st, "attn_fwd_fp8")
     return o, l_
+
+
+def merge(o_acc, lse_acc, o_part, lse_part, *, accumulate: bool = True, o_out=None):
+    """Ring-Attention step: merge (o_part bf16, lse_part) into (o_acc fp32, lse_acc) in place.
+
+    o_acc/o_part/o_out [B,S,H,D]; lse_acc/lse_part [B,H,S] fp32. With
+    accumulate=False the running result is treated as empty. o_out (bf16) also
+    receives the merged output if given. Returns (o_acc, lse_acc).
+    """
+    import torch
+    _check_tensors(o_acc, lse_acc, lse_part, dtype=torch.float32)
+    _check_tensors(o_part, dtype=torch.bfloat16)
+    if o_acc.dim() != 4 or tuple(o_part.shape) != tuple(o_acc.shape):
+        raise ValueError("o_acc and o_part must both be [B, S, H, D]")
+    B, S, H, D = o_acc.shape
+    for t in (lse_acc, lse_part):
+        if tuple(t.shape) != (B, H, S):
+            raise ValueError("lse_acc and lse_part must be [B, H, S]")
+    if o_out is not None:
+        _check_tensors(o_out, dtype=torch.bfloat16)
+        if tuple(o_out.shape) != (B, S, H, D):
+            raise ValueError("o_out must be [B, S, H, D]")
+    st = load_library().attn_merge(_ptr(o_acc), _ptr(lse_acc), _ptr(o_part), _ptr(lse_part), _ptr(o_out), B, S, H,
+                                   D, int(bool(accumulate)), _stream())
+    _check(st, "attn_merge")
+    return o_acc, lse_acc
 
 
 def bwd_workspace_bytes(batch: int, hq: int, seqlen: int) -> int:

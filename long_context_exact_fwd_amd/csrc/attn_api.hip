@@ -166,6 +166,30 @@ attn_status attn_bwd_phases(unsigned phases, const void* q, const void* k, const
   return launch_result(mi355attn::run_bwd(p, phases, reinterpret_cast<hipStream_t>(stream)));
 }
 
+attn_status attn_merge(float* o_acc, float* lse_acc, const void* o_part, const float* lse_part, void* o_out,
+                       int batch, int seqlen, int heads, int head_dim, int accumulate, attn_stream_t stream) {
+  if (!o_acc || !lse_acc || !o_part || !lse_part) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned16(o_acc) || !aligned16(o_part) || (o_out && !aligned16(o_out))) return ATTN_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(lse_acc) & 3u) || (reinterpret_cast<uintptr_t>(lse_part) & 3u))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (batch < 1 || seqlen < 1 || heads < 1 || head_dim < 1) return ATTN_ERR_INVALID_ARGUMENT;
+  if (accumulate != 0 && accumulate != 1) return ATTN_ERR_INVALID_ARGUMENT;
+  if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)batch * seqlen * heads * (head_dim / 8) > (long long)UINT32_MAX * 256) return ATTN_ERR_UNSUPPORTED;
+  mi355attn::MergeParams p{};
+  p.o_acc = o_acc;
+  p.lse_acc = lse_acc;
+  p.o_part = static_cast<const __bf16*>(o_part);
+  p.lse_part = lse_part;
+  p.o_out = static_cast<__bf16*>(o_out);
+  p.batch = batch;
+  p.seqlen = seqlen;
+  p.heads = heads;
+  p.head_dim = head_dim;
+  p.accumulate = accumulate;
+  return launch_result(mi355attn::run_merge(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                      void* dq, void* dk, void* dv, void* workspace, int batch, int hq, int hkv, int seqlen,
                      int head_dim, int causal, const int32_t* cu_seqlens, int num_seqs, float scale,

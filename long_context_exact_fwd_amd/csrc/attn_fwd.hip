@@ -149,7 +149,6 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_bf16_kernel(FwdParams
 #pragma unroll
     for (int i = 0; i < NI; ++i) dma16_buf(rv, ld_voff[i], vd + (i * kWaves + wave) * 512);
   };
-  // S^T of a 64-key tile in two 32-key blocks
   // S^T of one tile: the two 32-key chains alternate, and the K operands of
   // step t + 2 are read before the MFMAs of step t, so the LDS latency
   // overlaps MFMAs instead of stalling each one.

@@ -66,9 +66,20 @@ struct BwdParams {
 constexpr int kStatAlign = 64;
 inline int stat_stride_for(int seqlen) { return (seqlen + kStatAlign - 1) / kStatAlign * kStatAlign; }
 
+struct MergeParams {
+  float* o_acc;            // [B, S, H, D] fp32, read if accumulate, written
+  float* lse_acc;          // [B, H, S] fp32, read if accumulate, written
+  const __bf16* o_part;    // [B, S, H, D] bf16
+  const float* lse_part;   // [B, H, S] fp32
+  __bf16* o_out;           // [B, S, H, D] bf16 or null
+  int batch, seqlen, heads, head_dim;
+  int accumulate;
+};
+
 hipError_t run_fwd_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t run_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream);
 constexpr unsigned kBwdDelta = 1u, kBwdDkDv = 2u, kBwdDq = 4u;
 hipError_t run_bwd(const BwdParams& p, unsigned phases, hipStream_t stream);
+hipError_t run_merge(const MergeParams& p, hipStream_t stream);
 
 }  // namespace mi355attn

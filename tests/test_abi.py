@@ -119,3 +119,22 @@ def test_unsupported_head_dims(D):
 def test_binding_raises_without_library(tmp_path):
     with pytest.raises(ImportError):
         lca.load_library(str(tmp_path / "missing.so"))
+
+
+def _merge(**kw):
+    a = dict(oa=P, la=P, op=P, lp=P, out=NULL, B=1, S=128, H=4, D=128, acc=1)
+    a.update(kw)
+    return lca.load_library().attn_merge(a["oa"], a["la"], a["op"], a["lp"], a["out"], a["B"], a["S"], a["H"],
+                                         a["D"], a["acc"], S0)
+
+
+@pytest.mark.parametrize("kw", [dict(oa=NULL), dict(la=NULL), dict(op=NULL), dict(lp=NULL), dict(oa=PM),
+                                dict(op=PM), dict(out=PM), dict(la=ctypes.c_void_p((1 << 20) + 2)),
+                                dict(B=0), dict(S=0), dict(H=-1), dict(D=0), dict(acc=2)])
+def test_merge_invalid_arguments_rejected(kw):
+    assert _merge(**kw) == lca.ATTN_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("D", [32, 80, 256])
+def test_merge_unsupported_head_dims(D):
+    assert _merge(D=D) == lca.ATTN_ERR_UNSUPPORTED

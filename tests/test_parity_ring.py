@@ -1,0 +1,152 @@
+"""GPU parity for the Ring-Attention pieces, through the C ABI.
+
+* attn_merge against the oracle's merge of two partial results, including
+  parts with no visible key (LSE = -inf) and rows where neither part has one;
+* a ring forward on one GPU: the sequence is cut into N chunks, query chunk r
+  attends to key chunks c <= r (non-causal for c < r, causal for c = r) with
+  attn_fwd, and the partial results are merged in ring order. It must equal
+  the oracle's full attention (bf16 tolerances: O max-abs <= 1e-2 or one bf16
+  ulp, rel-L2 <= 5e-3; LSE <= 1e-3);
+* the matching backward: attn_bwd on every (query chunk, key chunk) pair with
+  the final O and LSE gives the global probabilities restricted to that
+  chunk pair, so the pair gradients summed over chunks must equal the
+  oracle's full gradients (rel-L2 <= 1e-2).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+from tests.gpu_helpers import check_fwd, check_grads, dev_bf16, host, max_abs
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import long_context_exact_fwd_amd as lca
+    return lca
+
+
+MERGE_CASES = [
+    # B, S, H, D, accumulate, with_out
+    (1, 37, 3, 128, True, True),
+    (2, 100, 2, 64, True, False),
+    (1, 1, 1, 128, False, True),
+    (1, 513, 5, 64, False, False),
+]
+
+
+@pytest.mark.parametrize("B,S,H,D,acc,with_out", MERGE_CASES)
+def test_merge_kernel_matches_oracle(B, S, H, D, acc, with_out):
+    import torch
+    lca = _lib()
+    print(f"merge B={B} S={S} H={H} D={D} accumulate={acc} out={with_out}", flush=True)
+    rng = np.random.default_rng(S * 31 + H)
+    o1 = rng.standard_normal((B, S, H, D)).astype(np.float32)
+    l1 = rng.uniform(-20, 20, (B, H, S)).astype(np.float32)
+    p_bits = si.bf16_bits_from_f32(rng.standard_normal((B, S, H, D)).astype(np.float32))
+    l2 = (l1 + rng.uniform(-30, 30, (B, H, S))).astype(np.float32)
+    # empty parts: some rows with no key in the running part, some in the new part, some in both
+    l1.reshape(-1)[::7] = -np.inf
+    l2.reshape(-1)[::5] = -np.inf
+    dev = torch.device("cuda")
+    o_acc = torch.from_numpy(o1.copy()).to(dev)
+    lse_acc = torch.from_numpy(l1.copy()).to(dev)
+    o_part = dev_bf16(p_bits)
+    lse_part = torch.from_numpy(l2).to(dev)
+    o_out = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=dev) if with_out else None
+    lca.merge(o_acc, lse_acc, o_part, lse_part, accumulate=acc, o_out=o_out)
+    torch.cuda.synchronize()
+    r_o1 = o1.astype(np.float64) if acc else np.zeros_like(o1, dtype=np.float64)
+    r_l1 = l1.astype(np.float64) if acc else np.full(l1.shape, -np.inf)
+    ro, rl = oracle.merge_partials(r_o1, r_l1, si.bf16_bits_to_f64(p_bits), l2.astype(np.float64))
+    go, gl = host(o_acc), host(lse_acc)
+    assert np.array_equal(np.isneginf(gl), np.isneginf(rl)), "empty rows differ"
+    fin = np.isfinite(rl)
+    err_l = float(np.max(np.abs(gl[fin] - rl[fin]))) if fin.any() else 0.0
+    err_o = max_abs(go, ro)
+    print(f"merge O maxabs={err_o:.3e} LSE maxabs={err_l:.3e}", flush=True)
+    # fp32 arithmetic on O(1) values and LSEs of magnitude <= 50
+    assert err_o <= 2e-6 and err_l <= 2e-5
+    if with_out:
+        # the bf16 copy is the fp32 result rounded to nearest
+        gb = host(o_out)
+        assert np.max(np.abs(gb - go) - np.abs(go) * 2.0 ** -8) <= 0.0
+
+
+def _ring_inputs(B, Hq, Hkv, S, D, seed):
+    x = si.make_inputs(B, Hq, Hkv, S, D, seed)
+    return x, dev_bf16(x.q_bits), dev_bf16(x.k_bits), dev_bf16(x.v_bits), dev_bf16(x.do_bits)
+
+
+def ring_forward(q, k, v, nchunk, causal, scale):
+    """Ring order on one GPU: query chunk r merges its partials over key chunks 0..r (all chunks if not causal)."""
+    import torch
+    lca = _lib()
+    B, S, Hq, D = q.shape
+    L = S // nchunk
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    for r in range(nchunk):
+        qr = q[:, r * L:(r + 1) * L].contiguous()
+        o_acc = torch.empty((B, L, Hq, D), dtype=torch.float32, device=q.device)
+        l_acc = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+        o_r = torch.empty((B, L, Hq, D), dtype=torch.bfloat16, device=q.device)
+        chunks = list(range(r + 1)) if causal else list(range(nchunk))
+        for i, c in enumerate(chunks):
+            kc = k[:, c * L:(c + 1) * L].contiguous()
+            vc = v[:, c * L:(c + 1) * L].contiguous()
+            po, pl = lca.fwd(qr, kc, vc, causal=(causal and c == r), scale=scale)
+            lca.merge(o_acc, l_acc, po, pl, accumulate=(i > 0), o_out=o_r if i == len(chunks) - 1 else None)
+        o[:, r * L:(r + 1) * L] = o_r
+        lse[:, :, r * L:(r + 1) * L] = l_acc
+    return o, lse
+
+
+def ring_backward(q, k, v, o, lse, do, nchunk, causal, scale):
+    """Pair backward with the final O and LSE; gradients summed over chunk pairs in fp32."""
+    import torch
+    lca = _lib()
+    B, S, Hq, D = q.shape
+    L = S // nchunk
+    dq = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.zeros(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.zeros(v.shape, dtype=torch.float32, device=q.device)
+    for r in range(nchunk):
+        rs = slice(r * L, (r + 1) * L)
+        qr, orr, dor = q[:, rs].contiguous(), o[:, rs].contiguous(), do[:, rs].contiguous()
+        lr = lse[:, :, rs].contiguous()
+        for c in (range(r + 1) if causal else range(nchunk)):
+            cs = slice(c * L, (c + 1) * L)
+            g = lca.bwd(qr, k[:, cs].contiguous(), v[:, cs].contiguous(), orr, lr, dor,
+                        causal=(causal and c == r), scale=scale)
+            dq[:, rs] += g[0].float()
+            dk[:, cs] += g[1].float()
+            dv[:, cs] += g[2].float()
+    return dq, dk, dv
+
+
+RING_CASES = [
+    # B, Hq, Hkv, S, D, nchunk, causal
+    (1, 4, 2, 512, 128, 2, True),
+    (1, 4, 2, 512, 128, 4, True),
+    (2, 2, 1, 384, 64, 3, True),
+    (1, 3, 3, 256, 128, 4, False),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,D,nchunk,causal", RING_CASES)
+def test_ring_forward_and_backward_equal_full_attention(B, Hq, Hkv, S, D, nchunk, causal):
+    import torch
+    print(f"ring B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} N={nchunk} causal={causal}", flush=True)
+    x, q, k, v, do = _ring_inputs(B, Hq, Hkv, S, D, seed=90 + nchunk)
+    scale = 1.0 / np.sqrt(D)
+    o, lse = ring_forward(q, k, v, nchunk, causal, scale)
+    torch.cuda.synchronize()
+    qv, kv, vv = x.values("q"), x.values("k"), x.values("v")
+    ro, rl = oracle.attention_fwd(qv, kv, vv, causal=causal, scale=scale, workers=None)
+    check_fwd(host(o), host(lse), ro, rl, tag="ring fwd")
+    dq, dk, dv = ring_backward(q, k, v, o, lse, do, nchunk, causal, scale)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_bwd(qv, kv, vv, x.values("do"), causal=causal, scale=scale, workers=None)
+    check_grads([("dQ", host(dq), rq), ("dK", host(dk), rk), ("dV", host(dv), rv)], tag="ring bwd")
