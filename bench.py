@@ -20,7 +20,9 @@ Prints one JSON line. The roofline object describes the kernel with the
 largest share of the step time. ``cpu_baseline`` times the fp64 oracle on a
 bounded sample of the same workload on the host cores. ``workloads`` holds
 the other configurations measured the same way (mid: bf16 forward; packed32k:
-packed fwd+bwd; fp8_64k: fp8 forward against the fp8 dense peak).
+packed fwd+bwd; fp8_64k: fp8 forward against the fp8 dense peak; ring4_gqa32k:
+the gqa32k forward as a 4-chunk Ring-Attention pass with attn_merge, plus the
+merge kernel's HBM rate).
 
     python bench.py [--steps 20] [--warmup 3] [--gpus 1] [--no-secondary]
 """
@@ -56,6 +58,7 @@ KERNEL_SOURCES = {
     "attn_bwd_dq_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h"),
     "attn_bwd_delta_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h"),
     "attn_fwd_fp8_kernel": ("attn_fwd_fp8.hip", "attn_device.h", "attn_internal.h"),
+    "attn_merge_kernel": ("attn_merge.hip", "attn_device.h", "attn_internal.h"),
 }
 KERNEL_OF_PHASE = {"attn_fwd": "attn_fwd_bf16_kernel", "bwd_delta": "attn_bwd_delta_kernel",
                    "bwd_dkdv": "attn_bwd_dkdv_kernel", "bwd_dq": "attn_bwd_dq_kernel"}
@@ -215,6 +218,75 @@ def secondary(name, steps, warmup, dev):
     }
 
 
+def ring_case(nchunk, steps, warmup, dev):
+    """Ring-Attention forward of the gqa32k shape on one GPU, plus the merge kernel on its own.
+
+    Query chunk r attends to key chunks 0..r (non-causal for c < r, causal for
+    c = r) with attn_fwd, and attn_merge folds each partial into the chunk's
+    running fp32 result, in ring order. All chunks' work runs on this GPU, so
+    the visible pairs are those of the full causal sequence.
+    """
+    import torch
+    import seeded_inputs as si
+    import long_context_exact_fwd_amd as lca
+    w = si.WORKLOADS["gqa32k"]
+    x = si.workload_inputs(w, with_do=False)
+    up = lca.bf16_from_bits
+    q, k, v = up(x.q_bits, dev), up(x.k_bits, dev), up(x.v_bits, dev)
+    B, S, Hq, D = q.shape
+    L = S // nchunk
+    qs = [q[:, r * L:(r + 1) * L].contiguous() for r in range(nchunk)]
+    ks = [k[:, c * L:(c + 1) * L].contiguous() for c in range(nchunk)]
+    vs = [v[:, c * L:(c + 1) * L].contiguous() for c in range(nchunk)]
+    del q, k, v
+    po = torch.empty((B, L, Hq, D), dtype=torch.bfloat16, device=dev)
+    pl = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+    o_acc = [torch.empty((B, L, Hq, D), dtype=torch.float32, device=dev) for _ in range(nchunk)]
+    l_acc = [torch.empty((B, Hq, L), dtype=torch.float32, device=dev) for _ in range(nchunk)]
+    o_out = [torch.empty((B, L, Hq, D), dtype=torch.bfloat16, device=dev) for _ in range(nchunk)]
+
+    def step(tm, i):
+        if tm is not None:
+            tm.mark(i, 0)
+        for r in range(nchunk):
+            for c in range(r + 1):
+                lca.fwd(qs[r], ks[c], vs[c], causal=(c == r), scale=w.scale, out=po, lse=pl)
+                lca.merge(o_acc[r], l_acc[r], po, pl, accumulate=(c > 0), o_out=o_out[r] if c == r else None)
+        if tm is not None:
+            tm.mark(i, 1)
+
+    ms, _ = run_steps(step, ["ring_fwd"], steps, warmup)
+    pairs = _pairs(S, True) * B * Hq
+    tf = 4.0 * D * pairs / (ms * 1e-3) / 1e12
+
+    # the merge kernel alone: accumulate into chunk 0's running result, no bf16 copy
+    reps = 50
+    for _ in range(3):
+        lca.merge(o_acc[0], l_acc[0], po, pl, accumulate=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        lca.merge(o_acc[0], l_acc[0], po, pl, accumulate=True)
+    e1.record()
+    torch.cuda.synchronize()
+    m_ms = e0.elapsed_time(e1) / reps
+    elems, rows = B * L * Hq * D, B * L * Hq
+    m_bytes = elems * (4 + 2 + 4) + rows * (4 + 4 + 4)  # O_acc read + O_part read + O_acc write; 3 LSEs
+    gbs = m_bytes / (m_ms * 1e-3) / 1e9
+    return {
+        "config": f"ring forward of gqa32k (B={B} Hq={Hq} Hkv={w.hkv} S={S} D={D} causal bf16) in {nchunk} chunks "
+                  f"of {L}: attn_fwd per (query chunk, key chunk <= it) + attn_merge, all on one GPU, "
+                  f"N(0,1) seed {w.seed}",
+        "tflops": round(tf, 2), "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2), "peak_tflops": PEAK_BF16_TFLOPS,
+        "ms_per_step": round(ms, 4), "steps": steps,
+        "merge": {"kernel": "attn_merge_kernel", "bound": "hbm", "avg_launch_ms": round(m_ms, 5),
+                  "algorithmic_bytes_per_launch": m_bytes, "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                  "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                  "shape": f"O [{B},{L},{Hq},{D}] fp32 running + bf16 part, accumulate"},
+    }
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -307,6 +379,9 @@ def main(argv=None) -> int:
         for name in ("mid", "packed32k", "fp8_64k"):
             result["workloads"][name] = secondary(name, sec_steps, min(2, a.warmup), dev)
             print(f"bench: {name} done", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        result["workloads"]["ring4_gqa32k"] = ring_case(4, sec_steps, min(2, a.warmup), dev)
+        print("bench: ring4_gqa32k done", file=sys.stderr, flush=True)
     if not a.no_cpu_baseline:
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, x, a.cpu_sample_len)
