@@ -150,3 +150,38 @@ def test_fp8_64k_full_forward_sampled():
     print(f"fp8_64k sampled ({len(picks)} rows): O relL2={rr:.3e} LSE maxabs={rlse:.3e}", flush=True)
     assert np.all(np.isfinite(o_h)) and np.all(np.isfinite(lse_h))
     assert rr <= TOL_FP8_REL and rlse <= TOL_LSE
+
+
+def test_long_sequence_256k_sampled():
+    """B=1, Hq=2, Hkv=1, S=262144, D=128 causal fwd + bwd: the longest sequence tested, for the 32-bit
+    row and byte arithmetic of the kernels. Forward and dQ on sampled rows; dK/dV through the whole-tensor
+    identities (sum_j dK_j = 0, sum_j dV_j = sum_i dO_i), which involve every key row."""
+    import torch
+    import long_context_exact_fwd_amd as lca
+    B, Hq, Hkv, S, D, seed = 1, 2, 1, 262144, 128, 21
+    print(f"long case: B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} causal seed={seed}", flush=True)
+    x = si.make_inputs(B, Hq, Hkv, S, D, seed)
+    q, k, v = _upload(x)
+    do = lca.bf16_from_bits(x.do_bits, "cuda")
+    scale = 1.0 / np.sqrt(D)
+    o, lse = lca.fwd(q, k, v, causal=True, scale=scale)
+    dq, dk, dv = lca.bwd(q, k, v, o, lse, do, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    print("long case: GPU done", flush=True)
+    o_h, lse_h, dq_h, dk_h, dv_h = host(o), host(lse), host(dq), host(dk), host(dv)
+    assert np.all(np.isfinite(o_h)) and np.all(np.isfinite(dq_h)) and np.all(np.isfinite(dk_h))
+    rows = si.sample_indices(seed, S, 48, must=[0, 1, 65535, 65536, 131071, 131072, S - 2, S - 1])
+    picks = [(0, h, int(i)) for h in range(Hq) for i in rows]
+    qv, kv, vv = x.values("q"), x.values("k"), x.values("v")
+    ro, rl = oracle.attention_fwd_rows(qv, kv, vv, picks, causal=True, scale=scale)
+    check_fwd(np.stack([o_h[0, i, h] for _, h, i in picks]), np.array([lse_h[0, h, i] for _, h, i in picks]),
+              ro, rl, tag=f"long fwd ({len(picks)} rows)")
+    dov = x.values("do")
+    rq = oracle.attention_dq_rows(qv, kv, vv, dov, picks, causal=True, scale=scale)
+    e_q = rel_l2(np.stack([dq_h[0, i, h] for _, h, i in picks]), rq)
+    sk = dk_h[0, :, 0].sum(axis=0)
+    e_k = float(np.linalg.norm(sk) / np.linalg.norm(dk_h[0, :, 0]))
+    e_v = rel_l2(dv_h[0, :, 0].sum(axis=0), dov[0, :, :].sum(axis=(0, 1)))
+    print(f"long bwd: dQ relL2={e_q:.3e} ({len(picks)} rows); |sum dK|/|dK|={e_k:.3e}; sum dV vs sum dO "
+          f"relL2={e_v:.3e}", flush=True)
+    assert e_q <= TOL_GRAD_REL and e_k <= 1e-2 and e_v <= 1e-2
