@@ -162,7 +162,7 @@ def bf16_case(w, x, dev):
     if w.backward:
         do = up(x.do_bits, dev)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        ws = torch.empty(lca.bwd_workspace_bytes(B, Hq, S) // 4, dtype=torch.float32, device=dev)
+        ws = torch.empty(lca.bwd_workspace_bytes(B, Hq, w.hkv, S, w.head_dim) // 4, dtype=torch.float32, device=dev)
         names += ["bwd_delta", "bwd_dkdv", "bwd_dq"]
 
     def step(tm, i):

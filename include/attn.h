@@ -98,14 +98,16 @@ attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                          int causal, const int32_t* cu_seqlens, int num_seqs,
                          float scale, attn_stream_t stream);
 
-/* Bytes of device workspace attn_bwd needs: 8 * batch * hq * S64 + 8 * NB,
- * with S64 = seqlen rounded up to a multiple of 64 and NB = ceil(seqlen / 128).
- * It holds two fp32 per-row arrays of [batch, hq, S64], Delta_i = dO_i . O_i
- * and LSE_i * log2(e) (the padding rows are written as zeros), then two int32
- * arrays of NB entries: the order in which the dK/dV and the dQ kernels take
- * their 128-row blocks, heaviest first under the mask. Returns 0 for
- * non-positive sizes. */
-size_t attn_bwd_workspace_bytes(int batch, int hq, int seqlen);
+/* Bytes of device workspace attn_bwd needs for these sizes. It holds, in
+ * order: two fp32 per-row arrays [batch, hq, S64] (S64 = seqlen rounded up to
+ * a multiple of 64): Delta_i = dO_i . O_i and LSE_i * log2(e), the padding
+ * rows written as zeros; the int32 work order of the dK/dV and dQ kernels
+ * (NB * (split + 1) entries, NB = ceil(seqlen / 128)); and, when the dK/dV
+ * pass splits the query heads of a GQA group over `split` > 1 workgroups
+ * (chosen from the sizes, for grids too small to fill the GPU), 256-byte
+ * aligned fp32 partial dK and dV of 8 * split * batch * seqlen * hkv *
+ * head_dim bytes. Returns 0 for non-positive sizes or hq % hkv != 0. */
+size_t attn_bwd_workspace_bytes(int batch, int hq, int hkv, int seqlen, int head_dim);
 
 /* Backward: dq, dk, dv from q, k, v, the forward's o and lse, and dout.
  * The probabilities are recomputed from lse. No S x S buffer is used.

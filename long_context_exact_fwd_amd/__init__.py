@@ -54,7 +54,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_bwd_phases.restype = i
     lib.attn_merge.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, st]
     lib.attn_merge.restype = i
-    lib.attn_bwd_workspace_bytes.argtypes = [i, i, i]
+    lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_status_str.argtypes = [i]
     lib.attn_status_str.restype = ctypes.c_char_p
@@ -179,8 +179,8 @@ def merge(o_acc, lse_acc, o_part, lse_part, *, accumulate: bool = True, o_out=No
     return o_acc, lse_acc
 
 
-def bwd_workspace_bytes(batch: int, hq: int, seqlen: int) -> int:
-    return int(load_library().attn_bwd_workspace_bytes(batch, hq, seqlen))
+def bwd_workspace_bytes(batch: int, hq: int, hkv: int, seqlen: int, head_dim: int) -> int:
+    return int(load_library().attn_bwd_workspace_bytes(batch, hq, hkv, seqlen, head_dim))
 
 
 def bwd(q, k, v, o, lse, do, *, causal: bool, cu_seqlens=None, scale: Optional[float] = None, workspace=None,
@@ -199,7 +199,7 @@ def bwd(q, k, v, o, lse, do, *, causal: bool, cu_seqlens=None, scale: Optional[f
     dq = dq if dq is not None else torch.empty_like(q)
     dk = dk if dk is not None else torch.empty_like(k)
     dv = dv if dv is not None else torch.empty_like(v)
-    nbytes = bwd_workspace_bytes(B, Hq, S)
+    nbytes = bwd_workspace_bytes(B, Hq, Hkv, S, D)
     if workspace is None:
         workspace = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=q.device)
     elif not (workspace.is_contiguous() and workspace.numel() * workspace.element_size() >= nbytes

@@ -59,10 +59,9 @@ const char* attn_status_str(attn_status s) {
 
 int attn_last_hip_error(void) { return g_last_hip_error; }
 
-size_t attn_bwd_workspace_bytes(int batch, int hq, int seqlen) {
-  if (batch <= 0 || hq <= 0 || seqlen <= 0) return 0;
-  const size_t nblk = ((size_t)seqlen + 127) / 128;
-  return (size_t)8 * (size_t)batch * (size_t)hq * (size_t)mi355attn::stat_stride_for(seqlen) + 8 * nblk;
+size_t attn_bwd_workspace_bytes(int batch, int hq, int hkv, int seqlen, int head_dim) {
+  if (batch <= 0 || hq <= 0 || hkv <= 0 || seqlen <= 0 || head_dim <= 0 || hq % hkv != 0) return 0;
+  return mi355attn::bwd_workspace_size(batch, hq, hkv, seqlen, head_dim);
 }
 
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
@@ -152,7 +151,12 @@ attn_status attn_bwd_phases(unsigned phases, const void* q, const void* k, const
   p.stat_stride = mi355attn::stat_stride_for(seqlen);
   p.delta = static_cast<float*>(workspace);
   p.lse2 = p.delta + (size_t)batch * hq * p.stat_stride;
-  p.order = reinterpret_cast<int*>(p.lse2 + (size_t)batch * hq * p.stat_stride);
+  p.order = reinterpret_cast<int*>(static_cast<char*>(workspace) + mi355attn::bwd_order_offset(batch, hq, seqlen));
+  p.head_split = mi355attn::bwd_head_split(batch, hq, hkv, seqlen);
+  p.part = p.head_split > 1
+               ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          mi355attn::bwd_part_offset(batch, hq, hkv, seqlen))
+               : nullptr;
   p.cu_seqlens = cu_seqlens;
   p.num_seqs = num_seqs;
   p.batch = batch;

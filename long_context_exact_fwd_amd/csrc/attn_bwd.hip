@@ -33,16 +33,17 @@ constexpr int kQT = 64;  // queries per tile (dK/dV pass)
 constexpr int kKT = 64;  // keys per tile (dQ pass)
 
 // ---------------------------------------------------------------------------
-// Work order. The dK/dV and dQ passes each run one workgroup per 128-row
-// block, and a block's cost is the number of 64-row tiles of the other
-// operand it visits. Under a causal or packed mask the costs differ by up to
-// the longest segment over the tile size, and with about two blocks per CU
-// the launch order decides the makespan: both passes launch their blocks
-// heaviest first (longest-processing-time order). For a single causal
-// sequence this is key blocks from the start and query blocks from the end.
+// Work order. The dK/dV and dQ passes run one workgroup per 128-row block
+// (dK/dV: per block and share of the group's query heads), and a workgroup's
+// cost is the number of 64-row tiles of the other operand it visits, times
+// its heads. Under a causal or packed mask the costs differ by up to the
+// longest segment over the tile size, and with a few workgroups per CU the
+// launch order decides the makespan: both passes launch their work heaviest
+// first (longest-processing-time order). For a single causal sequence this
+// is key blocks from the start and query blocks from the end.
 // ---------------------------------------------------------------------------
 template <bool CAUSAL>
-__device__ int block_cost(const BwdParams& p, int pass, int blk) {
+__device__ int block_tiles(const BwdParams& p, int pass, int blk) {
   const int r0 = blk * 128;
   const int r1 = min(r0 + 128, p.seqlen) - 1;
   int s0a, s1a, s0b, s1b;
@@ -54,34 +55,52 @@ __device__ int block_cost(const BwdParams& p, int pass, int blk) {
   return (hi + 63) / 64 - lo / 64;
 }
 
-// Rank of each block by descending cost, ties by index; order[rank] = block.
-// Each thread ranks one block against all of them, 256 at a time through LDS.
+// Query heads [g0, g1) of a group of G handled by share `split` of `ns`.
+__device__ __forceinline__ void head_share(int G, int ns, int split, int& g0, int& g1) {
+  g0 = split * G / ns;
+  g1 = (split + 1) * G / ns;
+}
+
+// Entry e of a pass: dK/dV (pass 0) e = key block * head_split + share; dQ (pass 1) e = query block.
+template <bool CAUSAL>
+__device__ int entry_cost(const BwdParams& p, int pass, int e) {
+  if (pass == 1) return block_tiles<CAUSAL>(p, 1, e);
+  const int ns = p.head_split;
+  int g0, g1;
+  head_share(p.hq / p.hkv, ns, e % ns, g0, g1);
+  return block_tiles<CAUSAL>(p, 0, e / ns) * (g1 - g0);
+}
+
+// Rank of each entry by descending cost, ties by index; order[rank] = entry.
+// Each thread ranks one entry against all of the pass, 256 at a time through LDS.
 template <bool CAUSAL>
 __device__ void block_order(const BwdParams& p, int wg) {
   __shared__ int cost[256];
-  const int nblk = p.num_blk;
-  const int per_pass = (nblk + 255) / 256;
-  const int pass = wg / per_pass;
-  const int i = (wg - pass * per_pass) * 256 + (int)threadIdx.x;
-  const int mine = i < nblk ? block_cost<CAUSAL>(p, pass, i) : 0;
+  const int n0 = p.num_blk * p.head_split, n1 = p.num_blk;
+  const int c0 = (n0 + 255) / 256;
+  const int pass = wg < c0 ? 0 : 1;
+  const int n = pass == 0 ? n0 : n1;
+  const int i = (pass == 0 ? wg : wg - c0) * 256 + (int)threadIdx.x;
+  const int mine = i < n ? entry_cost<CAUSAL>(p, pass, i) : 0;
   int rank = 0;
-  for (int c = 0; c < nblk; c += 256) {
+  for (int c = 0; c < n; c += 256) {
     const int j = c + (int)threadIdx.x;
     __syncthreads();
-    cost[threadIdx.x] = j < nblk ? block_cost<CAUSAL>(p, pass, j) : INT32_MIN;
+    cost[threadIdx.x] = j < n ? entry_cost<CAUSAL>(p, pass, j) : INT32_MIN;
     __syncthreads();
-    const int m = min(256, nblk - c);
+    const int m = min(256, n - c);
     for (int t = 0; t < m; ++t) {
       const int cj = cost[t];
       rank += (cj > mine) || (cj == mine && c + t < i);
     }
   }
-  if (i < nblk) p.order[pass * nblk + rank] = i;
+  if (i < n) p.order[(pass == 0 ? 0 : n0) + rank] = i;
 }
 
 // ---------------------------------------------------------------------------
 // Delta_i = dO_i . O_i and LSE_i * log2(e), both fp32 [B, Hq, S]; the last
-// 2 * ceil(num_blk / 256) workgroups write the work order instead.
+// ceil(num_blk * head_split / 256) + ceil(num_blk / 256) workgroups write the
+// work order instead.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
@@ -163,7 +182,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   const int hk = bh - b * p.hkv;
   const int G = p.hq / p.hkv;
   // clamped, so that a workspace without a Delta pass gives wrong sums, never a stray address
-  const int k0 = (int)min((unsigned)p.order[blockIdx.y], (unsigned)(p.num_blk - 1)) * 128;
+  const int ns = p.head_split;
+  const int entry = (int)min((unsigned)p.order[blockIdx.y], (unsigned)(p.num_blk * ns - 1));
+  const int kblk = __builtin_amdgcn_readfirstlane(entry / ns);
+  const int split = __builtin_amdgcn_readfirstlane(entry - kblk * ns);
+  const int k0 = kblk * 128;
   const int my_k = k0 + pair * 32 + n;
   const bool k_ok = my_k < p.seqlen;
   const int kv_stride = p.hkv * D;
@@ -198,7 +221,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   const int tile_begin = wg_hi > wg_lo ? wg_lo / kQT : 0;
   const int tile_end = wg_hi > wg_lo ? (wg_hi + kQT - 1) / kQT : 0;
   const int ntiles = tile_end - tile_begin;
-  const int nsteps = ntiles * G;
+  int g_lo, g_hi;  // this workgroup's query heads of the group
+  head_share(G, ns, split, g_lo, g_hi);
+  g_lo = __builtin_amdgcn_readfirstlane(g_lo);
+  g_hi = __builtin_amdgcn_readfirstlane(g_hi);
+  const int nsteps = ntiles * (g_hi - g_lo);
 
   // This wave's operand (K for A, V for B) as B operands: lane (n, h) holds row my_k, d = 16t + 8h .. +7
   bf16x8 xf[KS];
@@ -240,8 +267,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   // no integer division in the loop.
   auto advance = [&](int& g, int& ti) {
     ++g;
-    if (g == G) {
-      g = 0;
+    if (g == g_hi) {
+      g = g_lo;
       --ti;
     }
   };
@@ -281,7 +308,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
   const float c = p.scale_log2e;
 
-  int nx_g = 0, nx_ti = tile_end - 1;  // head and query tile of the next step to load
+  int nx_g = g_lo, nx_ti = tile_end - 1;  // head and query tile of the next step to load
   if (nsteps > 0) {
     issue_step(nx_g, nx_ti, std::integral_constant<int, 0>{});
     advance(nx_g, nx_ti);
@@ -341,7 +368,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
     }
   };
   if (role == 0) {
-    int cur_g = 0, cur_ti = tile_end - 1;
+    int cur_g = g_lo, cur_ti = tile_end - 1;
     auto body_a = [&](int step, auto r_c) {
       constexpr int r = decltype(r_c)::value;
       prefetch(step, r_c);
@@ -461,17 +488,53 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   }
 
   if (k_ok) {
-    __bf16* dst = (role == 0 ? p.dv : p.dk) + ((size_t)b * p.seqlen + my_k) * kv_stride + hk * D;
     const float mul = role == 0 ? 1.0f : p.scale;
+    const size_t row = ((size_t)b * p.seqlen + my_k) * kv_stride + hk * D;
+    if (ns == 1) {
+      __bf16* dst = (role == 0 ? p.dv : p.dk) + row;
 #pragma unroll
-    for (int d = 0; d < DB; ++d)
+      for (int d = 0; d < DB; ++d)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 w;
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[d][4 * g + e] * mul);
-        *reinterpret_cast<bf16x4*>(dst + 32 * d + 8 * g + 4 * h) = w;
-      }
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[d][4 * g + e] * mul);
+          *reinterpret_cast<bf16x4*>(dst + 32 * d + 8 * g + 4 * h) = w;
+        }
+    } else {
+      // fp32 partial of this share of the heads: part[dK | dV][split][b][s][hk][d]
+      const size_t plane = (size_t)p.batch * p.seqlen * kv_stride;
+      float* dst = p.part + (size_t)(role == 0 ? 1 : 0) * ns * plane + (size_t)split * plane + row;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = acc[d][4 * g + e] * mul;
+          *reinterpret_cast<f32x4*>(dst + 32 * d + 8 * g + 4 * h) = w;
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV = sum of the head-share partials, rounded to bf16 (head_split > 1)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_reduce_kernel(BwdParams p) {
+  const size_t plane = (size_t)p.batch * p.seqlen * p.hkv * p.head_dim;
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= plane) return;
+  const int ns = p.head_split;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {  // 0: dK, 1: dV
+    const float* src = p.part + (size_t)t * ns * plane + i;
+    f32x4 sum = *reinterpret_cast<const f32x4*>(src);
+    for (int sp = 1; sp < ns; ++sp) sum += *reinterpret_cast<const f32x4*>(src + (size_t)sp * plane);
+    bf16x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = (__bf16)sum[e];
+    *reinterpret_cast<bf16x4*>((t == 0 ? p.dk : p.dv) + i) = w;
   }
 }
 
@@ -500,7 +563,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   const int b = bh / p.hq;
   const int hq = bh - b * p.hq;
   const int hk = hq / (p.hq / p.hkv);
-  const int qblk = (int)min((unsigned)p.order[p.num_blk + blockIdx.y], (unsigned)(p.num_blk - 1));
+  const int qblk = (int)min((unsigned)p.order[p.num_blk * p.head_split + blockIdx.y], (unsigned)(p.num_blk - 1));
   const int my_q = qblk * 128 + wave * 32 + n;
   const bool q_ok = my_q < p.seqlen;
   const int q_stride = p.hq * D;
@@ -687,17 +750,23 @@ hipError_t launch_bwd(const BwdParams& p_in, unsigned phases, hipStream_t stream
     constexpr int RPB = 256 / (D / 8);
     const long nrows = (long)q.batch * q.hq * q.stat_stride;
     const long nstat = (nrows + RPB - 1) / RPB;
-    const long norder = 2L * ((q.num_blk + 255) / 256);
+    const long norder = (q.num_blk * (long)q.head_split + 255) / 256 + (q.num_blk + 255) / 256;
     dim3 grid((unsigned)(nstat + norder));
     hipLaunchKernelGGL((attn_bwd_delta_kernel<D, CAUSAL>), grid, dim3(256), 0, stream, q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (phases & kBwdDkDv) {
-    dim3 grid(q.batch * q.hkv, q.num_blk);
+    dim3 grid(q.batch * q.hkv, q.num_blk * q.head_split);
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL>), grid, dim3(512), 0, stream, q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (q.head_split > 1) {
+      const size_t quads = (size_t)q.batch * q.seqlen * q.hkv * D / 4;
+      hipLaunchKernelGGL(attn_bwd_dkdv_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, stream, q);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   if (phases & kBwdDq) {
     dim3 grid(q.batch * q.hq, q.num_blk);

@@ -52,7 +52,9 @@ struct BwdParams {
   float* delta;  // workspace [B, Hq, stat_stride]: Delta_i = dO_i . O_i
   float* lse2;   // workspace [B, Hq, stat_stride]: LSE_i * log2(e)
   int stat_stride;  // seqlen rounded up to kStatAlign; the padding holds zeros
-  int* order;       // workspace [2, num_blk]: block order of the dK/dV pass, then of the dQ pass
+  int* order;       // workspace: dK/dV work order [num_blk * head_split], then dQ block order [num_blk]
+  float* part;      // workspace [2][head_split][B][S][Hkv][D] fp32 partial dK, dV (head_split > 1 only)
+  int head_split;   // query heads of a GQA group split over this many dK/dV workgroups
   const int32_t* cu_seqlens;
   int num_seqs;
   int batch, hq, hkv, seqlen, head_dim;
@@ -65,6 +67,36 @@ struct BwdParams {
 // Row length of the backward's per-row statistics in the workspace.
 constexpr int kStatAlign = 64;
 inline int stat_stride_for(int seqlen) { return (seqlen + kStatAlign - 1) / kStatAlign * kStatAlign; }
+
+// dK/dV work split. The pass runs one workgroup of 8 waves per CU and per
+// (b, kv head, 128-key block); with few kv heads and short sequences that is
+// too few workgroups to fill the CUs and balance the causal costs. The G
+// query heads of a group are then split over up to G workgroups, which write
+// fp32 partial sums that a small kernel adds up.
+constexpr long kDkdvTargetBlocks = 1024;  // about four workgroups per CU
+inline int bwd_head_split(int batch, int hq, int hkv, int seqlen) {
+  const long units = (long)batch * hkv * ((seqlen + 127) / 128);
+  const int g = hq / hkv;
+  if (units >= kDkdvTargetBlocks) return 1;
+  const long want = (kDkdvTargetBlocks + units - 1) / units;
+  return (int)(want < g ? want : g);
+}
+// Workspace layout, in bytes from its start: Delta and LSE*log2(e) (fp32
+// [B, Hq, S64] each), the work order (int32, NB * split + NB with
+// NB = ceil(S / 128)), then, 256-byte aligned, the fp32 partials.
+inline size_t bwd_order_offset(int batch, int hq, int seqlen) {
+  return (size_t)8 * batch * hq * stat_stride_for(seqlen);
+}
+inline size_t bwd_part_offset(int batch, int hq, int hkv, int seqlen) {
+  const size_t nblk = ((size_t)seqlen + 127) / 128;
+  const size_t end = bwd_order_offset(batch, hq, seqlen) + 4 * nblk * (bwd_head_split(batch, hq, hkv, seqlen) + 1);
+  return (end + 255) / 256 * 256;
+}
+inline size_t bwd_workspace_size(int batch, int hq, int hkv, int seqlen, int head_dim) {
+  const int ns = bwd_head_split(batch, hq, hkv, seqlen);
+  const size_t part = ns > 1 ? (size_t)8 * ns * batch * seqlen * hkv * head_dim : 0;
+  return bwd_part_offset(batch, hq, hkv, seqlen) + part;
+}
 
 struct MergeParams {
   float* o_acc;            // [B, S, H, D] fp32, read if accumulate, written

@@ -40,15 +40,39 @@ def test_status_strings():
     assert lib.attn_last_hip_error() == 0
 
 
+def _split(B, Hq, Hkv, S):
+    units = B * Hkv * (-(-S // 128))
+    return 1 if units >= 1024 else min(Hq // Hkv, -(-1024 // units))
+
+
+def _ws(B, Hq, Hkv, S, D):
+    """Layout stated in include/attn.h: Delta + LSE*log2e, work order, then 256-byte aligned partials."""
+    s64 = -(-S // 64) * 64
+    nblk = -(-S // 128)
+    ns = _split(B, Hq, Hkv, S)
+    end = 8 * B * Hq * s64 + 4 * nblk * (ns + 1)
+    end = -(-end // 256) * 256
+    return end + (8 * ns * B * S * Hkv * D if ns > 1 else 0)
+
+
 def test_workspace_bytes():
     lib = lca.load_library()
-    # two fp32 arrays [B, Hq, S rounded up to 64], two int32 arrays [ceil(S / 128)]
-    assert lib.attn_bwd_workspace_bytes(1, 28, 32768) == 8 * 28 * 32768 + 8 * 256
-    assert lib.attn_bwd_workspace_bytes(2, 3, 5) == 8 * 2 * 3 * 64 + 8
-    assert lib.attn_bwd_workspace_bytes(1, 1, 65) == 8 * 128 + 8
-    assert lib.attn_bwd_workspace_bytes(1, 1, 129) == 8 * 192 + 16
-    assert lib.attn_bwd_workspace_bytes(0, 3, 5) == 0
-    assert lib.attn_bwd_workspace_bytes(1, -1, 5) == 0
+    # gqa32k: enough dK/dV workgroups, no head split
+    assert _split(1, 28, 4, 32768) == 1
+    assert lib.attn_bwd_workspace_bytes(1, 28, 4, 32768, 128) == 8 * 28 * 32768 + 8 * 256
+    # packed32k share: 512 key-block units, the 7 heads of a group split in 2
+    assert _split(1, 14, 2, 32768) == 2
+    assert lib.attn_bwd_workspace_bytes(1, 14, 2, 32768, 128) == _ws(1, 14, 2, 32768, 128)
+    assert lib.attn_bwd_workspace_bytes(1, 14, 2, 32768, 128) > 8 * 2 * 32768 * 2 * 128
+    # short sequences: split up to the group size
+    assert _split(2, 3, 1, 5) == 3
+    for args in [(2, 3, 1, 5, 64), (1, 1, 1, 65, 128), (1, 1, 1, 129, 64), (1, 8, 1, 65536, 128),
+                 (3, 12, 4, 1000, 64), (1, 7, 1, 32768, 128)]:
+        assert lib.attn_bwd_workspace_bytes(*args) == _ws(*args), args
+    assert lib.attn_bwd_workspace_bytes(0, 3, 1, 5, 64) == 0
+    assert lib.attn_bwd_workspace_bytes(1, -1, 1, 5, 64) == 0
+    assert lib.attn_bwd_workspace_bytes(1, 6, 4, 5, 64) == 0
+    assert lib.attn_bwd_workspace_bytes(1, 4, 2, 5, 0) == 0
 
 
 # fake, 16-byte aligned, never dereferenced: every case below must fail validation first

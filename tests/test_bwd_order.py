@@ -22,6 +22,11 @@ def _segment(cu, i):
     return int(cu[s]), int(cu[s + 1])
 
 
+def _split(B, Hq, Hkv, S):
+    units = B * Hkv * (-(-S // 128))
+    return 1 if units >= 1024 else min(Hq // Hkv, -(-1024 // units))
+
+
 def _cost(cu, S, causal, pass_, blk):
     first, last = blk * 128, min(blk * 128 + 128, S) - 1
     if pass_ == 0:  # keys first..last: the union of the queries they see
@@ -49,20 +54,27 @@ def test_block_order(S, causal, lengths):
     import torch
     import long_context_exact_fwd_amd as lca
     print(f"order S={S} causal={causal} lengths={lengths}", flush=True)
-    B, Hq, Hkv, D = 1, 2, 1, 128
+    B, Hq, Hkv, D = 1, 8, 1, 128
     z = torch.zeros((B, S, Hq, D), dtype=torch.bfloat16, device="cuda")
     kv = torch.zeros((B, S, Hkv, D), dtype=torch.bfloat16, device="cuda")
     lse = torch.zeros((B, Hq, S), dtype=torch.float32, device="cuda")
     cu_h = si.cu_seqlens_from_lengths(lengths) if lengths else np.array([0, S], dtype=np.int32)
     cu = dev_i32(cu_h) if lengths else None
-    nbytes = lca.bwd_workspace_bytes(B, Hq, S)
+    nbytes = lca.bwd_workspace_bytes(B, Hq, Hkv, S, D)
     ws = torch.full((nbytes // 4,), -7, dtype=torch.int32, device="cuda")
     lca.bwd(z, kv, kv, z, lse, z, causal=causal, cu_seqlens=cu, workspace=ws, phases=lca.BWD_DELTA)
     torch.cuda.synchronize()
     nblk = -(-S // 128)
-    order = ws[-2 * nblk:].cpu().numpy().reshape(2, nblk)
-    for pass_ in (0, 1):
-        got = order[pass_]
-        assert sorted(got.tolist()) == list(range(nblk)), f"pass {pass_}: not a permutation"
-        keys = [(-_cost(cu_h, S, causal, pass_, int(b)), int(b)) for b in got]
+    ns = _split(B, Hq, Hkv, S)
+    G = Hq // Hkv
+    off = 2 * B * Hq * (-(-S // 64) * 64)  # int32 words before the order
+    order = ws[off:off + nblk * (ns + 1)].cpu().numpy()
+    # dK/dV entries e = key block * ns + share of the group's heads; cost = tiles * heads in the share
+    heads = [(s_ + 1) * G // ns - s_ * G // ns for s_ in range(ns)]
+    for pass_, got, n in ((0, order[:nblk * ns], nblk * ns), (1, order[nblk * ns:], nblk)):
+        assert sorted(got.tolist()) == list(range(n)), f"pass {pass_}: not a permutation"
+        if pass_ == 0:
+            keys = [(-_cost(cu_h, S, causal, 0, int(e) // ns) * heads[int(e) % ns], int(e)) for e in got]
+        else:
+            keys = [(-_cost(cu_h, S, causal, 1, int(e)), int(e)) for e in got]
         assert keys == sorted(keys), f"pass {pass_}: not heaviest first"

@@ -64,7 +64,8 @@ def _run_fwd_bwd(name, backward):
     if backward:
         do = lca.bf16_from_bits(x.do_bits, "cuda")
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        ws = torch.empty(lca.bwd_workspace_bytes(w.batch, w.hq, w.seqlen) // 4, dtype=torch.float32, device="cuda")
+        ws = torch.empty(lca.bwd_workspace_bytes(w.batch, w.hq, w.hkv, w.seqlen, w.head_dim) // 4,
+                         dtype=torch.float32, device="cuda")
         for ph in (lca.BWD_DELTA, lca.BWD_DKDV, lca.BWD_DQ):  # as bench.py launches them
             lca.bwd(q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, phases=ph, **kw)
     torch.cuda.synchronize()
