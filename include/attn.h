@@ -102,11 +102,13 @@ attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
  * order: two fp32 per-row arrays [batch, hq, S64] (S64 = seqlen rounded up to
  * a multiple of 64): Delta_i = dO_i . O_i and LSE_i * log2(e), the padding
  * rows written as zeros; the int32 work order of the dK/dV and dQ kernels
- * (NB * (split + 1) entries, NB = ceil(seqlen / 128)); and, when the dK/dV
- * pass splits the query heads of a GQA group over `split` > 1 workgroups
- * (chosen from the sizes, for grids too small to fill the GPU), 256-byte
- * aligned fp32 partial dK and dV of 8 * split * batch * seqlen * hkv *
- * head_dim bytes. Returns 0 for non-positive sizes or hq % hkv != 0. */
+ * (NB * (hsplit + ksplit) entries, NB = ceil(seqlen / 128)); then, each
+ * 256-byte aligned, fp32 partial dK and dV (8 * hsplit * batch * seqlen * hkv
+ * * head_dim bytes) when the dK/dV pass splits a GQA group's query heads over
+ * hsplit > 1 workgroups, and fp32 partial dQ (4 * ksplit * batch * seqlen *
+ * hq * head_dim bytes) when the dQ pass splits a query block's key tiles over
+ * ksplit > 1 workgroups. Both splits are chosen from the sizes, for grids too
+ * small to fill the GPU. Returns 0 for non-positive sizes or hq % hkv != 0. */
 size_t attn_bwd_workspace_bytes(int batch, int hq, int hkv, int seqlen, int head_dim);
 
 /* Backward: dq, dk, dv from q, k, v, the forward's o and lse, and dout.

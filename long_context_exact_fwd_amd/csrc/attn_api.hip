@@ -153,10 +153,15 @@ attn_status attn_bwd_phases(unsigned phases, const void* q, const void* k, const
   p.lse2 = p.delta + (size_t)batch * hq * p.stat_stride;
   p.order = reinterpret_cast<int*>(static_cast<char*>(workspace) + mi355attn::bwd_order_offset(batch, hq, seqlen));
   p.head_split = mi355attn::bwd_head_split(batch, hq, hkv, seqlen);
+  p.key_split = mi355attn::bwd_key_split(batch, hq, seqlen);
   p.part = p.head_split > 1
                ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                           mi355attn::bwd_part_offset(batch, hq, hkv, seqlen))
                : nullptr;
+  p.dq_part = p.key_split > 1
+                  ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             mi355attn::bwd_dq_part_offset(batch, hq, hkv, seqlen, head_dim))
+                  : nullptr;
   p.cu_seqlens = cu_seqlens;
   p.num_seqs = num_seqs;
   p.batch = batch;

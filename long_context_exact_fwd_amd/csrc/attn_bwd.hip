@@ -55,20 +55,26 @@ __device__ int block_tiles(const BwdParams& p, int pass, int blk) {
   return (hi + 63) / 64 - lo / 64;
 }
 
-// Query heads [g0, g1) of a group of G handled by share `split` of `ns`.
-__device__ __forceinline__ void head_share(int G, int ns, int split, int& g0, int& g1) {
-  g0 = split * G / ns;
-  g1 = (split + 1) * G / ns;
+// Items [lo, hi) of n handled by share `split` of `ns` (query heads of a
+// group in the dK/dV pass, key tiles of a query block in the dQ pass).
+__device__ __forceinline__ void share_range(int n, int ns, int split, int& lo, int& hi) {
+  lo = split * n / ns;
+  hi = (split + 1) * n / ns;
 }
 
-// Entry e of a pass: dK/dV (pass 0) e = key block * head_split + share; dQ (pass 1) e = query block.
+// Entry e of a pass: dK/dV (pass 0) e = key block * head_split + share of the
+// heads; dQ (pass 1) e = query block * key_split + share of the key tiles.
 template <bool CAUSAL>
 __device__ int entry_cost(const BwdParams& p, int pass, int e) {
-  if (pass == 1) return block_tiles<CAUSAL>(p, 1, e);
+  int lo, hi;
+  if (pass == 1) {
+    const int ns = p.key_split;
+    share_range(block_tiles<CAUSAL>(p, 1, e / ns), ns, e % ns, lo, hi);
+    return hi - lo;
+  }
   const int ns = p.head_split;
-  int g0, g1;
-  head_share(p.hq / p.hkv, ns, e % ns, g0, g1);
-  return block_tiles<CAUSAL>(p, 0, e / ns) * (g1 - g0);
+  share_range(p.hq / p.hkv, ns, e % ns, lo, hi);
+  return block_tiles<CAUSAL>(p, 0, e / ns) * (hi - lo);
 }
 
 // Rank of each entry by descending cost, ties by index; order[rank] = entry.
@@ -76,7 +82,7 @@ __device__ int entry_cost(const BwdParams& p, int pass, int e) {
 template <bool CAUSAL>
 __device__ void block_order(const BwdParams& p, int wg) {
   __shared__ int cost[256];
-  const int n0 = p.num_blk * p.head_split, n1 = p.num_blk;
+  const int n0 = p.num_blk * p.head_split, n1 = p.num_blk * p.key_split;
   const int c0 = (n0 + 255) / 256;
   const int pass = wg < c0 ? 0 : 1;
   const int n = pass == 0 ? n0 : n1;
@@ -99,8 +105,8 @@ __device__ void block_order(const BwdParams& p, int wg) {
 
 // ---------------------------------------------------------------------------
 // Delta_i = dO_i . O_i and LSE_i * log2(e), both fp32 [B, Hq, S]; the last
-// ceil(num_blk * head_split / 256) + ceil(num_blk / 256) workgroups write the
-// work order instead.
+// ceil(num_blk * head_split / 256) + ceil(num_blk * key_split / 256)
+// workgroups write the work order instead.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
@@ -222,7 +228,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   const int tile_end = wg_hi > wg_lo ? (wg_hi + kQT - 1) / kQT : 0;
   const int ntiles = tile_end - tile_begin;
   int g_lo, g_hi;  // this workgroup's query heads of the group
-  head_share(G, ns, split, g_lo, g_hi);
+  share_range(G, ns, split, g_lo, g_hi);
   g_lo = __builtin_amdgcn_readfirstlane(g_lo);
   g_hi = __builtin_amdgcn_readfirstlane(g_hi);
   const int nsteps = ntiles * (g_hi - g_lo);
@@ -563,7 +569,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   const int b = bh / p.hq;
   const int hq = bh - b * p.hq;
   const int hk = hq / (p.hq / p.hkv);
-  const int qblk = (int)min((unsigned)p.order[p.num_blk * p.head_split + blockIdx.y], (unsigned)(p.num_blk - 1));
+  const int nks = p.key_split;
+  const int qentry =
+      (int)min((unsigned)p.order[p.num_blk * p.head_split + blockIdx.y], (unsigned)(p.num_blk * nks - 1));
+  const int qblk = __builtin_amdgcn_readfirstlane(qentry / nks);
+  const int ksplit = __builtin_amdgcn_readfirstlane(qentry - qblk * nks);
   const int my_q = qblk * 128 + wave * 32 + n;
   const bool q_ok = my_q < p.seqlen;
   const int q_stride = p.hq * D;
@@ -595,8 +605,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   }
   wg_lo = __builtin_amdgcn_readfirstlane(wg_lo);
   wg_hi = __builtin_amdgcn_readfirstlane(wg_hi);
-  const int tile_begin = wg_hi > wg_lo ? wg_lo / kKT : 0;
-  const int tile_end = wg_hi > wg_lo ? (wg_hi + kKT - 1) / kKT : 0;
+  // this workgroup's share of the block's visible key tiles
+  int tile_begin = wg_hi > wg_lo ? wg_lo / kKT : 0;
+  int tile_end = wg_hi > wg_lo ? (wg_hi + kKT - 1) / kKT : 0;
+  {
+    int lo, hi;
+    share_range(tile_end - tile_begin, nks, ksplit, lo, hi);
+    tile_end = __builtin_amdgcn_readfirstlane(tile_begin + hi);
+    tile_begin = __builtin_amdgcn_readfirstlane(tile_begin + lo);
+  }
 
   bf16x8 qf[KS], gf[KS];
   {
@@ -729,17 +746,48 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   }
 
   if (q_ok) {
-    __bf16* row = p.dq + ((size_t)b * p.seqlen + my_q) * q_stride + hq * D;
+    const size_t roff = ((size_t)b * p.seqlen + my_q) * q_stride + hq * D;
+    if (nks == 1) {
+      __bf16* row = p.dq + roff;
 #pragma unroll
-    for (int d = 0; d < DB; ++d)
+      for (int d = 0; d < DB; ++d)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 w;
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[d][4 * g + e] * p.scale);
-        *reinterpret_cast<bf16x4*>(row + 32 * d + 8 * g + 4 * h) = w;
-      }
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[d][4 * g + e] * p.scale);
+          *reinterpret_cast<bf16x4*>(row + 32 * d + 8 * g + 4 * h) = w;
+        }
+    } else {
+      // fp32 partial of this share of the key tiles: dq_part[split][b][s][hq][d]
+      float* row = p.dq_part + (size_t)ksplit * p.batch * p.seqlen * q_stride + roff;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = acc[d][4 * g + e] * p.scale;
+          *reinterpret_cast<f32x4*>(row + 32 * d + 8 * g + 4 * h) = w;
+        }
+    }
   }
+}
+
+// ---------------------------------------------------------------------------
+// dQ = sum of the key-share partials, rounded to bf16 (key_split > 1)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void attn_bwd_dq_reduce_kernel(BwdParams p) {
+  const size_t plane = (size_t)p.batch * p.seqlen * p.hq * p.head_dim;
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= plane) return;
+  const float* src = p.dq_part + i;
+  f32x4 sum = *reinterpret_cast<const f32x4*>(src);
+  for (int sp = 1; sp < p.key_split; ++sp) sum += *reinterpret_cast<const f32x4*>(src + (size_t)sp * plane);
+  bf16x4 w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = (__bf16)sum[e];
+  *reinterpret_cast<bf16x4*>(p.dq + i) = w;
 }
 
 template <int D, bool CAUSAL>
@@ -750,7 +798,7 @@ hipError_t launch_bwd(const BwdParams& p_in, unsigned phases, hipStream_t stream
     constexpr int RPB = 256 / (D / 8);
     const long nrows = (long)q.batch * q.hq * q.stat_stride;
     const long nstat = (nrows + RPB - 1) / RPB;
-    const long norder = (q.num_blk * (long)q.head_split + 255) / 256 + (q.num_blk + 255) / 256;
+    const long norder = (q.num_blk * (long)q.head_split + 255) / 256 + (q.num_blk * (long)q.key_split + 255) / 256;
     dim3 grid((unsigned)(nstat + norder));
     hipLaunchKernelGGL((attn_bwd_delta_kernel<D, CAUSAL>), grid, dim3(256), 0, stream, q);
     hipError_t e = hipGetLastError();
@@ -769,10 +817,16 @@ hipError_t launch_bwd(const BwdParams& p_in, unsigned phases, hipStream_t stream
     }
   }
   if (phases & kBwdDq) {
-    dim3 grid(q.batch * q.hq, q.num_blk);
+    dim3 grid(q.batch * q.hq, q.num_blk * q.key_split);
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), grid, dim3(256), 0, stream, q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (q.key_split > 1) {
+      const size_t quads = (size_t)q.batch * q.seqlen * q.hq * D / 4;
+      hipLaunchKernelGGL(attn_bwd_dq_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, stream, q);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }

@@ -52,9 +52,11 @@ struct BwdParams {
   float* delta;  // workspace [B, Hq, stat_stride]: Delta_i = dO_i . O_i
   float* lse2;   // workspace [B, Hq, stat_stride]: LSE_i * log2(e)
   int stat_stride;  // seqlen rounded up to kStatAlign; the padding holds zeros
-  int* order;       // workspace: dK/dV work order [num_blk * head_split], then dQ block order [num_blk]
+  int* order;       // workspace: dK/dV work order [num_blk * head_split], then dQ's [num_blk * key_split]
   float* part;      // workspace [2][head_split][B][S][Hkv][D] fp32 partial dK, dV (head_split > 1 only)
+  float* dq_part;   // workspace [key_split][B][S][Hq][D] fp32 partial dQ (key_split > 1 only)
   int head_split;   // query heads of a GQA group split over this many dK/dV workgroups
+  int key_split;    // visible key tiles of a query block split over this many dQ workgroups
   const int32_t* cu_seqlens;
   int num_seqs;
   int batch, hq, hkv, seqlen, head_dim;
@@ -81,21 +83,38 @@ inline int bwd_head_split(int batch, int hq, int hkv, int seqlen) {
   const long want = (kDkdvTargetBlocks + units - 1) / units;
   return (int)(want < g ? want : g);
 }
+// dQ work split, for the same reason: the dQ pass runs two 4-wave
+// workgroups per CU and per (b, query head, 128-query block); below about
+// 1024 of them the visible key tiles of each block are split over up to 4
+// workgroups, which write fp32 partial dQ.
+inline int bwd_key_split(int batch, int hq, int seqlen) {
+  const long units = (long)batch * hq * ((seqlen + 127) / 128);
+  if (units >= kDkdvTargetBlocks) return 1;
+  const long want = (kDkdvTargetBlocks + units - 1) / units;
+  return (int)(want < 4 ? want : 4);
+}
 // Workspace layout, in bytes from its start: Delta and LSE*log2(e) (fp32
-// [B, Hq, S64] each), the work order (int32, NB * split + NB with
-// NB = ceil(S / 128)), then, 256-byte aligned, the fp32 partials.
+// [B, Hq, S64] each), the work order (int32, NB * (head split + key split)
+// with NB = ceil(S / 128)), then, each 256-byte aligned, the fp32 partial
+// dK/dV and the fp32 partial dQ when their splits are above 1.
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 inline size_t bwd_order_offset(int batch, int hq, int seqlen) {
   return (size_t)8 * batch * hq * stat_stride_for(seqlen);
 }
 inline size_t bwd_part_offset(int batch, int hq, int hkv, int seqlen) {
   const size_t nblk = ((size_t)seqlen + 127) / 128;
-  const size_t end = bwd_order_offset(batch, hq, seqlen) + 4 * nblk * (bwd_head_split(batch, hq, hkv, seqlen) + 1);
-  return (end + 255) / 256 * 256;
+  const size_t entries = nblk * (bwd_head_split(batch, hq, hkv, seqlen) + bwd_key_split(batch, hq, seqlen));
+  return align256(bwd_order_offset(batch, hq, seqlen) + 4 * entries);
 }
-inline size_t bwd_workspace_size(int batch, int hq, int hkv, int seqlen, int head_dim) {
+inline size_t bwd_dq_part_offset(int batch, int hq, int hkv, int seqlen, int head_dim) {
   const int ns = bwd_head_split(batch, hq, hkv, seqlen);
   const size_t part = ns > 1 ? (size_t)8 * ns * batch * seqlen * hkv * head_dim : 0;
-  return bwd_part_offset(batch, hq, hkv, seqlen) + part;
+  return align256(bwd_part_offset(batch, hq, hkv, seqlen) + part);
+}
+inline size_t bwd_workspace_size(int batch, int hq, int hkv, int seqlen, int head_dim) {
+  const int nk = bwd_key_split(batch, hq, seqlen);
+  const size_t part = nk > 1 ? (size_t)4 * nk * batch * seqlen * hq * head_dim : 0;
+  return bwd_dq_part_offset(batch, hq, hkv, seqlen, head_dim) + part;
 }
 
 struct MergeParams {

@@ -45,27 +45,33 @@ def _split(B, Hq, Hkv, S):
     return 1 if units >= 1024 else min(Hq // Hkv, -(-1024 // units))
 
 
+def _ksplit(B, Hq, S):
+    units = B * Hq * (-(-S // 128))
+    return 1 if units >= 1024 else min(4, -(-1024 // units))
+
+
 def _ws(B, Hq, Hkv, S, D):
-    """Layout stated in include/attn.h: Delta + LSE*log2e, work order, then 256-byte aligned partials."""
+    """Layout stated in include/attn.h: Delta + LSE*log2e, work order, partial dK/dV, partial dQ."""
+    a256 = lambda x: -(-x // 256) * 256
     s64 = -(-S // 64) * 64
     nblk = -(-S // 128)
-    ns = _split(B, Hq, Hkv, S)
-    end = 8 * B * Hq * s64 + 4 * nblk * (ns + 1)
-    end = -(-end // 256) * 256
-    return end + (8 * ns * B * S * Hkv * D if ns > 1 else 0)
+    ns, nk = _split(B, Hq, Hkv, S), _ksplit(B, Hq, S)
+    end = a256(8 * B * Hq * s64 + 4 * nblk * (ns + nk))
+    end = a256(end + (8 * ns * B * S * Hkv * D if ns > 1 else 0))
+    return end + (4 * nk * B * S * Hq * D if nk > 1 else 0)
 
 
 def test_workspace_bytes():
     lib = lca.load_library()
-    # gqa32k: enough dK/dV workgroups, no head split
-    assert _split(1, 28, 4, 32768) == 1
+    # gqa32k: enough dK/dV and dQ workgroups, no split
+    assert _split(1, 28, 4, 32768) == 1 and _ksplit(1, 28, 32768) == 1
     assert lib.attn_bwd_workspace_bytes(1, 28, 4, 32768, 128) == 8 * 28 * 32768 + 8 * 256
     # packed32k share: 512 key-block units, the 7 heads of a group split in 2
     assert _split(1, 14, 2, 32768) == 2
     assert lib.attn_bwd_workspace_bytes(1, 14, 2, 32768, 128) == _ws(1, 14, 2, 32768, 128)
     assert lib.attn_bwd_workspace_bytes(1, 14, 2, 32768, 128) > 8 * 2 * 32768 * 2 * 128
-    # short sequences: split up to the group size
-    assert _split(2, 3, 1, 5) == 3
+    # short sequences: split up to the group size (dK/dV) and up to 4 (dQ)
+    assert _split(2, 3, 1, 5) == 3 and _ksplit(2, 3, 5) == 4
     for args in [(2, 3, 1, 5, 64), (1, 1, 1, 65, 128), (1, 1, 1, 129, 64), (1, 8, 1, 65536, 128),
                  (3, 12, 4, 1000, 64), (1, 7, 1, 32768, 128)]:
         assert lib.attn_bwd_workspace_bytes(*args) == _ws(*args), args

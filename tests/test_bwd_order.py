@@ -27,6 +27,11 @@ def _split(B, Hq, Hkv, S):
     return 1 if units >= 1024 else min(Hq // Hkv, -(-1024 // units))
 
 
+def _ksplit(B, Hq, S):
+    units = B * Hq * (-(-S // 128))
+    return 1 if units >= 1024 else min(4, -(-1024 // units))
+
+
 def _cost(cu, S, causal, pass_, blk):
     first, last = blk * 128, min(blk * 128 + 128, S) - 1
     if pass_ == 0:  # keys first..last: the union of the queries they see
@@ -65,16 +70,17 @@ def test_block_order(S, causal, lengths):
     lca.bwd(z, kv, kv, z, lse, z, causal=causal, cu_seqlens=cu, workspace=ws, phases=lca.BWD_DELTA)
     torch.cuda.synchronize()
     nblk = -(-S // 128)
-    ns = _split(B, Hq, Hkv, S)
+    ns, nk = _split(B, Hq, Hkv, S), _ksplit(B, Hq, S)
     G = Hq // Hkv
     off = 2 * B * Hq * (-(-S // 64) * 64)  # int32 words before the order
-    order = ws[off:off + nblk * (ns + 1)].cpu().numpy()
-    # dK/dV entries e = key block * ns + share of the group's heads; cost = tiles * heads in the share
-    heads = [(s_ + 1) * G // ns - s_ * G // ns for s_ in range(ns)]
-    for pass_, got, n in ((0, order[:nblk * ns], nblk * ns), (1, order[nblk * ns:], nblk)):
+    order = ws[off:off + nblk * (ns + nk)].cpu().numpy()
+    # dK/dV entries e = key block * ns + share of the group's heads; cost = tiles * heads in the share.
+    # dQ entries e = query block * nk + share of the block's key tiles; cost = tiles in the share.
+    share = lambda n, m, i: (i + 1) * n // m - i * n // m
+    for pass_, got, n in ((0, order[:nblk * ns], nblk * ns), (1, order[nblk * ns:], nblk * nk)):
         assert sorted(got.tolist()) == list(range(n)), f"pass {pass_}: not a permutation"
         if pass_ == 0:
-            keys = [(-_cost(cu_h, S, causal, 0, int(e) // ns) * heads[int(e) % ns], int(e)) for e in got]
+            keys = [(-_cost(cu_h, S, causal, 0, int(e) // ns) * share(G, ns, int(e) % ns), int(e)) for e in got]
         else:
-            keys = [(-_cost(cu_h, S, causal, 1, int(e)), int(e)) for e in got]
+            keys = [(-share(_cost(cu_h, S, causal, 1, int(e) // nk), nk, int(e) % nk), int(e)) for e in got]
         assert keys == sorted(keys), f"pass {pass_}: not heaviest first"
