@@ -59,6 +59,8 @@ KERNEL_SOURCES = {
     "attn_bwd_delta_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h"),
     "attn_fwd_fp8_kernel": ("attn_fwd_fp8.hip", "attn_device.h", "attn_internal.h"),
     "attn_merge_kernel": ("attn_merge.hip", "attn_device.h", "attn_internal.h"),
+    "attn_bwd_dkdv_reduce_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h"),
+    "attn_bwd_dq_reduce_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h"),
 }
 KERNEL_OF_PHASE = {"attn_fwd": "attn_fwd_bf16_kernel", "bwd_delta": "attn_bwd_delta_kernel",
                    "bwd_dkdv": "attn_bwd_dkdv_kernel", "bwd_dq": "attn_bwd_dq_kernel"}
