@@ -42,6 +42,10 @@
  *     return ATTN_ERR_UNSUPPORTED so the caller can fall back to a standard
  *     implementation. Automatic fallback when the fused kernel is unusable
  *     is described in the FlashAttention page's "实际怎么用" section.
+ *   - Size: seqlen * Hq * D must not exceed 2^31 - 1 (the kernels address one
+ *     batch slice with 32-bit row offsets and their tile copies with 32-bit
+ *     byte ranges); larger requests return ATTN_ERR_UNSUPPORTED. attn_merge
+ *     accepts up to 2^40 elements in total.
  *   - Ownership: the caller allocates and owns every buffer, including the
  *     backward workspace. The library allocates nothing and keeps no state
  *     besides its loaded code. It is safe to call from several host threads.
@@ -108,7 +112,8 @@ attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
  * hsplit > 1 workgroups, and fp32 partial dQ (4 * ksplit * batch * seqlen *
  * hq * head_dim bytes) when the dQ pass splits a query block's key tiles over
  * ksplit > 1 workgroups. Both splits are chosen from the sizes, for grids too
- * small to fill the GPU. Returns 0 for non-positive sizes or hq % hkv != 0. */
+ * small to fill the GPU. Returns 0 for non-positive sizes, hq % hkv != 0 or
+ * a request over the size limit above. */
 size_t attn_bwd_workspace_bytes(int batch, int hq, int hkv, int seqlen, int head_dim);
 
 /* Backward: dq, dk, dv from q, k, v, the forward's o and lse, and dout.

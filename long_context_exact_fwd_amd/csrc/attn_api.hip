@@ -61,6 +61,7 @@ int attn_last_hip_error(void) { return g_last_hip_error; }
 
 size_t attn_bwd_workspace_bytes(int batch, int hq, int hkv, int seqlen, int head_dim) {
   if (batch <= 0 || hq <= 0 || hkv <= 0 || seqlen <= 0 || head_dim <= 0 || hq % hkv != 0) return 0;
+  if ((long long)seqlen * hq * head_dim > (long long)INT32_MAX) return 0;
   return mi355attn::bwd_workspace_size(batch, hq, hkv, seqlen, head_dim);
 }
 

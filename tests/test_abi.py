@@ -168,3 +168,15 @@ def test_merge_invalid_arguments_rejected(kw):
 @pytest.mark.parametrize("D", [32, 80, 256])
 def test_merge_unsupported_head_dims(D):
     assert _merge(D=D) == lca.ATTN_ERR_UNSUPPORTED
+
+
+def test_oversized_requests_unsupported():
+    """seqlen * Hq * D beyond 2^31 - 1 is refused before any HIP call."""
+    big = dict(S=1 << 20, Hq=16, Hkv=4, D=128)  # 2^31 elements per batch slice
+    assert _fwd(**big) == lca.ATTN_ERR_UNSUPPORTED
+    assert _bwd(**big) == lca.ATTN_ERR_UNSUPPORTED
+    assert _fp8(**big) == lca.ATTN_ERR_UNSUPPORTED
+    lib = lca.load_library()
+    assert lib.attn_bwd_workspace_bytes(1, 16, 4, 1 << 20, 128) == 0
+    # merge: more than 2^40 elements in total
+    assert _merge(B=1 << 10, S=1 << 20, H=1 << 10, D=128) == lca.ATTN_ERR_UNSUPPORTED
