@@ -37,6 +37,7 @@ TOL_O_MAXABS = 1e-2
 TOL_O_REL = 5e-3
 TOL_LSE = 1e-3
 TOL_GRAD_REL = 1e-2
+TOL_ZERO_GRAD_ABS = 1e-3  # where the exact gradient is zero
 TOL_FP8_REL = 5e-2
 
 
@@ -71,9 +72,18 @@ def check_grads(pairs, tag=""):
     msgs = []
     ok = True
     for name, x, r in pairs:
-        e = rel_l2(x, r)
-        msgs.append(f"{name} relL2={e:.3e}")
-        ok = ok and np.all(np.isfinite(x)) and e <= TOL_GRAD_REL
+        if np.any(np.asarray(r) != 0):
+            e = rel_l2(x, r)
+            msgs.append(f"{name} relL2={e:.3e}")
+            ok = ok and np.all(np.isfinite(x)) and e <= TOL_GRAD_REL
+        else:
+            # exactly zero reference (e.g. dQ, dK when every row sees one key):
+            # the kernel's dP - Delta is a difference of two fp32 dot products
+            # of the same values summed in different orders, so it leaves
+            # rounding noise of about 1e-6 instead of exact zeros
+            e = max_abs(x, r)
+            msgs.append(f"{name} maxabs={e:.3e} (zero reference)")
+            ok = ok and np.all(np.isfinite(x)) and e <= TOL_ZERO_GRAD_ABS
     msg = tag + " " + " ".join(msgs)
     print(msg, flush=True)
     assert ok, msg

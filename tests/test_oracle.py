@@ -147,6 +147,19 @@ def test_single_token():
                                        atol=1e-14)
 
 
+def test_one_token_segments_backward():
+    # each row sees only its own key: P = 1, so dS = P (dP - Delta) = dO.V - dO.V = 0,
+    # dQ = dK = 0, and dV of a key is the sum of dO over the query heads of its group
+    S, D = 6, 5
+    q, k, v, do = _rand((1, S, 4, D), 40), _rand((1, S, 2, D), 41), _rand((1, S, 2, D), 42), _rand((1, S, 4, D), 43)
+    cu = cu_seqlens_from_lengths([1] * S)
+    for causal in (True, False):
+        dq, dk, dv = oracle.attention_bwd(q, k, v, do, causal=causal, scale=0.7, cu_seqlens=cu)
+        np.testing.assert_allclose(dq, 0.0, atol=1e-14)
+        np.testing.assert_allclose(dk, 0.0, atol=1e-14)
+        np.testing.assert_allclose(dv, do.reshape(1, S, 2, 2, D).sum(axis=3), atol=1e-14)
+
+
 def test_constant_values_give_that_row():
     S, D = 20, 6
     q, k = _rand((1, S, 2, D), 12, 3.0), _rand((1, S, 2, D), 13, 3.0)

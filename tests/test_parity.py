@@ -66,6 +66,9 @@ EDGE = [
     (1, 7, 1, 1000, 128, True, [100, 1, 1, 64, 65, 500, 269]),
     (1, 2, 2, 700, 128, False, [300, 400]),
     (1, 14, 2, 2048, 128, True, None),
+    (1, 2, 1, 64, 128, True, [1] * 64),           # every segment one token: O = V, LSE = scale q.k
+    (1, 3, 3, 80, 64, False, [1] * 80),
+    (1, 3, 3, 320, 64, False, [64, 64, 128, 64]),  # segments ending on tile boundaries
 ]
 
 
@@ -89,3 +92,21 @@ def test_peaky_scores_exercise_rescaling():
     doubled here; rel-L2, LSE and gradient bounds are unchanged.
     """
     _run_case(1, 4, 1, 1500, 128, True, seed=46, qk_std=3.0, abs_factor=2.0)
+
+
+def test_outputs_are_bitwise_deterministic():
+    """No atomics: two runs on the same inputs give identical bits, with and without the split passes."""
+    import torch
+    lca = _lib()
+    for (B, Hq, Hkv, S, D, causal) in [(1, 8, 1, 1000, 128, True), (1, 28, 4, 8192, 128, True)]:
+        print(f"case B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} causal={causal}", flush=True)
+        x = si.make_inputs(B, Hq, Hkv, S, D, 47, with_do=True)
+        q, k, v, do = dev_bf16(x.q_bits), dev_bf16(x.k_bits), dev_bf16(x.v_bits), dev_bf16(x.do_bits)
+        runs = []
+        for _ in range(2):
+            o, lse = lca.fwd(q, k, v, causal=causal)
+            dq, dk, dv = lca.bwd(q, k, v, o, lse, do, causal=causal)
+            torch.cuda.synchronize()
+            runs.append([t.clone() for t in (o, lse, dq, dk, dv)])
+        for a, b in zip(*runs):
+            assert torch.equal(a, b)
