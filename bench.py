@@ -301,7 +301,7 @@ def main(argv=None) -> int:
                     help="after the timed region, run one plain device copy of this many MiB (counter calibration)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
-        print(f"bench.py: only one GPU is supported by this build (got --gpus {a.gpus}); the kernels run one GPU's "
+        print(f"bench.py measures one GPU only (got --gpus {a.gpus}); the kernels run one GPU's "
               f"head share and no collectives are implemented", file=sys.stderr)
         return 2
 

@@ -71,7 +71,7 @@ typedef struct ihipStream_t* attn_stream_t; /* same object as hipStream_t */
 typedef enum attn_status {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARGUMENT = 1, /* inconsistent shape, flag or pointer; nothing enqueued */
-  ATTN_ERR_UNSUPPORTED = 2,      /* valid request this build has no kernel for; caller may fall back */
+  ATTN_ERR_UNSUPPORTED = 2,      /* valid request the library has no kernel for; caller may fall back */
   ATTN_ERR_HIP = 3               /* a kernel launch failed; see attn_last_hip_error() */
 } attn_status;
 
