@@ -31,6 +31,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -54,6 +55,7 @@ def _pairs(seqlen: int, causal: bool, cu=None) -> float:
 
 KERNEL_SOURCES = {
     "attn_fwd_bf16_kernel": ("attn_fwd.hip", "attn_device.h", "attn_internal.h"),
+    "attn_fwd_combine_kernel": ("attn_fwd.hip", "attn_device.h", "attn_internal.h"),
     "attn_bwd_dkdv_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h"),
     "attn_bwd_dq_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h"),
     "attn_bwd_delta_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h"),
@@ -160,6 +162,8 @@ def bf16_case(w, x, dev):
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
     kw = dict(causal=w.causal, cu_seqlens=cu, scale=w.scale)
+    nf = lca.fwd_workspace_bytes(B, Hq, w.hkv, S, w.head_dim)
+    fws = torch.empty((nf + 3) // 4, dtype=torch.float32, device=dev) if nf > 0 else None
     names = ["attn_fwd"]
     if w.backward:
         do = up(x.do_bits, dev)
@@ -170,7 +174,7 @@ def bf16_case(w, x, dev):
     def step(tm, i):
         if tm is not None:
             tm.mark(i, 0)
-        lca.fwd(q, k, v, out=o, lse=lse, **kw)
+        lca.fwd(q, k, v, out=o, lse=lse, workspace=fws, **kw)
         if tm is not None:
             tm.mark(i, 1)
         if w.backward:
@@ -218,6 +222,40 @@ def secondary(name, steps, warmup, dev):
         "tflops": round(tf, 2), "pct_of_peak": round(100.0 * tf / peak, 2), "peak_tflops": peak,
         "ms_per_step": round(ms, 4), "steps": steps, "phases_ms": {n: round(t, 4) for n, t in per.items()},
     }
+
+
+def key_split_case(steps, warmup, dev):
+    """Forward of a grid too small to fill the GPU (B=1, Hq=2, Hkv=1, S=32768, D=128, causal: 512
+    query-block units), with the key split chosen from the sizes and with it turned off."""
+    import torch
+    import seeded_inputs as si
+    import long_context_exact_fwd_amd as lca
+    B, Hq, Hkv, S, D, seed = 1, 2, 1, 32768, 128, 6
+    x = si.make_inputs(B, Hq, Hkv, S, D, seed, with_do=False)
+    up = lca.bf16_from_bits
+    q, k, v = up(x.q_bits, dev), up(x.k_bits, dev), up(x.v_bits, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    nf = lca.fwd_workspace_bytes(B, Hq, Hkv, S, D)
+    fws = torch.empty((nf + 3) // 4, dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    flops = 4.0 * D * _pairs(S, True) * B * Hq
+    out = {"config": f"B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} causal bf16 fwd, N(0,1) seed {seed}; "
+                     f"{B * Hq * (S // 128)} query-block units",
+           "workspace_bytes": nf}
+    for label, split in (("split", True), ("unsplit", False)):
+        def step(tm, i, split=split):
+            if tm is not None:
+                tm.mark(i, 0)
+            lca.fwd(q, k, v, causal=True, scale=scale, out=o, lse=lse, workspace=fws if split else None,
+                    split=split)
+            if tm is not None:
+                tm.mark(i, 1)
+        ms, _ = run_steps(step, ["attn_fwd"], steps, warmup)
+        tf = flops / (ms * 1e-3) / 1e12
+        out[label] = {"ms": round(ms, 4), "tflops": round(tf, 2), "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2)}
+    out["key_split"] = nf // (4 * B * Hq * S * (D + 1))  # workspace = ks partial O planes + ks row-stat planes
+    return out
 
 
 def ring_case(nchunk, steps, warmup, dev):
@@ -384,6 +422,8 @@ def main(argv=None) -> int:
         torch.cuda.empty_cache()
         result["workloads"]["ring4_gqa32k"] = ring_case(4, sec_steps, min(2, a.warmup), dev)
         print("bench: ring4_gqa32k done", file=sys.stderr, flush=True)
+        result["workloads"]["key_split_2h32k"] = key_split_case(sec_steps, min(2, a.warmup), dev)
+        print("bench: key_split_2h32k done", file=sys.stderr, flush=True)
     if not a.no_cpu_baseline:
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, x, a.cpu_sample_len)

@@ -47,7 +47,7 @@
  *     byte ranges); larger requests return ATTN_ERR_UNSUPPORTED. attn_merge
  *     accepts up to 2^40 elements in total.
  *   - Ownership: the caller allocates and owns every buffer, including the
- *     backward workspace. The library allocates nothing and keeps no state
+ *     forward and backward workspaces. The library allocates nothing and keeps no state
  *     besides its loaded code. It is safe to call from several host threads.
  *   - Asynchrony: each call only enqueues kernels on `stream` (0 = the null
  *     stream). Results are valid once the stream reaches that point.
@@ -75,12 +75,29 @@ typedef enum attn_status {
   ATTN_ERR_HIP = 3               /* a kernel launch failed; see attn_last_hip_error() */
 } attn_status;
 
+/* Bytes of device workspace attn_fwd can use for these sizes: 0 when the
+ * forward runs unsplit. The FA-3 paragraph of the FlashAttention page (section
+ * "那么FlashAttention-2 和 -3 又改进了什么") has the kernel pick its tiling from
+ * the sequence length; here the work split is picked from the sizes. With
+ * fewer than 1024 (batch, query head, 128-query block) units the key tiles of
+ * each block are split over ks = min(8, ceil(1024 / units), ceil(seqlen/64)/32)
+ * workgroups (ks > 1 needs 64 key tiles, seqlen > 4032). The workspace then holds fp32
+ * partial O [ks, B, S, Hq, D] and, 256-byte aligned after it, fp32 partial row
+ * statistics [ks, B, Hq, S]. Returns 0 for invalid sizes as well. */
+size_t attn_fwd_workspace_bytes(int batch, int hq, int hkv, int seqlen, int head_dim);
+
 /* Forward, bf16 in and out.
  * q [B,S,Hq,D], k and v [B,S,Hkv,D] bfloat16 (read only).
  * o [B,S,Hq,D] bfloat16 (written). lse [B,Hq,S] float32 (written).
+ * workspace: NULL, or 16-byte aligned device memory of at least
+ * attn_fwd_workspace_bytes() bytes. With NULL the forward always runs one
+ * workgroup per query block. With a workspace, sizes that
+ * attn_fwd_workspace_bytes() sizes above 0 run the key split: each share
+ * writes its partial output, and a second kernel combines the shares
+ * (O = sum of the shares' O weighted by 2^(their m + log2 l) over the total).
  * Rounding: O is accumulated in fp32 and rounded to bf16 (nearest-even).
  */
-attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
                      int batch, int hq, int hkv, int seqlen, int head_dim,
                      int causal, const int32_t* cu_seqlens, int num_seqs,
                      float scale, attn_stream_t stream);

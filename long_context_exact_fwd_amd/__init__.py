@@ -43,7 +43,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         raise ImportError(f"{p} is missing: build it with `python -m long_context_exact_fwd_amd.build`")
     lib = ctypes.CDLL(p)
     vp, i, f, st = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_void_p
-    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, f, st]
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, f, st]
     lib.attn_fwd.restype = i
     lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, f, st]
     lib.attn_fwd_fp8.restype = i
@@ -54,6 +54,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_bwd_phases.restype = i
     lib.attn_merge.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, st]
     lib.attn_merge.restype = i
+    lib.attn_fwd_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.attn_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_status_str.argtypes = [i]
@@ -65,8 +67,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     return lib
 
 
-EXPORTED = ("attn_fwd", "attn_fwd_fp8", "attn_bwd", "attn_bwd_phases", "attn_bwd_workspace_bytes",
-            "attn_merge", "attn_status_str", "attn_last_hip_error")
+EXPORTED = ("attn_fwd", "attn_fwd_workspace_bytes", "attn_fwd_fp8", "attn_bwd", "attn_bwd_phases",
+            "attn_bwd_workspace_bytes", "attn_merge", "attn_status_str", "attn_last_hip_error")
 
 BWD_DELTA, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 
@@ -120,8 +122,18 @@ def _check_tensors(*ts, dtype=None):
             raise ValueError(f"expected {dtype}, got {t.dtype}")
 
 
-def fwd(q, k, v, *, causal: bool, cu_seqlens=None, scale: Optional[float] = None, out=None, lse=None):
-    """Forward, bf16. Returns (o [B,S,Hq,D] bf16, lse [B,Hq,S] fp32)."""
+def fwd_workspace_bytes(batch: int, hq: int, hkv: int, seqlen: int, head_dim: int) -> int:
+    return int(load_library().attn_fwd_workspace_bytes(batch, hq, hkv, seqlen, head_dim))
+
+
+def fwd(q, k, v, *, causal: bool, cu_seqlens=None, scale: Optional[float] = None, out=None, lse=None,
+        workspace=None, split: bool = True):
+    """Forward, bf16. Returns (o [B,S,Hq,D] bf16, lse [B,Hq,S] fp32).
+
+    When attn_fwd_workspace_bytes() is above 0 for these sizes, a workspace is
+    allocated (or ``workspace`` is used) so the library can split key ranges;
+    ``split=False`` passes no workspace.
+    """
     import torch
     _check_tensors(q, k, v, dtype=torch.bfloat16)
     B, S, Hq, Hkv, D, n = _shape(q, k, cu_seqlens)
@@ -129,8 +141,18 @@ def fwd(q, k, v, *, causal: bool, cu_seqlens=None, scale: Optional[float] = None
         scale = 1.0 / math.sqrt(D)
     o = out if out is not None else torch.empty_like(q)
     l_ = lse if lse is not None else torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
-    st = load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l_), B, Hq, Hkv, S, D, int(bool(causal)),
-                                 _ptr(cu_seqlens), n, float(scale), _stream())
+    ws = None
+    nbytes = fwd_workspace_bytes(B, Hq, Hkv, S, D) if split else 0
+    if nbytes > 0:
+        if workspace is None:
+            ws = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=q.device)
+        elif workspace.is_contiguous() and workspace.numel() * workspace.element_size() >= nbytes \
+                and workspace.device == q.device:
+            ws = workspace
+        else:
+            raise ValueError(f"workspace must be a contiguous tensor of at least {nbytes} bytes on {q.device}")
+    st = load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l_), _ptr(ws), B, Hq, Hkv, S, D,
+                                 int(bool(causal)), _ptr(cu_seqlens), n, float(scale), _stream())
     _check(st, "attn_fwd")
     return o, l_
 

@@ -65,12 +65,19 @@ size_t attn_bwd_workspace_bytes(int batch, int hq, int hkv, int seqlen, int head
   return mi355attn::bwd_workspace_size(batch, hq, hkv, seqlen, head_dim);
 }
 
-attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int hq, int hkv,
-                     int seqlen, int head_dim, int causal, const int32_t* cu_seqlens, int num_seqs, float scale,
-                     attn_stream_t stream) {
+size_t attn_fwd_workspace_bytes(int batch, int hq, int hkv, int seqlen, int head_dim) {
+  if (batch <= 0 || hq <= 0 || hkv <= 0 || seqlen <= 0 || head_dim <= 0 || hq % hkv != 0) return 0;
+  if ((long long)seqlen * hq * head_dim > (long long)INT32_MAX) return 0;
+  return mi355attn::fwd_workspace_size(batch, hq, seqlen, head_dim);
+}
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace, int batch,
+                     int hq, int hkv, int seqlen, int head_dim, int causal, const int32_t* cu_seqlens, int num_seqs,
+                     float scale, attn_stream_t stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return ATTN_ERR_INVALID_ARGUMENT;
+  if (workspace && !aligned16(workspace)) return ATTN_ERR_INVALID_ARGUMENT;
   attn_status st = check_common(batch, hq, hkv, seqlen, head_dim, causal, cu_seqlens, num_seqs, scale);
   if (st != ATTN_OK) return st;
   if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
@@ -90,6 +97,14 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   p.causal = causal;
   p.scale = scale;
   p.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  p.key_split = 1;
+  const int ks = mi355attn::fwd_key_split(batch, hq, seqlen);
+  if (workspace != nullptr && ks > 1) {
+    p.key_split = ks;
+    p.part_o = static_cast<float*>(workspace);
+    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          mi355attn::fwd_part_lse_offset(batch, hq, seqlen, head_dim, ks));
+  }
   return launch_result(mi355attn::run_fwd_bf16(p, reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -25,6 +25,9 @@
 //   * Tiles partly (or wholly) outside a wave's visible keys are masked per
 //     element. Every LDS address is a per-lane base computed once plus a
 //     compile-time offset, and every per-tile branch is scalar.
+//   * Key split (grids too small to fill the GPU, chosen on the host): the key
+//     tiles of a query block are shared over key_split workgroups, which write
+//     fp32 partial results; attn_fwd_combine_kernel merges them.
 #include "attn_device.h"
 #include "attn_internal.h"
 
@@ -60,7 +63,12 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_bf16_kernel(FwdParams
   const int b = bh / p.hq;
   const int hq = bh - b * p.hq;
   const int hk = hq / (p.hq / p.hkv);
-  const int qblk = p.num_qblk - 1 - (int)blockIdx.y;  // heaviest blocks first
+  // blockIdx.y = rank * key_split + share, ranks from the heaviest block
+  // (the last one) down; with a key split the shares of a block run together
+  const int ks = p.key_split;
+  const int yrank = (int)blockIdx.y / ks;
+  const int share = (int)blockIdx.y - yrank * ks;
+  const int qblk = p.num_qblk - 1 - yrank;
   const int my_q = qblk * kBM + wave * 32 + n;
   const bool q_ok = my_q < p.seqlen;
 
@@ -98,8 +106,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_bf16_kernel(FwdParams
   }
   wg_lo = __builtin_amdgcn_readfirstlane(wg_lo);
   wg_hi = __builtin_amdgcn_readfirstlane(wg_hi);
-  const int tile_begin = wg_hi > wg_lo ? wg_lo / kBN : 0;
-  const int tile_end = wg_hi > wg_lo ? (wg_hi + kBN - 1) / kBN : 0;
+  const int blk_begin = wg_hi > wg_lo ? wg_lo / kBN : 0;
+  const int blk_tiles = wg_hi > wg_lo ? (wg_hi + kBN - 1) / kBN - blk_begin : 0;
+  // this workgroup's share of the block's key tiles (all of them without a split)
+  const int tile_begin = blk_begin + share * blk_tiles / ks;
+  const int tile_end = blk_begin + (share + 1) * blk_tiles / ks;
 
   // Q slice as B operands: lane (n, h) holds Q[my_q][16t + 8h .. +7]
   bf16x8 qf[KS];
@@ -259,10 +270,27 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_bf16_kernel(FwdParams
     if (i + 1 < ntile) body(i + 1, std::integral_constant<int, 1>{});
   }
 
-  // epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
+  // epilogue: O = acc / l, LSE = (m + log2 l) * ln 2; with a key split the
+  // share's fp32 O and m + log2 l, combined by attn_fwd_combine_kernel
   const float l_tot = sum_lane_halves(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (q_ok) {
+  if (q_ok && ks > 1) {
+    const size_t plane = (size_t)p.batch * p.seqlen * q_stride;
+    float* orow = p.part_o + (size_t)share * plane + ((size_t)b * p.seqlen + my_q) * q_stride + hq * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = acc[db][4 * g + e] * inv;
+        *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * g + 4 * h) = w;
+      }
+    if (h == 0) {
+      p.part_lse[(((size_t)share * p.batch + b) * p.hq + hq) * p.seqlen + my_q] =
+          l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
+    }
+  } else if (q_ok) {
     __bf16* orow = p.o + ((size_t)b * p.seqlen + my_q) * q_stride + hq * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -282,12 +310,65 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_bf16_kernel(FwdParams
   }
 }
 
+// ---------------------------------------------------------------------------
+// Key-split combine: for each (b, s, h_q) row and shares s = 1..ks with
+// partial outputs O_s and L_s = m_s + log2 l_s,
+//   O = sum_s 2^(L_s - M) O_s / sum_s 2^(L_s - M),  M = max_s L_s,
+//   LSE = (M + log2 sum_s 2^(L_s - M)) ln 2.
+// One thread per 8 consecutive d of a row; the D / 8 threads of a row sit in
+// one wave. HBM-bound: 4 ks bytes read and 2 written per output element.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_fwd_combine_kernel(FwdParams p) {
+  constexpr int T = D / 8;
+  const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t rows = (size_t)p.batch * p.seqlen * p.hq;
+  const size_t row = gid / T;  // (b * S + s) * Hq + h
+  const int sub = (int)(gid % T);
+  if (row >= rows) return;
+  const int hq = (int)(row % p.hq);
+  const size_t bs = row / p.hq;
+  const int s = (int)(bs % p.seqlen);
+  const int b = (int)(bs / p.seqlen);
+  const int ks = p.key_split;
+  const size_t lstride = (size_t)p.batch * p.hq * p.seqlen;
+  const size_t li = ((size_t)b * p.hq + hq) * p.seqlen + s;
+  float m = -INFINITY;
+  for (int sp = 0; sp < ks; ++sp) m = fmaxf(m, p.part_lse[sp * lstride + li]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float tot = 0.f;
+  if (m > -INFINITY) {
+    const size_t plane = rows * D;
+    for (int sp = 0; sp < ks; ++sp) {
+      const float w = fast_exp2(p.part_lse[sp * lstride + li] - m);  // 0 for a share without keys
+      tot += w;
+      const f32x4* src = reinterpret_cast<const f32x4*>(p.part_o + sp * plane + row * D + 8 * sub);
+      const f32x4 a = src[0], c = src[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += w * a[e];
+        acc[4 + e] += w * c[e];
+      }
+    }
+  }
+  const float inv = tot > 0.f ? 1.0f / tot : 0.f;
+  bf16x8 out;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = (__bf16)(acc[e] * inv);
+  *reinterpret_cast<bf16x8*>(p.o + row * D + 8 * sub) = out;
+  if (sub == 0) p.lse[li] = tot > 0.f ? (m + __log2f(tot)) * kLn2 : -INFINITY;
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
   FwdParams q = p;
   q.num_qblk = (p.seqlen + kBM - 1) / kBM;
-  dim3 grid(p.batch * p.hq, q.num_qblk);
+  dim3 grid(p.batch * p.hq, q.num_qblk * q.key_split);
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), grid, dim3(kWaves * 64), 0, stream, q);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || q.key_split == 1) return e;
+  const size_t threads = (size_t)p.batch * p.seqlen * p.hq * (D / 8);
+  hipLaunchKernelGGL((attn_fwd_combine_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, q);
   return hipGetLastError();
 }
 

@@ -20,6 +20,9 @@ struct FwdParams {
   float scale;
   float scale_log2e;  // scale * log2(e)
   int num_qblk;       // set by the launcher
+  int key_split;      // shares of each query block's key tiles (1: no split)
+  float* part_o;      // key_split > 1: fp32 partial O [ks][B][S][Hq][D], each normalised by its share's sum
+  float* part_lse;    // key_split > 1: fp32 m + log2 l [ks][B][Hq][S] (-inf for a share without visible keys)
 };
 
 struct Fp8FwdParams {
@@ -115,6 +118,38 @@ inline size_t bwd_workspace_size(int batch, int hq, int hkv, int seqlen, int hea
   const int nk = bwd_key_split(batch, hq, seqlen);
   const size_t part = nk > 1 ? (size_t)4 * nk * batch * seqlen * hq * head_dim : 0;
   return bwd_dq_part_offset(batch, hq, hkv, seqlen, head_dim) + part;
+}
+
+// Forward key split. The forward runs two 4-wave workgroups per CU and per
+// (b, query head, 128-query block), and a block's time grows with the keys it
+// visits, so with fewer than about 1024 blocks the slowest block (the last one
+// under a causal mask) sets the time while CUs idle. The key tiles of each
+// block are then split over up to 8 workgroups; each writes an fp32 partial
+// (O normalised by its own sum, and m + log2 l), and a second kernel combines
+// the shares. Every share keeps at least 32 key tiles (2048 keys): the
+// combine moves 8 bytes per share and output element, which shorter rows do
+// not earn back. The split needs the caller's workspace; without one the
+// forward runs unsplit.
+constexpr long kFwdTargetBlocks = 1024;
+constexpr int kFwdMaxKeySplit = 8;
+constexpr int kFwdMinTilesPerShare = 32;
+inline int fwd_key_split(int batch, int hq, int seqlen) {
+  const long units = (long)batch * hq * ((seqlen + 127) / 128);
+  if (units >= kFwdTargetBlocks) return 1;
+  long ks = (kFwdTargetBlocks + units - 1) / units;
+  if (ks > kFwdMaxKeySplit) ks = kFwdMaxKeySplit;
+  const long by_len = ((long)seqlen + 63) / 64 / kFwdMinTilesPerShare;
+  if (ks > by_len) ks = by_len;
+  return ks < 1 ? 1 : (int)ks;
+}
+// Workspace layout: partial O, then (256-byte aligned) the partial row statistics.
+inline size_t fwd_part_lse_offset(int batch, int hq, int seqlen, int head_dim, int ks) {
+  return align256((size_t)4 * ks * batch * seqlen * hq * head_dim);
+}
+inline size_t fwd_workspace_size(int batch, int hq, int seqlen, int head_dim) {
+  const int ks = fwd_key_split(batch, hq, seqlen);
+  if (ks == 1) return 0;
+  return fwd_part_lse_offset(batch, hq, seqlen, head_dim, ks) + (size_t)4 * ks * batch * hq * seqlen;
 }
 
 struct MergeParams {

@@ -89,10 +89,11 @@ S0 = ctypes.c_void_p(0)
 
 
 def _fwd(**kw):
-    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=4, Hkv=2, S=128, D=128, causal=1, cu=NULL, n=0, scale=0.088)
+    a = dict(q=P, k=P, v=P, o=P, lse=P, ws=NULL, B=1, Hq=4, Hkv=2, S=128, D=128, causal=1, cu=NULL, n=0,
+             scale=0.088)
     a.update(kw)
-    return lca.load_library().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["S"],
-                                       a["D"], a["causal"], a["cu"], a["n"], a["scale"], S0)
+    return lca.load_library().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"], a["B"], a["Hq"],
+                                       a["Hkv"], a["S"], a["D"], a["causal"], a["cu"], a["n"], a["scale"], S0)
 
 
 def _fp8(**kw):
@@ -128,13 +129,10 @@ def test_invalid_arguments_rejected(kw):
     assert _fp8(**kw) == lca.ATTN_ERR_INVALID_ARGUMENT
 
 
-@pytest.mark.parametrize("fn,kw", [(_fwd, dict(ws=None)), (_bwd, dict(ws=NULL)), (_bwd, dict(do=NULL)),
+@pytest.mark.parametrize("fn,kw", [(_fwd, dict(ws=PM)), (_bwd, dict(ws=NULL)), (_bwd, dict(do=NULL)),
                                    (_bwd, dict(ws=PM)), (_fp8, dict(dq=NULL)),
                                    (_fp8, dict(dv=ctypes.c_void_p((1 << 20) + 2)))])
 def test_entry_specific_pointers(fn, kw):
-    kw = {k: v for k, v in kw.items() if v is not None}
-    if not kw:
-        pytest.skip("attn_fwd has no workspace")
     assert fn(**kw) == lca.ATTN_ERR_INVALID_ARGUMENT
 
 
@@ -180,3 +178,28 @@ def test_oversized_requests_unsupported():
     assert lib.attn_bwd_workspace_bytes(1, 16, 4, 1 << 20, 128) == 0
     # merge: more than 2^40 elements in total
     assert _merge(B=1 << 10, S=1 << 20, H=1 << 10, D=128) == lca.ATTN_ERR_UNSUPPORTED
+
+
+def _fwd_split(B, Hq, S):
+    units = B * Hq * (-(-S // 128))
+    if units >= 1024:
+        return 1
+    return max(1, min(-(-1024 // units), 8, (-(-S // 64)) // 32))
+
+
+def test_fwd_workspace_bytes():
+    """Layout stated in include/attn.h: fp32 partial O, then (256-byte aligned) the partial row statistics."""
+    lib = lca.load_library()
+    a256 = lambda x: -(-x // 256) * 256
+    for args in [(1, 28, 4, 32768, 128), (2, 32, 32, 8192, 128), (1, 14, 2, 32768, 128), (1, 2, 1, 4032, 64),
+                 (1, 2, 1, 4033, 64), (1, 1, 1, 32768, 128), (1, 2, 1, 32768, 128), (3, 3, 1, 9000, 64),
+                 (1, 8, 1, 1000, 128), (1, 1, 1, 1, 128)]:
+        B, Hq, Hkv, S, D = args
+        ks = _fwd_split(B, Hq, S)
+        want = 0 if ks == 1 else a256(4 * ks * B * S * Hq * D) + 4 * ks * B * Hq * S
+        assert lib.attn_fwd_workspace_bytes(*args) == want, args
+    assert _fwd_split(1, 28, 32768) == 1 and _fwd_split(1, 1, 32768) == 4 and _fwd_split(1, 2, 4096) == 2
+    assert _fwd_split(1, 2, 4032) == 1 and _fwd_split(1, 2, 4033) == 2
+    assert lib.attn_fwd_workspace_bytes(0, 1, 1, 32768, 128) == 0
+    assert lib.attn_fwd_workspace_bytes(1, 3, 2, 32768, 128) == 0
+    assert lib.attn_fwd_workspace_bytes(1, 16, 4, 1 << 20, 128) == 0

@@ -94,11 +94,43 @@ def test_peaky_scores_exercise_rescaling():
     _run_case(1, 4, 1, 1500, 128, True, seed=46, qk_std=3.0, abs_factor=2.0)
 
 
-def test_outputs_are_bitwise_deterministic():
-    """No atomics: two runs on the same inputs give identical bits, with and without the split passes."""
+SPLIT = [
+    # B, Hq, Hkv, S, D, causal, lengths, expected key split
+    (1, 2, 1, 4096, 128, True, None, 2),
+    (1, 1, 1, 8192, 64, False, None, 4),
+    (1, 2, 1, 8192, 128, True, [3000, 5192], 4),
+    (2, 1, 1, 5000, 64, True, None, 2),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,D,causal,lengths,ks", SPLIT)
+def test_forward_key_split_matches_oracle(B, Hq, Hkv, S, D, causal, lengths, ks):
+    """Small grids split each query block's key tiles over ks workgroups and combine the shares;
+    the split and the unsplit forward both meet the oracle bar."""
     import torch
     lca = _lib()
-    for (B, Hq, Hkv, S, D, causal) in [(1, 8, 1, 1000, 128, True), (1, 28, 4, 8192, 128, True)]:
+    nbytes = lca.fwd_workspace_bytes(B, Hq, Hkv, S, D)
+    assert nbytes == -(-4 * ks * B * S * Hq * D // 256) * 256 + 4 * ks * B * Hq * S
+    print(f"case B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} causal={causal} lengths={lengths} ks={ks}", flush=True)
+    x = si.make_inputs(B, Hq, Hkv, S, D, 48, lengths=lengths, with_do=False)
+    q, k, v = dev_bf16(x.q_bits), dev_bf16(x.k_bits), dev_bf16(x.v_bits)
+    cu = dev_i32(x.cu_seqlens) if x.cu_seqlens is not None else None
+    scale = 1.0 / np.sqrt(D)
+    ro, rl = oracle.attention_fwd(x.values("q"), x.values("k"), x.values("v"), causal=causal, scale=scale,
+                                  cu_seqlens=x.cu_seqlens, workers=None)
+    for split in (True, False):
+        o, lse = lca.fwd(q, k, v, causal=causal, cu_seqlens=cu, scale=scale, split=split)
+        torch.cuda.synchronize()
+        check_fwd(host(o), host(lse), ro, rl, tag=f"fwd split={split}")
+
+
+def test_outputs_are_bitwise_deterministic():
+    """No atomics: two runs on the same inputs give identical bits, with and without the split passes
+    (the last case splits the forward's key tiles and the backward's heads and key tiles)."""
+    import torch
+    lca = _lib()
+    for (B, Hq, Hkv, S, D, causal) in [(1, 8, 1, 1000, 128, True), (1, 28, 4, 8192, 128, True),
+                                       (1, 2, 1, 8192, 128, True)]:
         print(f"case B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} causal={causal}", flush=True)
         x = si.make_inputs(B, Hq, Hkv, S, D, 47, with_do=True)
         q, k, v, do = dev_bf16(x.q_bits), dev_bf16(x.k_bits), dev_bf16(x.v_bits), dev_bf16(x.do_bits)
