@@ -79,8 +79,8 @@ typedef enum attn_status {
  * forward runs unsplit. The FA-3 paragraph of the FlashAttention page (section
  * "那么FlashAttention-2 和 -3 又改进了什么") has the kernel pick its tiling from
  * the sequence length; here the work split is picked from the sizes. With
- * fewer than 1024 (batch, query head, 128-query block) units the key tiles of
- * each block are split over ks = min(8, ceil(1024 / units), ceil(seqlen/64)/32)
+ * fewer than 512 (batch, query head, 128-query block) units the key tiles of
+ * each block are split over ks = min(8, ceil(512 / units), ceil(seqlen/64)/32)
  * workgroups (ks > 1 needs 64 key tiles, seqlen > 4032). The workspace then holds fp32
  * partial O [ks, B, S, Hq, D] and, 256-byte aligned after it, fp32 partial row
  * statistics [ks, B, Hq, S]. Returns 0 for invalid sizes as well. */

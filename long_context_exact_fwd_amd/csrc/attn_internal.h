@@ -120,17 +120,19 @@ inline size_t bwd_workspace_size(int batch, int hq, int hkv, int seqlen, int hea
   return bwd_dq_part_offset(batch, hq, hkv, seqlen, head_dim) + part;
 }
 
-// Forward key split. The forward runs two 4-wave workgroups per CU and per
-// (b, query head, 128-query block), and a block's time grows with the keys it
-// visits, so with fewer than about 1024 blocks the slowest block (the last one
-// under a causal mask) sets the time while CUs idle. The key tiles of each
-// block are then split over up to 8 workgroups; each writes an fp32 partial
-// (O normalised by its own sum, and m + log2 l), and a second kernel combines
-// the shares. Every share keeps at least 32 key tiles (2048 keys): the
-// combine moves 8 bytes per share and output element, which shorter rows do
-// not earn back. The split needs the caller's workspace; without one the
-// forward runs unsplit.
-constexpr long kFwdTargetBlocks = 1024;
+// Forward key split. The forward runs one workgroup per (b, query head,
+// 128-query block), two per CU, and a block's time grows with the keys it
+// visits. One workgroup alone on a CU still reaches about 94 % of the
+// throughput of two, so what a small grid loses is the slowest block (the last
+// one under a causal mask, twice the average) running on while CUs idle: with
+// fewer than about 512 blocks it outlasts the per-CU share of the work. The
+// key tiles of each block are then split over up to 8 workgroups; each writes
+// an fp32 partial (O normalised by its own sum, and m + log2 l), and a second
+// kernel combines the shares. Every share keeps at least 32 key tiles (2048
+// keys): the combine moves 8 bytes per share and output element, which
+// shorter rows do not earn back. The split needs the caller's workspace;
+// without one the forward runs unsplit.
+constexpr long kFwdTargetBlocks = 512;
 constexpr int kFwdMaxKeySplit = 8;
 constexpr int kFwdMinTilesPerShare = 32;
 inline int fwd_key_split(int batch, int hq, int seqlen) {

@@ -182,9 +182,9 @@ def test_oversized_requests_unsupported():
 
 def _fwd_split(B, Hq, S):
     units = B * Hq * (-(-S // 128))
-    if units >= 1024:
+    if units >= 512:
         return 1
-    return max(1, min(-(-1024 // units), 8, (-(-S // 64)) // 32))
+    return max(1, min(-(-512 // units), 8, (-(-S // 64)) // 32))
 
 
 def test_fwd_workspace_bytes():
@@ -198,7 +198,8 @@ def test_fwd_workspace_bytes():
         ks = _fwd_split(B, Hq, S)
         want = 0 if ks == 1 else a256(4 * ks * B * S * Hq * D) + 4 * ks * B * Hq * S
         assert lib.attn_fwd_workspace_bytes(*args) == want, args
-    assert _fwd_split(1, 28, 32768) == 1 and _fwd_split(1, 1, 32768) == 4 and _fwd_split(1, 2, 4096) == 2
+    assert _fwd_split(1, 28, 32768) == 1 and _fwd_split(1, 2, 32768) == 1 and _fwd_split(1, 1, 32768) == 2
+    assert _fwd_split(1, 2, 4096) == 2 and _fwd_split(1, 1, 16384) == 4
     assert _fwd_split(1, 2, 4032) == 1 and _fwd_split(1, 2, 4033) == 2
     assert lib.attn_fwd_workspace_bytes(0, 1, 1, 32768, 128) == 0
     assert lib.attn_fwd_workspace_bytes(1, 3, 2, 32768, 128) == 0
