@@ -363,6 +363,7 @@ template <int D, bool CAUSAL>
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
   FwdParams q = p;
   q.num_qblk = (p.seqlen + kBM - 1) / kBM;
+  if (q.key_split < 1 || q.part_o == nullptr || q.part_lse == nullptr) q.key_split = 1;
   dim3 grid(p.batch * p.hq, q.num_qblk * q.key_split);
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), grid, dim3(kWaves * 64), 0, stream, q);
   hipError_t e = hipGetLastError();
