@@ -1,0 +1,48 @@
+"""Host-side checks of bench.py that need no GPU: the one-GPU refusal, the
+visible-pair counts behind every TFLOP/s figure, and the source lists the
+HBM-traffic records are keyed on."""
+import os
+
+import numpy as np
+
+import bench
+import seeded_inputs as si
+
+
+def test_more_than_one_gpu_is_refused(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
+
+
+def _brute_pairs(S, causal, lengths=None):
+    seg = np.zeros(S, dtype=int) if lengths is None else np.repeat(np.arange(len(lengths)), lengths)
+    i, j = np.meshgrid(np.arange(S), np.arange(S), indexing="ij")
+    ok = seg[i] == seg[j]
+    if causal:
+        ok &= j <= i
+    return int(ok.sum())
+
+
+def test_visible_pairs_match_brute_force():
+    for S, causal, lengths in [(1, True, None), (7, True, None), (7, False, None), (64, True, None),
+                               (20, True, [5, 1, 14]), (20, False, [5, 1, 14]), (9, True, [1] * 9)]:
+        cu = None if lengths is None else np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+        assert bench._pairs(S, causal, cu) == _brute_pairs(S, causal, lengths), (S, causal, lengths)
+
+
+def test_headline_flop_count():
+    # gqa32k: 14 D flops per visible pair (4 forward + 10 backward), 28 query heads
+    w = si.WORKLOADS["gqa32k"]
+    pairs = bench._pairs(w.seqlen, True) * w.batch * w.hq
+    assert pairs == 28 * 32768 * 32769 / 2
+    assert abs(14 * 128 * pairs - 2.694e13) / 2.694e13 < 1e-3
+
+
+def test_kernel_sources_exist_and_hash_stably():
+    csrc = os.path.join(bench.ROOT, "long_context_exact_fwd_amd", "csrc")
+    for kernel, files in bench.KERNEL_SOURCES.items():
+        for f in files:
+            assert os.path.exists(os.path.join(csrc, f)), (kernel, f)
+        h = bench.kernel_source_hash(kernel)
+        assert h == bench.kernel_source_hash(kernel) and len(h) >= 16
+    assert set(bench.KERNEL_OF_PHASE.values()) <= set(bench.KERNEL_SOURCES)
