@@ -75,7 +75,7 @@ typedef enum attn_status {
   ATTN_ERR_HIP = 3               /* a kernel launch failed; see attn_last_hip_error() */
 } attn_status;
 
-/* Bytes of device workspace attn_fwd can use for these sizes: 0 when the
+/* Bytes of device workspace attn_fwd (and attn_fwd_fp8) can use for these sizes: 0 when the
  * forward runs unsplit. The FA-3 paragraph of the FlashAttention page (section
  * "那么FlashAttention-2 和 -3 又改进了什么") has the kernel pick its tiling from
  * the sequence length; here the work split is picked from the sizes. With
@@ -110,11 +110,13 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
  * code * descale. descale_q/k/v: device pointers to one float each.
  * o: bfloat16 [B,S,Hq,D]; lse: float32 [B,Hq,S] of the dequantised scores.
  * The probabilities fed to the PV product are rounded to E4M3. The row sum is
- * taken from the fp32 probabilities. head_dim must be 128.
+ * taken from the fp32 probabilities. head_dim must be 128. workspace: as for
+ * attn_fwd (NULL, or attn_fwd_workspace_bytes() bytes for the same sizes);
+ * the key split and the combine work the same way.
  */
 attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
                          const float* descale_q, const float* descale_k, const float* descale_v,
-                         void* o, float* lse,
+                         void* o, float* lse, void* workspace,
                          int batch, int hq, int hkv, int seqlen, int head_dim,
                          int causal, const int32_t* cu_seqlens, int num_seqs,
                          float scale, attn_stream_t stream);

@@ -45,7 +45,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     vp, i, f, st = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_void_p
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, f, st]
     lib.attn_fwd.restype = i
-    lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, f, st]
+    lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, f, st]
     lib.attn_fwd_fp8.restype = i
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, f, st]
     lib.attn_bwd.restype = i
@@ -141,25 +141,33 @@ def fwd(q, k, v, *, causal: bool, cu_seqlens=None, scale: Optional[float] = None
         scale = 1.0 / math.sqrt(D)
     o = out if out is not None else torch.empty_like(q)
     l_ = lse if lse is not None else torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
-    ws = None
-    nbytes = fwd_workspace_bytes(B, Hq, Hkv, S, D) if split else 0
-    if nbytes > 0:
-        if workspace is None:
-            ws = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=q.device)
-        elif workspace.is_contiguous() and workspace.numel() * workspace.element_size() >= nbytes \
-                and workspace.device == q.device:
-            ws = workspace
-        else:
-            raise ValueError(f"workspace must be a contiguous tensor of at least {nbytes} bytes on {q.device}")
+    ws = _fwd_workspace(B, Hq, Hkv, S, D, q.device, workspace, split)
     st = load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l_), _ptr(ws), B, Hq, Hkv, S, D,
                                  int(bool(causal)), _ptr(cu_seqlens), n, float(scale), _stream())
     _check(st, "attn_fwd")
     return o, l_
 
 
+def _fwd_workspace(B, Hq, Hkv, S, D, device, workspace, split):
+    """The key-split workspace for a forward call, or None (marshalling only)."""
+    import torch
+    nbytes = fwd_workspace_bytes(B, Hq, Hkv, S, D) if split else 0
+    if nbytes == 0:
+        return None
+    if workspace is None:
+        return torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=device)
+    if workspace.is_contiguous() and workspace.numel() * workspace.element_size() >= nbytes \
+            and workspace.device == device:
+        return workspace
+    raise ValueError(f"workspace must be a contiguous tensor of at least {nbytes} bytes on {device}")
+
+
 def fwd_fp8(q8, k8, v8, descale_q, descale_k, descale_v, *, causal: bool, cu_seqlens=None,
-            scale: Optional[float] = None, out=None, lse=None):
-    """Forward with E4M3FN codes (uint8 tensors) and fp32 device descales (1 element each)."""
+            scale: Optional[float] = None, out=None, lse=None, workspace=None, split: bool = True):
+    """Forward with E4M3FN codes (uint8 tensors) and fp32 device descales (1 element each).
+
+    ``workspace`` and ``split`` work as in fwd().
+    """
     import torch
     _check_tensors(q8, k8, v8, dtype=torch.uint8)
     _check_tensors(descale_q, descale_k, descale_v, dtype=torch.float32)
@@ -168,9 +176,10 @@ def fwd_fp8(q8, k8, v8, descale_q, descale_k, descale_v, *, causal: bool, cu_seq
         scale = 1.0 / math.sqrt(D)
     o = out if out is not None else torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device=q8.device)
     l_ = lse if lse is not None else torch.empty((B, Hq, S), dtype=torch.float32, device=q8.device)
+    ws = _fwd_workspace(B, Hq, Hkv, S, D, q8.device, workspace, split) if D == 128 else None
     st = load_library().attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(descale_q), _ptr(descale_k),
-                                     _ptr(descale_v), _ptr(o), _ptr(l_), B, Hq, Hkv, S, D, int(bool(causal)),
-                                     _ptr(cu_seqlens), n, float(scale), _stream())
+                                     _ptr(descale_v), _ptr(o), _ptr(l_), _ptr(ws), B, Hq, Hkv, S, D,
+                                     int(bool(causal)), _ptr(cu_seqlens), n, float(scale), _stream())
     _check(st, "attn_fwd_fp8")
     return o, l_
 

@@ -109,12 +109,13 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
 }
 
 attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* descale_q,
-                         const float* descale_k, const float* descale_v, void* o, float* lse, int batch, int hq,
-                         int hkv, int seqlen, int head_dim, int causal, const int32_t* cu_seqlens, int num_seqs,
-                         float scale, attn_stream_t stream) {
+                         const float* descale_k, const float* descale_v, void* o, float* lse, void* workspace,
+                         int batch, int hq, int hkv, int seqlen, int head_dim, int causal,
+                         const int32_t* cu_seqlens, int num_seqs, float scale, attn_stream_t stream) {
   if (!q8 || !k8 || !v8 || !descale_q || !descale_k || !descale_v || !o || !lse) return ATTN_ERR_INVALID_ARGUMENT;
   if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o) || !aligned16(lse))
     return ATTN_ERR_INVALID_ARGUMENT;
+  if (workspace && !aligned16(workspace)) return ATTN_ERR_INVALID_ARGUMENT;
   if ((reinterpret_cast<uintptr_t>(descale_q) & 3u) || (reinterpret_cast<uintptr_t>(descale_k) & 3u) ||
       (reinterpret_cast<uintptr_t>(descale_v) & 3u))
     return ATTN_ERR_INVALID_ARGUMENT;
@@ -139,6 +140,14 @@ attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const f
   p.head_dim = head_dim;
   p.causal = causal;
   p.scale = scale;
+  p.key_split = 1;
+  const int ks = mi355attn::fwd_key_split(batch, hq, seqlen);
+  if (workspace != nullptr && ks > 1) {
+    p.key_split = ks;
+    p.part_o = static_cast<float*>(workspace);
+    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          mi355attn::fwd_part_lse_offset(batch, hq, seqlen, head_dim, ks));
+  }
   return launch_result(mi355attn::run_fwd_fp8(p, reinterpret_cast<hipStream_t>(stream)));
 }
 

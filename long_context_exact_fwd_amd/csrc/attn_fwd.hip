@@ -368,12 +368,21 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), grid, dim3(kWaves * 64), 0, stream, q);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || q.key_split == 1) return e;
-  const size_t threads = (size_t)p.batch * p.seqlen * p.hq * (D / 8);
-  hipLaunchKernelGGL((attn_fwd_combine_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, q);
-  return hipGetLastError();
+  return run_fwd_combine(q, stream);
 }
 
 }  // namespace
+
+hipError_t run_fwd_combine(const FwdParams& p, hipStream_t stream) {
+  const size_t threads = (size_t)p.batch * p.seqlen * p.hq * (p.head_dim / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (p.head_dim == 128) {
+    hipLaunchKernelGGL((attn_fwd_combine_kernel<128>), grid, dim3(256), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((attn_fwd_combine_kernel<64>), grid, dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
+}
 
 hipError_t run_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   if (p.head_dim == 128) {

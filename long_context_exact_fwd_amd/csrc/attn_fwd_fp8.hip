@@ -78,7 +78,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_fp8_kernel(Fp8FwdPara
   const int b = bh / p.hq;
   const int hq = bh - b * p.hq;
   const int hk = hq / (p.hq / p.hkv);
-  const int qblk = p.num_qblk - 1 - (int)blockIdx.y;
+  // blockIdx.y = rank * key_split + share, ranks from the heaviest block down
+  const int ks = p.key_split;
+  const int yrank = (int)blockIdx.y / ks;
+  const int share = (int)blockIdx.y - yrank * ks;
+  const int qblk = p.num_qblk - 1 - yrank;
   const int my_q = qblk * kBM + wave * 32 + n;
   const bool q_ok = my_q < p.seqlen;
 
@@ -112,8 +116,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_fp8_kernel(Fp8FwdPara
   }
   wg_lo = __builtin_amdgcn_readfirstlane(wg_lo);
   wg_hi = __builtin_amdgcn_readfirstlane(wg_hi);
-  const int tile_begin = wg_hi > wg_lo ? wg_lo / kBN : 0;
-  const int tile_end = wg_hi > wg_lo ? (wg_hi + kBN - 1) / kBN : 0;
+  const int blk_begin = wg_hi > wg_lo ? wg_lo / kBN : 0;
+  const int blk_tiles = wg_hi > wg_lo ? (wg_hi + kBN - 1) / kBN - blk_begin : 0;
+  // this workgroup's share of the block's key tiles (all of them without a split)
+  const int tile_begin = blk_begin + share * blk_tiles / ks;
+  const int tile_end = blk_begin + (share + 1) * blk_tiles / ks;
 
   // Q as B operands: k-step t, bytes [64t + 32h, +32) of the lane's query row.
   i32x8 qf[2];
@@ -264,7 +271,24 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_fp8_kernel(Fp8FwdPara
   // O = acc * descale_v / l; LSE = (m - offset + log2 l) * ln 2
   const float l_tot = sum_lane_halves(l_run);
   const float inv = l_tot > 0.f ? dv / l_tot : 0.f;
-  if (q_ok) {
+  if (q_ok && ks > 1) {
+    // key split: this share's O (fp32, descaled) and m - offset + log2 l
+    const size_t plane = (size_t)p.batch * p.seqlen * p.hq * kD;
+    float* orow = p.part_o + (size_t)share * plane + ((size_t)b * p.seqlen + my_q) * (size_t)(p.hq * kD) + hq * kD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = acc[db][4 * g + e] * inv;
+        *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * g + 4 * h) = w;
+      }
+    if (h == 0) {
+      p.part_lse[(((size_t)share * p.batch + b) * p.hq + hq) * p.seqlen + my_q] =
+          l_tot > 0.f ? m_run - kP8Offset + __log2f(l_tot) : -INFINITY;
+    }
+  } else if (q_ok) {
     __bf16* orow = p.o + ((size_t)b * p.seqlen + my_q) * (size_t)(p.hq * kD) + hq * kD;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -288,9 +312,22 @@ template <bool CAUSAL>
 hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream) {
   Fp8FwdParams q = p;
   q.num_qblk = (p.seqlen + kBM - 1) / kBM;
-  dim3 grid(p.batch * p.hq, q.num_qblk);
+  if (q.key_split < 1 || q.part_o == nullptr || q.part_lse == nullptr) q.key_split = 1;
+  dim3 grid(p.batch * p.hq, q.num_qblk * q.key_split);
   hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL>), grid, dim3(kWaves * 64), 0, stream, q);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || q.key_split == 1) return e;
+  FwdParams c{};
+  c.o = q.o;
+  c.lse = q.lse;
+  c.part_o = q.part_o;
+  c.part_lse = q.part_lse;
+  c.batch = q.batch;
+  c.seqlen = q.seqlen;
+  c.hq = q.hq;
+  c.head_dim = kD;
+  c.key_split = q.key_split;
+  return run_fwd_combine(c, stream);
 }
 
 }  // namespace

@@ -40,6 +40,9 @@ struct Fp8FwdParams {
   int causal;
   float scale;
   int num_qblk;
+  int key_split;    // as in FwdParams (1: no split)
+  float* part_o;    // key_split > 1: fp32 partial O [ks][B][S][Hq][D]
+  float* part_lse;  // key_split > 1: fp32 m + log2 l [ks][B][Hq][S], in log2 units of the scores
 };
 
 struct BwdParams {
@@ -165,6 +168,9 @@ struct MergeParams {
 };
 
 hipError_t run_fwd_bf16(const FwdParams& p, hipStream_t stream);
+// Combine the key-split partials of p.part_o / p.part_lse into p.o and p.lse
+// (uses o, lse, part_o, part_lse, batch, seqlen, hq, head_dim, key_split).
+hipError_t run_fwd_combine(const FwdParams& p, hipStream_t stream);
 hipError_t run_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream);
 constexpr unsigned kBwdDelta = 1u, kBwdDkDv = 2u, kBwdDq = 4u;
 hipError_t run_bwd(const BwdParams& p, unsigned phases, hipStream_t stream);

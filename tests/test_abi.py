@@ -97,12 +97,12 @@ def _fwd(**kw):
 
 
 def _fp8(**kw):
-    a = dict(q=P, k=P, v=P, dq=P, dk=P, dv=P, o=P, lse=P, B=1, Hq=4, Hkv=2, S=128, D=128, causal=1, cu=NULL, n=0,
-             scale=0.088)
+    a = dict(q=P, k=P, v=P, dq=P, dk=P, dv=P, o=P, lse=P, ws=NULL, B=1, Hq=4, Hkv=2, S=128, D=128, causal=1,
+             cu=NULL, n=0, scale=0.088)
     a.update(kw)
     return lca.load_library().attn_fwd_fp8(a["q"], a["k"], a["v"], a["dq"], a["dk"], a["dv"], a["o"], a["lse"],
-                                           a["B"], a["Hq"], a["Hkv"], a["S"], a["D"], a["causal"], a["cu"], a["n"],
-                                           a["scale"], S0)
+                                           a["ws"], a["B"], a["Hq"], a["Hkv"], a["S"], a["D"], a["causal"], a["cu"],
+                                           a["n"], a["scale"], S0)
 
 
 def _bwd(**kw):
@@ -130,7 +130,7 @@ def test_invalid_arguments_rejected(kw):
 
 
 @pytest.mark.parametrize("fn,kw", [(_fwd, dict(ws=PM)), (_bwd, dict(ws=NULL)), (_bwd, dict(do=NULL)),
-                                   (_bwd, dict(ws=PM)), (_fp8, dict(dq=NULL)),
+                                   (_bwd, dict(ws=PM)), (_fp8, dict(dq=NULL)), (_fp8, dict(ws=PM)),
                                    (_fp8, dict(dv=ctypes.c_void_p((1 << 20) + 2)))])
 def test_entry_specific_pointers(fn, kw):
     assert fn(**kw) == lca.ATTN_ERR_INVALID_ARGUMENT

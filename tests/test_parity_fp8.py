@@ -16,17 +16,17 @@ from tests.gpu_helpers import TOL_FP8_REL, TOL_LSE, dev_i32, dev_u8, host, max_a
 pytestmark = pytest.mark.gpu
 
 
-def _run_fp8(B, Hq, Hkv, S, D, causal, lengths=None, seed=21, qk_std=1.0):
+def _run_fp8(B, Hq, Hkv, S, D, causal, lengths=None, seed=21, qk_std=1.0, split=True):
     import torch
     import long_context_exact_fwd_amd as lca
     print(f"fp8 case B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} causal={causal} lengths={lengths} seed={seed} "
-          f"qk_std={qk_std}", flush=True)
+          f"qk_std={qk_std} split={split}", flush=True)
     x = si.make_inputs(B, Hq, Hkv, S, D, seed, lengths=lengths, fp8=True, with_do=False, qk_std=qk_std)
     q8, k8, v8 = dev_u8(x.q_bits), dev_u8(x.k_bits), dev_u8(x.v_bits)
     ds = [torch.tensor([float(d)], dtype=torch.float32, device="cuda") for d in x.descale]
     cu = dev_i32(x.cu_seqlens) if x.cu_seqlens is not None else None
     scale = 1.0 / np.sqrt(D)
-    o, lse = lca.fwd_fp8(q8, k8, v8, *ds, causal=causal, cu_seqlens=cu, scale=scale)
+    o, lse = lca.fwd_fp8(q8, k8, v8, *ds, causal=causal, cu_seqlens=cu, scale=scale, split=split)
     torch.cuda.synchronize()
     qv = oracle.e4m3_decode(x.q_bits) * float(x.descale[0])
     kv = oracle.e4m3_decode(x.k_bits) * float(x.descale[1])
@@ -57,6 +57,18 @@ CASES = [
 @pytest.mark.parametrize("B,Hq,Hkv,S,D,causal,lengths", CASES)
 def test_fp8_forward(B, Hq, Hkv, S, D, causal, lengths):
     _run_fp8(B, Hq, Hkv, S, D, causal, lengths=lengths)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,causal,lengths,ks", [(1, 1, 1, 8192, True, None, 4),
+                                                          (1, 2, 1, 8192, False, [3000, 5192], 4),
+                                                          (1, 8, 1, 4096, True, None, 2)])
+def test_fp8_forward_key_split(B, Hq, Hkv, S, causal, lengths, ks):
+    """Small grids split the key tiles over ks workgroups (shares combined by the same kernel as the bf16
+    path); both the split and the unsplit fp8 forward meet the fp8 bar."""
+    import long_context_exact_fwd_amd as lca
+    assert lca.fwd_workspace_bytes(B, Hq, Hkv, S, 128) == -(-4 * ks * B * S * Hq * 128 // 256) * 256 + 4 * ks * B * Hq * S
+    for split in (True, False):
+        _run_fp8(B, Hq, Hkv, S, 128, causal, lengths=lengths, seed=22, split=split)
 
 
 def test_fp8_peaky_scores_exercise_rescaling():
