@@ -108,42 +108,64 @@ __device__ void block_order(const BwdParams& p, int wg) {
 // ceil(num_blk * head_split / 256) + ceil(num_blk * key_split / 256)
 // workgroups write the work order instead.
 // ---------------------------------------------------------------------------
+// Rows per thread of the Delta kernel: all their loads are issued before the
+// first product, so each thread keeps 2 * kDeltaRows 16-byte loads in flight.
+constexpr int kDeltaRows = 4;
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
-  constexpr int LPR = D / 8;  // lanes per row
-  constexpr int RPB = 256 / LPR;
-  {
-    const long nrows = (long)p.batch * p.hq * p.stat_stride;
-    const int nstat = (int)((nrows + RPB - 1) / RPB);
-    if ((int)blockIdx.x >= nstat) {
-      block_order<CAUSAL>(p, (int)blockIdx.x - nstat);
-      return;
+  constexpr int LPR = D / 8;            // lanes per row, 16 bytes each
+  constexpr int RPB = 256 / LPR;        // rows per pass of the workgroup
+  constexpr int RPW = RPB * kDeltaRows;  // rows per workgroup
+  // Rows are taken in the memory order of O and dO ([B, S, Hq, D]), so a wave
+  // streams 64 / LPR consecutive rows. After them come the workgroups that
+  // zero the padding rows [S, S64) of the statistics, then the work order.
+  const long nrows = (long)p.batch * p.seqlen * p.hq;
+  const int nstat = (int)((nrows + RPW - 1) / RPW);
+  const int padw = p.stat_stride - p.seqlen;
+  const long npad = (long)p.batch * p.hq * padw;
+  const int npadwg = (int)((npad + 255) / 256);
+  const int wg = (int)blockIdx.x;
+  if (wg >= nstat + npadwg) {
+    block_order<CAUSAL>(p, wg - nstat - npadwg);
+    return;
+  }
+  if (wg >= nstat) {
+    // padding rows get zeros: whole-tile copies read them and mask them
+    const long j = (long)(wg - nstat) * 256 + threadIdx.x;
+    if (j < npad) {
+      const long r = (j / padw) * p.stat_stride + p.seqlen + (j % padw);
+      p.delta[r] = 0.f;
+      p.lse2[r] = 0.f;
     }
+    return;
   }
   const int tid = threadIdx.x;
-  const long r = (long)blockIdx.x * RPB + tid / LPR;  // index into [B, Hq, stat_stride]
-  const long nrows = (long)p.batch * p.hq * p.stat_stride;
   const int sub = tid % LPR;
-  const long i = r % p.stat_stride;
-  const bool real = r < nrows && i < p.seqlen;
-  float acc = 0.f;
-  if (real) {
-    const long bh = r / p.stat_stride;
-    const long b = bh / p.hq;
-    const long hq = bh % p.hq;
-    const size_t off = ((size_t)(b * p.seqlen + i) * p.hq + hq) * D + sub * 8;
-    const bf16x8 av = as_bf16x8(load16(p.o + off));
-    const bf16x8 gv = as_bf16x8(load16(p.dout + off));
+  const long r0 = (long)wg * RPW + tid / LPR;
+  bf16x8 av[kDeltaRows], gv[kDeltaRows];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += (float)av[e] * (float)gv[e];
+  for (int k = 0; k < kDeltaRows; ++k) {
+    const long r = min(r0 + (long)k * RPB, nrows - 1);  // rows past the end re-read the last one, unused
+    av[k] = as_bf16x8(load16(p.o + r * D + sub * 8));
+    gv[k] = as_bf16x8(load16(p.dout + r * D + sub * 8));
   }
 #pragma unroll
-  for (int o = LPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-  if (r < nrows && sub == 0) {
-    // padding rows get zeros: they are read by whole-tile copies and masked
-    const long bh = r / p.stat_stride;
-    p.delta[r] = acc;
-    p.lse2[r] = real ? p.lse[bh * p.seqlen + i] * kLog2e : 0.f;
+  for (int k = 0; k < kDeltaRows; ++k) {
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += (float)av[k][e] * (float)gv[k][e];
+#pragma unroll
+    for (int o = LPR / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    const long r = r0 + (long)k * RPB;  // (b * S + i) * Hq + h
+    if (r < nrows && sub == 0) {
+      const long hq = r % p.hq;
+      const long bs = r / p.hq;
+      const long i = bs % p.seqlen;
+      const long bh = (bs / p.seqlen) * p.hq + hq;
+      p.delta[bh * p.stat_stride + i] = acc;
+      p.lse2[bh * p.stat_stride + i] = p.lse[bh * p.seqlen + i] * kLog2e;
+    }
   }
 }
 
@@ -795,11 +817,12 @@ hipError_t launch_bwd(const BwdParams& p_in, unsigned phases, hipStream_t stream
   BwdParams q = p_in;
   q.num_blk = (q.seqlen + 127) / 128;
   if (phases & kBwdDelta) {
-    constexpr int RPB = 256 / (D / 8);
-    const long nrows = (long)q.batch * q.hq * q.stat_stride;
-    const long nstat = (nrows + RPB - 1) / RPB;
+    constexpr int RPW = 256 / (D / 8) * kDeltaRows;
+    const long nrows = (long)q.batch * q.seqlen * q.hq;
+    const long nstat = (nrows + RPW - 1) / RPW;
+    const long npadwg = ((long)q.batch * q.hq * (q.stat_stride - q.seqlen) + 255) / 256;
     const long norder = (q.num_blk * (long)q.head_split + 255) / 256 + (q.num_blk * (long)q.key_split + 255) / 256;
-    dim3 grid((unsigned)(nstat + norder));
+    dim3 grid((unsigned)(nstat + npadwg + norder));
     hipLaunchKernelGGL((attn_bwd_delta_kernel<D, CAUSAL>), grid, dim3(256), 0, stream, q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
