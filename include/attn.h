@@ -90,7 +90,9 @@ size_t attn_fwd_workspace_bytes(int batch, int hq, int hkv, int seqlen, int head
  * q [B,S,Hq,D], k and v [B,S,Hkv,D] bfloat16 (read only).
  * o [B,S,Hq,D] bfloat16 (written). lse [B,Hq,S] float32 (written).
  * workspace: NULL, or 16-byte aligned device memory of at least
- * attn_fwd_workspace_bytes() bytes. With NULL the forward always runs one
+ * attn_fwd_workspace_bytes() bytes, owned by the caller, contents on entry
+ * ignored; calls that may run at the same time need separate workspaces. With
+ * NULL the forward always runs one
  * workgroup per query block. With a workspace, sizes that
  * attn_fwd_workspace_bytes() sizes above 0 run the key split: each share
  * writes its partial output, and a second kernel combines the shares
