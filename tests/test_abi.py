@@ -204,3 +204,24 @@ def test_fwd_workspace_bytes():
     assert lib.attn_fwd_workspace_bytes(0, 1, 1, 32768, 128) == 0
     assert lib.attn_fwd_workspace_bytes(1, 3, 2, 32768, 128) == 0
     assert lib.attn_fwd_workspace_bytes(1, 16, 4, 1 << 20, 128) == 0
+
+
+def _phases(ph, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, ws=P, B=1, Hq=4, Hkv=2, S=128, D=128, causal=1,
+             cu=NULL, n=0, scale=0.088)
+    a.update(kw)
+    return lca.load_library().attn_bwd_phases(ph, a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                                              a["dv"], a["ws"], a["B"], a["Hq"], a["Hkv"], a["S"], a["D"], a["causal"],
+                                              a["cu"], a["n"], a["scale"], S0)
+
+
+@pytest.mark.parametrize("ph", [0, 8, 9, 15, 0xFFFFFFFF])
+def test_bwd_phases_bitmask_rejected(ph):
+    assert _phases(ph) == lca.ATTN_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", BAD[:8] + [dict(ws=NULL), dict(do=PM)])
+def test_bwd_phases_arguments_checked_like_bwd(kw):
+    for ph in (lca.BWD_DELTA, lca.BWD_DKDV, lca.BWD_DQ, lca.BWD_ALL):
+        assert _phases(ph, **kw) == lca.ATTN_ERR_INVALID_ARGUMENT
+    assert _phases(lca.BWD_ALL, D=96) == lca.ATTN_ERR_UNSUPPORTED
