@@ -376,6 +376,23 @@ def main(argv=None) -> int:
         "avg_launch_ms": round(per[dom], 4),
         "algorithmic_flops_per_launch": flops_k[dom],
     }
+    # every kernel of the step against its own bound: the three contractions
+    # against the bf16 MFMA peak (dQ also with the 6 D flops per pair it
+    # executes), Delta against HBM (read O and dO, write Delta and LSE*log2 e)
+    rows = w.batch * w.seqlen * Hq
+    delta_bytes = 2.0 * rows * D * 2 + 8.0 * rows
+    per_kernel = {}
+    for ph in ("attn_fwd", "bwd_dkdv", "bwd_dq"):
+        tf = flops_k[ph] / (per[ph] * 1e-3) / 1e12
+        per_kernel[KERNEL_OF_PHASE[ph]] = {"bound": "mfma", "avg_launch_ms": round(per[ph], 4),
+                                           "achieved": round(tf, 2), "unit": "TFLOP/s",
+                                           "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    dq_exec = 6.0 * D * pairs / (per["bwd_dq"] * 1e-3) / 1e12
+    per_kernel[KERNEL_OF_PHASE["bwd_dq"]]["executed_frac"] = round(dq_exec / PEAK_BF16_TFLOPS, 4)
+    gbs = delta_bytes / (per["bwd_delta"] * 1e-3) / 1e9
+    per_kernel[KERNEL_OF_PHASE["bwd_delta"]] = {"bound": "hbm", "avg_launch_ms": round(per["bwd_delta"], 4),
+                                                "achieved": round(gbs, 1), "unit": "GB/s",
+                                                "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
     if a.calib_copy_mib > 0:
         n = a.calib_copy_mib * (1 << 20) // 4
@@ -408,6 +425,7 @@ def main(argv=None) -> int:
         "phases_ms": {n: round(t, 4) for n, t in per.items()},
         "wall_s_timed": round(wall, 3),
         "roofline": roofline,
+        "kernels": per_kernel,
         "cpu_baseline": None,
         "workloads": None,
     }
