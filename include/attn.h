@@ -35,8 +35,14 @@
  *     both lie in the same segment (block-diagonal), and causal applies
  *     within the segment. Packing several samples into one long sequence is
  *     the packing of the Ulysses page §5 and of the FlashAttention page's
- *     section on engineering results. cu_seqlens contents are not checked on
- *     the device; a malformed array gives undefined results.
+ *     section on engineering results. cu_seqlens contents are not checked
+ *     by default (that needs a copy to the host and a sync): a malformed
+ *     array gives meaningless results, but the kernels clamp every segment to
+ *     [0, seqlen) around its own row, so they never access memory outside the
+ *     tensors. With the environment variable ATTN_VALIDATE=1 each call copies
+ *     cu_seqlens to the host first (synchronising `stream`) and returns
+ *     ATTN_ERR_INVALID_ARGUMENT, with nothing launched, unless cu_seqlens[0]
+ *     = 0, the entries strictly increase and cu_seqlens[num_seqs] = seqlen.
  *   - scale must be finite and > 0 (the configurations use 1/sqrt(D)).
  *   - head_dim must be 64 or 128 (bf16 paths) or 128 (fp8 path); other values
  *     return ATTN_ERR_UNSUPPORTED so the caller can fall back to a standard
@@ -51,9 +57,10 @@
  *     besides its loaded code. It is safe to call from several host threads.
  *   - Asynchrony: each call only enqueues kernels on `stream` (0 = the null
  *     stream). Results are valid once the stream reaches that point.
- *   - Errors: every argument check runs before any HIP call. A non-OK status
- *     means nothing was enqueued, except ATTN_ERR_HIP, which reports a failed
- *     launch (attn_last_hip_error() then gives the hipError_t value).
+ *   - Errors: every argument check runs before any HIP call (ATTN_VALIDATE's
+ *     copy comes after them). A non-OK status means nothing was enqueued,
+ *     except ATTN_ERR_HIP, which reports a failed copy or launch
+ *     (attn_last_hip_error() then gives the hipError_t value).
  *   - Determinism: no atomics; identical inputs give bitwise identical outputs.
  */
 #ifndef MI355ATTN_ATTN_H_

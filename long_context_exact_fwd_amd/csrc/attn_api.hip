@@ -1,9 +1,12 @@
 // C ABI of libmi355attn.so: argument checks, then kernel launches on the
-// caller's stream. Every check runs before any HIP call; see include/attn.h.
+// caller's stream. Every check runs before any HIP call (the optional
+// ATTN_VALIDATE copy of cu_seqlens runs after them and before any launch).
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+#include <vector>
 
 #include <hip/hip_runtime.h>
 
@@ -32,6 +35,24 @@ attn_status check_common(int batch, int hq, int hkv, int seqlen, int head_dim, i
   }
   // per-(b) slice of Q must be addressable with 32-bit row offsets times D
   if ((long long)seqlen * hq * head_dim > (long long)INT32_MAX) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+// ATTN_VALIDATE=1: copy cu_seqlens to the host (synchronising `stream`) and
+// check that it is a valid prefix-sum array before anything is launched.
+attn_status validate_cu(const int32_t* cu, int num_seqs, int seqlen, hipStream_t stream) {
+  const char* env = getenv("ATTN_VALIDATE");
+  if (cu == nullptr || env == nullptr || strcmp(env, "1") != 0) return ATTN_OK;
+  std::vector<int32_t> h((size_t)num_seqs + 1);
+  hipError_t e = hipMemcpyAsync(h.data(), cu, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return ATTN_ERR_HIP;
+  }
+  if (h[0] != 0 || h[num_seqs] != seqlen) return ATTN_ERR_INVALID_ARGUMENT;
+  for (int s = 0; s < num_seqs; ++s)
+    if (h[s + 1] <= h[s]) return ATTN_ERR_INVALID_ARGUMENT;
   return ATTN_OK;
 }
 
@@ -81,6 +102,8 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   attn_status st = check_common(batch, hq, hkv, seqlen, head_dim, causal, cu_seqlens, num_seqs, scale);
   if (st != ATTN_OK) return st;
   if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  st = validate_cu(cu_seqlens, num_seqs, seqlen, reinterpret_cast<hipStream_t>(stream));
+  if (st != ATTN_OK) return st;
   mi355attn::FwdParams p{};
   p.q = static_cast<const __bf16*>(q);
   p.k = static_cast<const __bf16*>(k);
@@ -122,6 +145,8 @@ attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const f
   attn_status st = check_common(batch, hq, hkv, seqlen, head_dim, causal, cu_seqlens, num_seqs, scale);
   if (st != ATTN_OK) return st;
   if (head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  st = validate_cu(cu_seqlens, num_seqs, seqlen, reinterpret_cast<hipStream_t>(stream));
+  if (st != ATTN_OK) return st;
   mi355attn::Fp8FwdParams p{};
   p.q = static_cast<const uint8_t*>(q8);
   p.k = static_cast<const uint8_t*>(k8);
@@ -163,6 +188,8 @@ attn_status attn_bwd_phases(unsigned phases, const void* q, const void* k, const
   attn_status st = check_common(batch, hq, hkv, seqlen, head_dim, causal, cu_seqlens, num_seqs, scale);
   if (st != ATTN_OK) return st;
   if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  st = validate_cu(cu_seqlens, num_seqs, seqlen, reinterpret_cast<hipStream_t>(stream));
+  if (st != ATTN_OK) return st;
   mi355attn::BwdParams p{};
   p.q = static_cast<const __bf16*>(q);
   p.k = static_cast<const __bf16*>(k);

@@ -239,8 +239,11 @@ __device__ __forceinline__ void segment_of(const int32_t* cu, int n, int seqlen,
     const int mid = (lo + hi) >> 1;
     if (cu[mid] <= i) lo = mid; else hi = mid;
   }
-  start = cu[lo];
-  end = cu[hi];
+  // Clamped so that 0 <= start <= i < end <= seqlen holds for any array:
+  // a no-op for valid prefix sums, and a malformed one still keeps every
+  // tile range inside the sequence.
+  start = max(0, min(cu[lo], i));
+  end = min(seqlen, max(cu[hi], i + 1));
 }
 
 __device__ __forceinline__ int wave_min(int x) {
