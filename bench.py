@@ -133,6 +133,17 @@ class Timer:
         n = len(self.ev)
         return {name: sum(e[j].elapsed_time(e[j + 1]) for e in self.ev) / n for j, name in enumerate(self.names)}
 
+    def step_stats_ms(self):
+        """Median, min and max over the timed steps of each phase and of the whole step (first to last event)."""
+        def stats(vals):
+            v = sorted(vals)
+            mid = len(v) // 2
+            med = v[mid] if len(v) % 2 else 0.5 * (v[mid - 1] + v[mid])
+            return {"median": round(med, 4), "min": round(v[0], 4), "max": round(v[-1], 4)}
+        out = {name: stats([e[j].elapsed_time(e[j + 1]) for e in self.ev]) for j, name in enumerate(self.names)}
+        out["step"] = stats([e[0].elapsed_time(e[-1]) for e in self.ev])
+        return out
+
 
 def run_steps(step, names, steps, warmup):
     """Warm up, then time exactly `steps` steps between two synchronisations; returns (ms/step, per-phase ms)."""
@@ -148,6 +159,7 @@ def run_steps(step, names, steps, warmup):
         step(tm, i)
     end.record()
     torch.cuda.synchronize()
+    run_steps.last_stats = tm.step_stats_ms()
     return start.elapsed_time(end) / steps, tm.per_phase_ms()
 
 
@@ -355,6 +367,7 @@ def main(argv=None) -> int:
     step, names = bf16_case(w, x, dev)
     t0 = time.perf_counter()
     ms_per_step, per = run_steps(step, names, a.steps, a.warmup)
+    step_stats = run_steps.last_stats
     wall = time.perf_counter() - t0
     print(f"bench: {a.steps} timed steps done", file=sys.stderr, flush=True)
 
@@ -423,6 +436,7 @@ def main(argv=None) -> int:
         },
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "phases_ms": {n: round(t, 4) for n, t in per.items()},
+        "per_step_ms": step_stats,
         "wall_s_timed": round(wall, 3),
         "roofline": roofline,
         "kernels": per_kernel,
