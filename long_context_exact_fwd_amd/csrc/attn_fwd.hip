@@ -259,6 +259,30 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_bf16_kernel(FwdParams
 #pragma unroll
       for (int db = 0; db < DB; ++db)
         acc[db] = mfma32(tr_read_pair(vs, voff[db] + 16 * u * D, 4 * D), pb[u], acc[db]);
+    if (!full) {
+      // Masked tiles hold every key of the rows that see fewer than 64, where
+      // a handful of probabilities carry the whole row and the bf16 rounding
+      // of P (2^-9 relative) would show in O. There the remainder
+      // p - bf16(p), itself rounded to bf16, goes through a second product,
+      // which leaves an error of about 2^-17 relative. Full tiles give every
+      // row at least 64 keys, and their rounding errors average out.
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float e[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x = fast_exp2(__builtin_fmaf(s_cur[kb][r], c, neg_m));
+          e[r] = x - (float)(__bf16)x;
+        }
+        pb[2 * kb] = pack_bf16(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+        pb[2 * kb + 1] = pack_bf16(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          acc[db] = mfma32(tr_read_pair(vs, voff[db] + 16 * u * D, 4 * D), pb[u], acc[db]);
+    }
     s_cur[0] = s_nxt[0];
     s_cur[1] = s_nxt[1];
     wait_dma();

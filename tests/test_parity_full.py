@@ -9,7 +9,7 @@ on the full GPU outputs: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i per kv
 head and segment (summed over the group's query heads).
 
 Tolerances as in the small-shape tests, applied to the sampled sets: O
-|err| <= max(1e-2, ulp) and rel-L2 <= 5e-3, LSE <= 1e-3, gradients rel-L2
+|err| <= max(1e-2, ulp / 2) and rel-L2 <= 5e-3, LSE <= 1e-3, gradients rel-L2
 <= 1e-2 per tensor, fp8 O rel-L2 <= 5e-2.
 """
 import numpy as np
@@ -24,11 +24,14 @@ pytestmark = pytest.mark.gpu
 
 
 def _sample_rows(w, cu, seed, count):
-    """Query/key rows: 0, 1, S-1, each segment's first and last row, plus seeded uniform rows."""
-    must = [0, 1, w.seqlen - 1]
-    if cu is not None:
-        for a, b in zip(cu[:-1], cu[1:]):
-            must += [int(a), int(b) - 1]
+    """Query/key rows: S-1, each segment's first 33 rows and last row, plus seeded uniform rows.
+
+    A row near its segment start sees few keys, so its output is an average of few V rows: the largest
+    |O| and the largest share of the bf16 rounding of P occur there."""
+    must = [w.seqlen - 1]
+    starts = [(int(a), int(b)) for a, b in zip(cu[:-1], cu[1:])] if cu is not None else [(0, w.seqlen)]
+    for a, b in starts:
+        must += list(range(a, min(a + 33, b))) + [b - 1]
     return si.sample_indices(seed, w.seqlen, count, must=must)
 
 
