@@ -92,29 +92,77 @@ def _traffic(kernel: str):
     return k.get("bytes_per_launch")
 
 
-def cpu_baseline(w, x, sample_len: int):
-    """Oracle (fp64, numpy) fwd+bwd of one kv group over a causal prefix of the same inputs."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, x, sample_len: int, single_len: int = 8192):
+    """Oracle (fp64, numpy) fwd+bwd of one kv group over a causal prefix of the same inputs.
+
+    Two timings: the group's G query heads over the first ``sample_len`` tokens with one worker thread
+    per core share (numpy's own BLAS threading pinned to 1 inside each worker), and one query head over
+    the first ``single_len`` tokens on a single thread. The oracle runs six contractions per visible
+    pair (scores, PV, dO V^T, dS K, dS^T Q, P^T dO), so its rate counts 12 D flops per pair; the GPU
+    metric's convention (14 D, which also counts the backward's recomputed scores) is given beside it.
+    The whole workload's time is extrapolated from each sample: cost is linear in (query head, visible
+    pair) at fixed D.
+    """
     import oracle
-    workers = min(16, len(os.sched_getaffinity(0)))
+    affinity = len(os.sched_getaffinity(0))
+    workers = min(16, affinity)
     L = min(sample_len, w.seqlen)
     g = w.hq // w.hkv
-    q = x.values("q")[:, :L, :g]
-    k = x.values("k")[:, :L, :1]
-    v = x.values("v")[:, :L, :1]
-    do = x.values("do")[:, :L, :g]
-    t0 = time.perf_counter()
-    oracle.attention_bwd_group(q, k, v, do, b=0, kv_head=0, causal=w.causal, scale=w.scale, workers=workers)
-    dt = time.perf_counter() - t0
-    flops = 14.0 * w.head_dim * _pairs(L, w.causal) * g
+    vals = {n: x.values(n) for n in ("q", "k", "v", "do")}
+
+    def run(nheads, length, nthreads):
+        q = vals["q"][:, :length, :nheads]
+        k = vals["k"][:, :length, :1]
+        v = vals["v"][:, :length, :1]
+        do = vals["do"][:, :length, :nheads]
+        t0 = time.perf_counter()
+        oracle.attention_bwd_group(q, k, v, do, b=0, kv_head=0, causal=w.causal, scale=w.scale, workers=nthreads)
+        return time.perf_counter() - t0
+
+    full_pairs = _pairs(w.seqlen, w.causal, x.cu_seqlens) * w.batch * w.hq
+    dt = run(g, L, workers)
+    pairs = _pairs(L, w.causal) * g
+    L1 = min(single_len, w.seqlen)
+    dt1 = run(1, L1, 1)
+    pairs1 = _pairs(L1, w.causal)
+    D = w.head_dim
     return {
-        "value": flops / dt / 1e12,
+        "value": 12.0 * D * pairs / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": workers,
         "kind": "oracle",
         "sample": (f"fp64 numpy oracle fwd+bwd (attention_bwd_group) of one kv group ({g} query heads) over the "
                    f"first {L} tokens of the same seeded inputs, causal; {dt:.1f} s on {workers} threads; "
-                   f"flops counted as for the GPU (14*D per visible pair)"),
-        "seconds": dt,
+                   f"flops counted as the oracle executes them (12*D per visible pair)"),
+        "seconds": round(dt, 6),
+        "threads": workers,
+        "host_cores": os.cpu_count(),
+        "affinity_cores": affinity,
+        "cpu_model": _cpu_model(),
+        "value_14d_convention": 14.0 * D * pairs / dt / 1e12,
+        "single_thread": {
+            "seconds": round(dt1, 6),
+            "value": 12.0 * D * pairs1 / dt1 / 1e12,
+            "unit": "TFLOP/s",
+            "sample": f"one query head over the first {L1} tokens, causal, 1 thread",
+        },
+        "extrapolated_full_workload_s": {
+            "note": "extrapolated, not measured: sample time x (visible pairs x query heads of the whole "
+                    "workload) / (those of the sample)",
+            "threads": round(dt * full_pairs / pairs, 2),
+            "single_thread": round(dt1 * full_pairs / pairs1, 1),
+        },
     }
 
 

@@ -46,3 +46,23 @@ def test_kernel_sources_exist_and_hash_stably():
         h = bench.kernel_source_hash(kernel)
         assert h == bench.kernel_source_hash(kernel) and len(h) >= 16
     assert set(bench.KERNEL_OF_PHASE.values()) <= set(bench.KERNEL_SOURCES)
+
+
+def test_cpu_baseline_fields_and_extrapolation():
+    """The CPU baseline reports threads and host cores apart, the CPU model, a single-thread time, the
+    flops the oracle executes (12 D per pair) and whole-workload times labelled as extrapolated."""
+    w = si.WORKLOADS["tiny"]
+    x = si.workload_inputs(w)
+    r = bench.cpu_baseline(w, x, sample_len=128, single_len=64)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s"
+    assert r["cores"] == r["threads"] >= 1 and r["host_cores"] >= 1 and r["affinity_cores"] >= 1
+    assert isinstance(r["cpu_model"], str) and r["cpu_model"]
+    g = w.hq // w.hkv
+    pairs = bench._pairs(128, w.causal) * g
+    assert abs(r["value"] - 12.0 * w.head_dim * pairs / r["seconds"] / 1e12) <= 0.01 * r["value"]
+    assert abs(r["value_14d_convention"] / r["value"] - 14.0 / 12.0) < 1e-9
+    full = bench._pairs(w.seqlen, w.causal) * w.batch * w.hq
+    ex = r["extrapolated_full_workload_s"]
+    assert "extrapolated" in ex["note"]
+    assert abs(ex["threads"] - r["seconds"] * full / pairs) <= 0.01 + 0.01 * ex["threads"]
+    assert r["single_thread"]["seconds"] > 0 and r["single_thread"]["value"] > 0
