@@ -79,7 +79,8 @@ typedef enum attn_status {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARGUMENT = 1, /* inconsistent shape, flag or pointer; nothing enqueued */
   ATTN_ERR_UNSUPPORTED = 2,      /* valid request the library has no kernel for; caller may fall back */
-  ATTN_ERR_HIP = 3               /* a kernel launch failed; see attn_last_hip_error() */
+  ATTN_ERR_HIP = 3,              /* a kernel launch failed; see attn_last_hip_error() */
+  ATTN_ERR_SCRATCH_TOO_SMALL = 4 /* attn_bwd_noalloc: the request needs more than its fixed scratch; nothing enqueued */
 } attn_status;
 
 /* Bytes of device workspace attn_fwd (and attn_fwd_fp8) can use for these sizes: 0 when the
@@ -174,6 +175,32 @@ attn_status attn_bwd_phases(unsigned phases, const void* q, const void* k, const
                             int batch, int hq, int hkv, int seqlen, int head_dim,
                             int causal, const int32_t* cu_seqlens, int num_seqs,
                             float scale, attn_stream_t stream);
+
+/* Backward without any allocation, for callers that cannot allocate device
+ * memory: code under HIP graph capture, allocation-free serving loops,
+ * harnesses that forbid hipMalloc. Same arguments, kernels and results as
+ * attn_bwd, minus the workspace: the workspace is a fixed array of
+ * ATTN_NOALLOC_SCRATCH_BYTES inside the library, one per device, held from
+ * the first call on a device until the process ends. The call makes no
+ * allocation of its own (its first call on a device looks up that device's
+ * copy of the array).
+ *   - The calling thread's current device must be the one `stream` runs on.
+ *   - When attn_bwd_workspace_bytes() for these sizes exceeds the scratch,
+ *     the backward runs without its head and key splits (the same kernels,
+ *     one workgroup per GQA group and per query block; results then differ
+ *     from attn_bwd's in rounding only). If even that needs more than the
+ *     scratch (8 * batch * hq * S64 bytes plus the work order), it returns
+ *     ATTN_ERR_SCRATCH_TOO_SMALL and enqueues nothing.
+ *   - Every call on a device shares that device's scratch and leaves its
+ *     contents behind (no call needs it cleared): calls that may run at the
+ *     same time on one device (other streams, other threads) race and must be
+ *     serialised by the caller. */
+#define ATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
+attn_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv,
+                             int batch, int hq, int hkv, int seqlen, int head_dim,
+                             int causal, const int32_t* cu_seqlens, int num_seqs,
+                             float scale, attn_stream_t stream);
 
 /* Ring-Attention step: merge one partial attention result into a running one.
  * Ring-Attention passes K/V blocks around a ring and accumulates partial

@@ -23,6 +23,8 @@ ATTN_OK = 0
 ATTN_ERR_INVALID_ARGUMENT = 1
 ATTN_ERR_UNSUPPORTED = 2
 ATTN_ERR_HIP = 3
+ATTN_ERR_SCRATCH_TOO_SMALL = 4
+NOALLOC_SCRATCH_BYTES = 64 << 20  # ATTN_NOALLOC_SCRATCH_BYTES in include/attn.h
 
 _lib = None
 
@@ -52,6 +54,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_bwd_phases.argtypes = [ctypes.c_uint, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i,
                                     f, st]
     lib.attn_bwd_phases.restype = i
+    lib.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, f, st]
+    lib.attn_bwd_noalloc.restype = i
     lib.attn_merge.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, st]
     lib.attn_merge.restype = i
     lib.attn_fwd_workspace_bytes.argtypes = [i, i, i, i, i]
@@ -68,7 +72,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
 
 
 EXPORTED = ("attn_fwd", "attn_fwd_workspace_bytes", "attn_fwd_fp8", "attn_bwd", "attn_bwd_phases",
-            "attn_bwd_workspace_bytes", "attn_merge", "attn_status_str", "attn_last_hip_error")
+            "attn_bwd_workspace_bytes", "attn_bwd_noalloc", "attn_merge", "attn_status_str", "attn_last_hip_error")
 
 BWD_DELTA, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 
@@ -242,4 +246,27 @@ def bwd(q, k, v, o, lse, do, *, causal: bool, cu_seqlens=None, scale: Optional[f
         _check(load_library().attn_bwd(*args), "attn_bwd")
     else:
         _check(load_library().attn_bwd_phases(int(phases), *args), "attn_bwd_phases")
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, lse, do, *, causal: bool, cu_seqlens=None, scale: Optional[float] = None, dq=None,
+                dk=None, dv=None):
+    """Backward through attn_bwd_noalloc: no workspace, the library's fixed scratch instead.
+
+    Returns (dq, dk, dv). The call itself allocates nothing on the device;
+    outputs not passed in are allocated here, by torch, before it.
+    """
+    import torch
+    _check_tensors(q, k, v, o, do, dtype=torch.bfloat16)
+    _check_tensors(lse, dtype=torch.float32)
+    B, S, Hq, Hkv, D, n = _shape(q, k, cu_seqlens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = dq if dq is not None else torch.empty_like(q)
+    dk = dk if dk is not None else torch.empty_like(k)
+    dv = dv if dv is not None else torch.empty_like(v)
+    st = load_library().attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                                         _ptr(dv), B, Hq, Hkv, S, D, int(bool(causal)), _ptr(cu_seqlens), n,
+                                         float(scale), _stream())
+    _check(st, "attn_bwd_noalloc")
     return dq, dk, dv

@@ -56,7 +56,11 @@ attn_status validate_cu(const int32_t* cu, int num_seqs, int seqlen, hipStream_t
   return ATTN_OK;
 }
 
-attn_status launch_result(hipError_t e) {
+}  // namespace
+
+namespace mi355attn {
+
+attn_status hip_result(hipError_t e) {
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return ATTN_ERR_HIP;
@@ -64,7 +68,64 @@ attn_status launch_result(hipError_t e) {
   return ATTN_OK;
 }
 
-}  // namespace
+attn_status bwd_check(unsigned phases, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, const void* workspace, bool need_workspace,
+                      int batch, int hq, int hkv, int seqlen, int head_dim, int causal, const int32_t* cu_seqlens,
+                      int num_seqs, float scale) {
+  if (phases == 0u || (phases & ~7u) != 0u) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_INVALID_ARGUMENT;
+  if (need_workspace && (!workspace || !aligned16(workspace))) return ATTN_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return ATTN_ERR_INVALID_ARGUMENT;
+  const attn_status st = check_common(batch, hq, hkv, seqlen, head_dim, causal, cu_seqlens, num_seqs, scale);
+  if (st != ATTN_OK) return st;
+  if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+attn_status bwd_launch(unsigned phases, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, void* workspace, int head_split, int key_split,
+                       int batch, int hq, int hkv, int seqlen, int head_dim, int causal, const int32_t* cu_seqlens,
+                       int num_seqs, float scale, hipStream_t stream) {
+  const attn_status st = validate_cu(cu_seqlens, num_seqs, seqlen, stream);
+  if (st != ATTN_OK) return st;
+  BwdParams p{};
+  p.q = static_cast<const __bf16*>(q);
+  p.k = static_cast<const __bf16*>(k);
+  p.v = static_cast<const __bf16*>(v);
+  p.o = static_cast<const __bf16*>(o);
+  p.lse = lse;
+  p.dout = static_cast<const __bf16*>(dout);
+  p.dq = static_cast<__bf16*>(dq);
+  p.dk = static_cast<__bf16*>(dk);
+  p.dv = static_cast<__bf16*>(dv);
+  p.stat_stride = stat_stride_for(seqlen);
+  char* ws = static_cast<char*>(workspace);
+  p.delta = reinterpret_cast<float*>(ws);
+  p.lse2 = p.delta + (size_t)batch * hq * p.stat_stride;
+  p.order = reinterpret_cast<int*>(ws + bwd_order_offset(batch, hq, seqlen));
+  p.head_split = head_split;
+  p.key_split = key_split;
+  p.part = head_split > 1 ? reinterpret_cast<float*>(ws + bwd_part_offset(batch, hq, seqlen, head_split, key_split))
+                          : nullptr;
+  p.dq_part = key_split > 1 ? reinterpret_cast<float*>(ws + bwd_dq_part_offset(batch, hq, hkv, seqlen, head_dim,
+                                                                               head_split, key_split))
+                            : nullptr;
+  p.cu_seqlens = cu_seqlens;
+  p.num_seqs = num_seqs;
+  p.batch = batch;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.seqlen = seqlen;
+  p.head_dim = head_dim;
+  p.causal = causal;
+  p.scale = scale;
+  p.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  return hip_result(run_bwd(p, phases, stream));
+}
+
+}  // namespace mi355attn
 
 extern "C" {
 
@@ -74,6 +135,7 @@ const char* attn_status_str(attn_status s) {
     case ATTN_ERR_INVALID_ARGUMENT: return "ATTN_ERR_INVALID_ARGUMENT";
     case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
     case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+    case ATTN_ERR_SCRATCH_TOO_SMALL: return "ATTN_ERR_SCRATCH_TOO_SMALL";
   }
   return "ATTN_ERR_UNKNOWN";
 }
@@ -128,7 +190,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
     p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                           mi355attn::fwd_part_lse_offset(batch, hq, seqlen, head_dim, ks));
   }
-  return launch_result(mi355attn::run_fwd_bf16(p, reinterpret_cast<hipStream_t>(stream)));
+  return mi355attn::hip_result(mi355attn::run_fwd_bf16(p, reinterpret_cast<hipStream_t>(stream)));
 }
 
 attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* descale_q,
@@ -173,58 +235,20 @@ attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const f
     p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                           mi355attn::fwd_part_lse_offset(batch, hq, seqlen, head_dim, ks));
   }
-  return launch_result(mi355attn::run_fwd_fp8(p, reinterpret_cast<hipStream_t>(stream)));
+  return mi355attn::hip_result(mi355attn::run_fwd_fp8(p, reinterpret_cast<hipStream_t>(stream)));
 }
 
 attn_status attn_bwd_phases(unsigned phases, const void* q, const void* k, const void* v, const void* o,
                             const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
                             int batch, int hq, int hkv, int seqlen, int head_dim, int causal,
                             const int32_t* cu_seqlens, int num_seqs, float scale, attn_stream_t stream) {
-  if (phases == 0u || (phases & ~7u) != 0u) return ATTN_ERR_INVALID_ARGUMENT;
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return ATTN_ERR_INVALID_ARGUMENT;
-  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, workspace};
-  for (const void* ptr : ptrs)
-    if (!aligned16(ptr)) return ATTN_ERR_INVALID_ARGUMENT;
-  attn_status st = check_common(batch, hq, hkv, seqlen, head_dim, causal, cu_seqlens, num_seqs, scale);
+  const attn_status st = mi355attn::bwd_check(phases, q, k, v, o, lse, dout, dq, dk, dv, workspace, true, batch, hq,
+                                              hkv, seqlen, head_dim, causal, cu_seqlens, num_seqs, scale);
   if (st != ATTN_OK) return st;
-  if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
-  st = validate_cu(cu_seqlens, num_seqs, seqlen, reinterpret_cast<hipStream_t>(stream));
-  if (st != ATTN_OK) return st;
-  mi355attn::BwdParams p{};
-  p.q = static_cast<const __bf16*>(q);
-  p.k = static_cast<const __bf16*>(k);
-  p.v = static_cast<const __bf16*>(v);
-  p.o = static_cast<const __bf16*>(o);
-  p.lse = lse;
-  p.dout = static_cast<const __bf16*>(dout);
-  p.dq = static_cast<__bf16*>(dq);
-  p.dk = static_cast<__bf16*>(dk);
-  p.dv = static_cast<__bf16*>(dv);
-  p.stat_stride = mi355attn::stat_stride_for(seqlen);
-  p.delta = static_cast<float*>(workspace);
-  p.lse2 = p.delta + (size_t)batch * hq * p.stat_stride;
-  p.order = reinterpret_cast<int*>(static_cast<char*>(workspace) + mi355attn::bwd_order_offset(batch, hq, seqlen));
-  p.head_split = mi355attn::bwd_head_split(batch, hq, hkv, seqlen);
-  p.key_split = mi355attn::bwd_key_split(batch, hq, seqlen);
-  p.part = p.head_split > 1
-               ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                          mi355attn::bwd_part_offset(batch, hq, hkv, seqlen))
-               : nullptr;
-  p.dq_part = p.key_split > 1
-                  ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                             mi355attn::bwd_dq_part_offset(batch, hq, hkv, seqlen, head_dim))
-                  : nullptr;
-  p.cu_seqlens = cu_seqlens;
-  p.num_seqs = num_seqs;
-  p.batch = batch;
-  p.hq = hq;
-  p.hkv = hkv;
-  p.seqlen = seqlen;
-  p.head_dim = head_dim;
-  p.causal = causal;
-  p.scale = scale;
-  p.scale_log2e = (float)((double)scale * 1.4426950408889634);
-  return launch_result(mi355attn::run_bwd(p, phases, reinterpret_cast<hipStream_t>(stream)));
+  return mi355attn::bwd_launch(phases, q, k, v, o, lse, dout, dq, dk, dv, workspace,
+                               mi355attn::bwd_head_split(batch, hq, hkv, seqlen),
+                               mi355attn::bwd_key_split(batch, hq, seqlen), batch, hq, hkv, seqlen, head_dim, causal,
+                               cu_seqlens, num_seqs, scale, reinterpret_cast<hipStream_t>(stream));
 }
 
 attn_status attn_merge(float* o_acc, float* lse_acc, const void* o_part, const float* lse_part, void* o_out,
@@ -248,7 +272,7 @@ attn_status attn_merge(float* o_acc, float* lse_acc, const void* o_part, const f
   p.heads = heads;
   p.head_dim = head_dim;
   p.accumulate = accumulate;
-  return launch_result(mi355attn::run_merge(p, reinterpret_cast<hipStream_t>(stream)));
+  return mi355attn::hip_result(mi355attn::run_merge(p, reinterpret_cast<hipStream_t>(stream)));
 }
 
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/attn.h"
+
 namespace mi355attn {
 
 struct FwdParams {
@@ -100,27 +102,30 @@ inline int bwd_key_split(int batch, int hq, int seqlen) {
   return (int)(want < 4 ? want : 4);
 }
 // Workspace layout, in bytes from its start: Delta and LSE*log2(e) (fp32
-// [B, Hq, S64] each), the work order (int32, NB * (head split + key split)
-// with NB = ceil(S / 128)), then, each 256-byte aligned, the fp32 partial
-// dK/dV and the fp32 partial dQ when their splits are above 1.
+// [B, Hq, S64] each), the work order (int32, NB * (hs + ks) with
+// NB = ceil(S / 128), hs and ks the head and key splits), then, each 256-byte
+// aligned, the fp32 partial dK/dV and the fp32 partial dQ when their splits
+// are above 1.
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 inline size_t bwd_order_offset(int batch, int hq, int seqlen) {
   return (size_t)8 * batch * hq * stat_stride_for(seqlen);
 }
-inline size_t bwd_part_offset(int batch, int hq, int hkv, int seqlen) {
+inline size_t bwd_part_offset(int batch, int hq, int seqlen, int hs, int ks) {
   const size_t nblk = ((size_t)seqlen + 127) / 128;
-  const size_t entries = nblk * (bwd_head_split(batch, hq, hkv, seqlen) + bwd_key_split(batch, hq, seqlen));
-  return align256(bwd_order_offset(batch, hq, seqlen) + 4 * entries);
+  return align256(bwd_order_offset(batch, hq, seqlen) + 4 * nblk * (size_t)(hs + ks));
 }
-inline size_t bwd_dq_part_offset(int batch, int hq, int hkv, int seqlen, int head_dim) {
-  const int ns = bwd_head_split(batch, hq, hkv, seqlen);
-  const size_t part = ns > 1 ? (size_t)8 * ns * batch * seqlen * hkv * head_dim : 0;
-  return align256(bwd_part_offset(batch, hq, hkv, seqlen) + part);
+inline size_t bwd_dq_part_offset(int batch, int hq, int hkv, int seqlen, int head_dim, int hs, int ks) {
+  const size_t part = hs > 1 ? (size_t)8 * hs * batch * seqlen * hkv * head_dim : 0;
+  return align256(bwd_part_offset(batch, hq, seqlen, hs, ks) + part);
 }
+inline size_t bwd_workspace_size(int batch, int hq, int hkv, int seqlen, int head_dim, int hs, int ks) {
+  const size_t part = ks > 1 ? (size_t)4 * ks * batch * seqlen * hq * head_dim : 0;
+  return bwd_dq_part_offset(batch, hq, hkv, seqlen, head_dim, hs, ks) + part;
+}
+// ... with the splits chosen from the sizes
 inline size_t bwd_workspace_size(int batch, int hq, int hkv, int seqlen, int head_dim) {
-  const int nk = bwd_key_split(batch, hq, seqlen);
-  const size_t part = nk > 1 ? (size_t)4 * nk * batch * seqlen * hq * head_dim : 0;
-  return bwd_dq_part_offset(batch, hq, hkv, seqlen, head_dim) + part;
+  return bwd_workspace_size(batch, hq, hkv, seqlen, head_dim, bwd_head_split(batch, hq, hkv, seqlen),
+                            bwd_key_split(batch, hq, seqlen));
 }
 
 // Forward key split. The forward runs one workgroup per (b, query head,
@@ -175,5 +180,23 @@ hipError_t run_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream);
 constexpr unsigned kBwdDelta = 1u, kBwdDkDv = 2u, kBwdDq = 4u;
 hipError_t run_bwd(const BwdParams& p, unsigned phases, hipStream_t stream);
 hipError_t run_merge(const MergeParams& p, hipStream_t stream);
+
+// ATTN_OK for hipSuccess; otherwise records e for attn_last_hip_error() and
+// returns ATTN_ERR_HIP.
+attn_status hip_result(hipError_t e);
+
+// Argument checks shared by the backward entry points (no HIP call); a
+// workspace pointer is required only when need_workspace is set.
+attn_status bwd_check(unsigned phases, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, const void* workspace, bool need_workspace,
+                      int batch, int hq, int hkv, int seqlen, int head_dim, int causal, const int32_t* cu_seqlens,
+                      int num_seqs, float scale);
+// Validation of cu_seqlens under ATTN_VALIDATE=1 (a copy and a sync), then
+// the backward kernels with the given splits on a workspace laid out for
+// them. Arguments must have passed bwd_check.
+attn_status bwd_launch(unsigned phases, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, void* workspace, int head_split, int key_split,
+                       int batch, int hq, int hkv, int seqlen, int head_dim, int causal, const int32_t* cu_seqlens,
+                       int num_seqs, float scale, hipStream_t stream);
 
 }  // namespace mi355attn

@@ -225,3 +225,29 @@ def test_bwd_phases_arguments_checked_like_bwd(kw):
     for ph in (lca.BWD_DELTA, lca.BWD_DKDV, lca.BWD_DQ, lca.BWD_ALL):
         assert _phases(ph, **kw) == lca.ATTN_ERR_INVALID_ARGUMENT
     assert _phases(lca.BWD_ALL, D=96) == lca.ATTN_ERR_UNSUPPORTED
+
+
+def _noalloc(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, Hq=4, Hkv=2, S=128, D=128, causal=1,
+             cu=NULL, n=0, scale=0.088)
+    a.update(kw)
+    return lca.load_library().attn_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                                               a["dv"], a["B"], a["Hq"], a["Hkv"], a["S"], a["D"], a["causal"],
+                                               a["cu"], a["n"], a["scale"], S0)
+
+
+@pytest.mark.parametrize("kw", BAD + [dict(do=NULL), dict(dk=PM)])
+def test_noalloc_arguments_checked_like_bwd(kw):
+    assert _noalloc(**kw) == lca.ATTN_ERR_INVALID_ARGUMENT
+
+
+def test_noalloc_size_limits():
+    """Requests whose per-row statistics alone (8 * B * Hq * S64 bytes) exceed the fixed scratch are
+    refused with ATTN_ERR_SCRATCH_TOO_SMALL before any HIP call; head dims and the 2^31 limit as bwd."""
+    lib = lca.load_library()
+    assert lib.attn_status_str(lca.ATTN_ERR_SCRATCH_TOO_SMALL) == b"ATTN_ERR_SCRATCH_TOO_SMALL"
+    assert _noalloc(B=1, Hq=64, Hkv=8, S=140000, D=128) == lca.ATTN_ERR_SCRATCH_TOO_SMALL
+    assert _noalloc(B=8, Hq=32, Hkv=8, S=33000, D=64) == lca.ATTN_ERR_SCRATCH_TOO_SMALL
+    assert 8 * 1 * 64 * 131072 >= lca.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(D=96) == lca.ATTN_ERR_UNSUPPORTED
+    assert _noalloc(S=1 << 20, Hq=16, Hkv=4, D=128) == lca.ATTN_ERR_UNSUPPORTED
