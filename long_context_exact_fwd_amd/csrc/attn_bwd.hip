@@ -395,20 +395,52 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // dV^T += dO^T P (role A) or dK^T += Q^T dS (role B) for one step's tile:
+  // the transposed fragments of query step u + 1 are read before the MFMAs
+  // of step u.
+  auto tr_times = [&](const __bf16* tile, const bf16x8 (&pk)[4]) {
+    bf16x8 fr[2][DB];
+#pragma unroll
+    for (int d = 0; d < DB; ++d) fr[0][d] = tr_read2(tile, trlo[d], trhi[d]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (u < 3) {
+#pragma unroll
+        for (int d = 0; d < DB; ++d)
+          fr[(u + 1) & 1][d] = tr_read2(tile, trlo[d] + 16 * (u + 1) * D, trhi[d] + 16 * (u + 1) * D);
+      }
+#pragma unroll
+      for (int d = 0; d < DB; ++d) acc[d] = mfma32(fr[u & 1][d], pk[u], acc[d]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // The two waves of a SIMD (A and B of one pair) alternate between the
+  // matrix pipe and the vector ALU within each barrier step:
+  //   A: S(j) and dV^T += dO(j-1)^T P(j-1)  [MFMA]  then P(j) = exp2(...)    [VALU]
+  //   B: dS(j-1) = P(j-1) (dP(j-1) - Delta) [VALU]  then dK^T += Q(j-1)^T dS(j-1), dP(j) [MFMA]
+  // so while one wave computes exponentials or dS the other keeps the matrix
+  // pipe busy. A carries P(j) and B carries dP(j) in registers into the next
+  // step; B reads P(j-1) from the exchange slot A wrote in step j - 1.
   if (role == 0) {
     int cur_g = g_lo, cur_ti = tile_end - 1;
+    bf16x8 pk[4];  // P of the previous step (bf16)
     auto body_a = [&](int step, auto r_c) {
       constexpr int r = decltype(r_c)::value;
       prefetch(step, r_c);
+      __bf16 *qs, *gs;
+      float* st;
+      slot_ptrs(std::integral_constant<int, r % 3>{}, qs, gs, st);
+      f32x16 sc[2] = {f32x16{}, f32x16{}};
+      if (step < nsteps) rows_times_x(qs, sc);
+      if (step > 0) {
+        __bf16 *qp, *gp;
+        float* sp;
+        slot_ptrs(std::integral_constant<int, (r + 2) % 3>{}, qp, gp, sp);
+        tr_times(gp, pk);
+      }
       if (step < nsteps) {
         const int t0 = cur_ti * kQT;
         const bool full = (t0 >= lo_max) && (t0 + kQT <= hi_min);
-        __bf16 *qs, *gs;
-        float* st;
-        slot_ptrs(std::integral_constant<int, r % 3>{}, qs, gs, st);
-        f32x16 sc[2] = {f32x16{}, f32x16{}};
-        rows_times_x(qs, sc);
-        bf16x8 pb[4];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           const f32x16& s = sc[qb];
@@ -430,26 +462,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
               pr[rr] = (qq < qlo || qq >= qhi) ? 0.f : pr[rr];
             }
           }
-          pb[2 * qb] = pack_bf16(pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]);
-          pb[2 * qb + 1] = pack_bf16(pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]);
-          xchg[r % 2][pair][qb][0][lane] = __builtin_bit_cast(u32x4, pb[2 * qb]);
-          xchg[r % 2][pair][qb][1][lane] = __builtin_bit_cast(u32x4, pb[2 * qb + 1]);
-        }
-        // dV^T += dO^T P; the fragments of query step u + 1 are read before
-        // the MFMAs of step u.
-        bf16x8 fr[2][DB];
-#pragma unroll
-        for (int d = 0; d < DB; ++d) fr[0][d] = tr_read2(gs, trlo[d], trhi[d]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (u < 3) {
-#pragma unroll
-            for (int d = 0; d < DB; ++d)
-              fr[(u + 1) & 1][d] = tr_read2(gs, trlo[d] + 16 * (u + 1) * D, trhi[d] + 16 * (u + 1) * D);
-          }
-#pragma unroll
-          for (int d = 0; d < DB; ++d) acc[d] = mfma32(fr[u & 1][d], pb[u], acc[d]);
-          __builtin_amdgcn_sched_barrier(0);
+          pk[2 * qb] = pack_bf16(pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]);
+          pk[2 * qb + 1] = pack_bf16(pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]);
+          xchg[r % 2][pair][qb][0][lane] = __builtin_bit_cast(u32x4, pk[2 * qb]);
+          xchg[r % 2][pair][qb][1][lane] = __builtin_bit_cast(u32x4, pk[2 * qb + 1]);
         }
         advance(cur_g, cur_ti);
       }
@@ -458,6 +474,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
     };
     steps6(body_a);
   } else {
+    f32x16 dp[2];  // dP of the previous step
     auto body_b = [&](int step, auto r_c) {
       constexpr int r = decltype(r_c)::value;
       prefetch(step, r_c);
@@ -467,8 +484,6 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
         float* st;
         slot_ptrs(std::integral_constant<int, (r + 2) % 3>{}, qs, gs, st);
         constexpr int xs = (r + 1) % 2;
-        f32x16 dp[2] = {f32x16{}, f32x16{}};
-        rows_times_x(gs, dp);
         bf16x8 db[4];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
@@ -493,21 +508,15 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
           db[2 * qb] = pack_bf16(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
           db[2 * qb + 1] = pack_bf16(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
         }
-        // dK^T += Q^T dS, fragments read one query step ahead
-        bf16x8 fr[2][DB];
-#pragma unroll
-        for (int d = 0; d < DB; ++d) fr[0][d] = tr_read2(qs, trlo[d], trhi[d]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (u < 3) {
-#pragma unroll
-            for (int d = 0; d < DB; ++d)
-              fr[(u + 1) & 1][d] = tr_read2(qs, trlo[d] + 16 * (u + 1) * D, trhi[d] + 16 * (u + 1) * D);
-          }
-#pragma unroll
-          for (int d = 0; d < DB; ++d) acc[d] = mfma32(fr[u & 1][d], db[u], acc[d]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        tr_times(qs, db);
+      }
+      if (step < nsteps) {
+        __bf16 *qs, *gs;
+        float* st;
+        slot_ptrs(std::integral_constant<int, r % 3>{}, qs, gs, st);
+        dp[0] = f32x16{};
+        dp[1] = f32x16{};
+        rows_times_x(gs, dp);
       }
       wait_dma();
       __syncthreads();
