@@ -56,6 +56,7 @@ def _pairs(seqlen: int, causal: bool, cu=None) -> float:
 KERNEL_SOURCES = {
     "attn_fwd_bf16_kernel": ("attn_fwd.hip", "attn_device.h", "attn_internal.h"),
     "attn_fwd_combine_kernel": ("attn_fwd.hip", "attn_device.h", "attn_internal.h"),
+    "attn_fwd_fewkeys_kernel": ("attn_fwd.hip", "attn_device.h", "attn_internal.h"),
     "attn_bwd_dkdv_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h"),
     "attn_bwd_dq_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h"),
     "attn_bwd_delta_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h"),

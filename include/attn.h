@@ -105,7 +105,10 @@ size_t attn_fwd_workspace_bytes(int batch, int hq, int hkv, int seqlen, int head
  * attn_fwd_workspace_bytes() sizes above 0 run the key split: each share
  * writes its partial output, and a second kernel combines the shares
  * (O = sum of the shares' O weighted by 2^(their m + log2 l) over the total).
- * Rounding: O is accumulated in fp32 and rounded to bf16 (nearest-even).
+ * Rounding: O is accumulated in fp32 and rounded to bf16 (nearest-even). The
+ * probabilities enter the PV product rounded to bf16 (the row sum uses them
+ * unrounded), except in rows that see fewer than 64 keys: a last small kernel
+ * recomputes those rows in fp32 with unrounded probabilities.
  */
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
                      int batch, int hq, int hkv, int seqlen, int head_dim,

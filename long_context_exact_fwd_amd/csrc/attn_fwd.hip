@@ -25,6 +25,8 @@
 //   * Tiles partly (or wholly) outside a wave's visible keys are masked per
 //     element. Every LDS address is a per-lane base computed once plus a
 //     compile-time offset, and every per-tile branch is scalar.
+//   * Rows that see fewer than 64 keys are recomputed afterwards in fp32 by
+//     attn_fwd_fewkeys_kernel.
 //   * Key split (grids too small to fill the GPU, chosen on the host): the key
 //     tiles of a query block are shared over key_split workgroups, which write
 //     fp32 partial results; attn_fwd_combine_kernel merges them.
@@ -259,30 +261,6 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_bf16_kernel(FwdParams
 #pragma unroll
       for (int db = 0; db < DB; ++db)
         acc[db] = mfma32(tr_read_pair(vs, voff[db] + 16 * u * D, 4 * D), pb[u], acc[db]);
-    if (!full) {
-      // Masked tiles hold every key of the rows that see fewer than 64, where
-      // a handful of probabilities carry the whole row and the bf16 rounding
-      // of P (2^-9 relative) would show in O. There the remainder
-      // p - bf16(p), itself rounded to bf16, goes through a second product,
-      // which leaves an error of about 2^-17 relative. Full tiles give every
-      // row at least 64 keys, and their rounding errors average out.
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float e[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float x = fast_exp2(__builtin_fmaf(s_cur[kb][r], c, neg_m));
-          e[r] = x - (float)(__bf16)x;
-        }
-        pb[2 * kb] = pack_bf16(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-        pb[2 * kb + 1] = pack_bf16(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          acc[db] = mfma32(tr_read_pair(vs, voff[db] + 16 * u * D, 4 * D), pb[u], acc[db]);
-    }
     s_cur[0] = s_nxt[0];
     s_cur[1] = s_nxt[1];
     wait_dma();
@@ -383,6 +361,101 @@ __global__ __launch_bounds__(256) void attn_fwd_combine_kernel(FwdParams p) {
   if (sub == 0) p.lse[li] = tot > 0.f ? (m + __log2f(tot)) * kLn2 : -INFINITY;
 }
 
+// ---------------------------------------------------------------------------
+// Rows that see fewer than 64 keys (the first 63 rows of every causal segment,
+// and every row of a non-causal segment shorter than 64) carry their whole
+// softmax on a handful of probabilities, so the bf16 rounding of P in the
+// tiled kernel (2^-9 relative) shows in their O. This kernel recomputes those
+// rows exactly as the definition reads, in fp32 with unrounded
+// probabilities, and overwrites their O and LSE: scores s_j = scale q . k_j,
+// an online maximum and normaliser over the row's keys, O = sum_j p_j v_j / l,
+// LSE = m + ln l.
+// Workgroup (4-row block of a segment, h_q, b): the segment's first keys (at
+// most 63) go to LDS, then one wave per row: lane j computes the score of key
+// j, the wave takes the exact maximum and sum, and lane t accumulates
+// O[d] = sum_j p_j v_j[d] for d = t, t + 64.
+// ---------------------------------------------------------------------------
+constexpr int kFewKeys = 64;    // rows with fewer visible keys are recomputed
+constexpr int kFewRowsPerWg = 4;  // one wave per row
+constexpr int kFewBlocks = (kFewKeys + kFewRowsPerWg - 1) / kFewRowsPerWg;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_fwd_fewkeys_kernel(FwdParams p) {
+  constexpr int C = D / 8;  // 16-byte chunks per row
+  // K rows with chunk c of row j stored at chunk (c + j) % C, so that 64 lanes
+  // reading one chunk each of 64 different rows hit different banks
+  __shared__ __attribute__((aligned(16))) __bf16 ks[kFewKeys - 1][D];
+  __shared__ __attribute__((aligned(16))) __bf16 vs[kFewKeys - 1][D];
+  __shared__ __attribute__((aligned(16))) float qs[kFewRowsPerWg][D];
+  const int hq = blockIdx.y;
+  const int b = blockIdx.z;
+  const int seg = (int)blockIdx.x / kFewBlocks;
+  const int rblk = (int)blockIdx.x % kFewBlocks;
+  int s0 = 0, s1 = p.seqlen;
+  if (p.cu_seqlens != nullptr) {
+    // clamped to [0, seqlen): a malformed array gives meaningless rows, never a stray address
+    s0 = max(0, min(p.cu_seqlens[seg], p.seqlen));
+    s1 = max(s0, min(p.cu_seqlens[seg + 1], p.seqlen));
+  }
+  const int len = s1 - s0;
+  // these rows see keys [s0, s0 + nrows) only
+  const int nrows = CAUSAL ? min(kFewKeys - 1, len) : (len < kFewKeys ? len : 0);
+  if (rblk * kFewRowsPerWg >= nrows) return;  // uniform over the workgroup
+  const int hk = hq / (p.hq / p.hkv);
+  const size_t q_stride = (size_t)p.hq * D, kv_stride = (size_t)p.hkv * D;
+  const __bf16* kg = p.k + ((size_t)b * p.seqlen + s0) * kv_stride + hk * D;
+  const __bf16* vg = p.v + ((size_t)b * p.seqlen + s0) * kv_stride + hk * D;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < nrows * C; e += 256) {
+    const int j = e / C, c = e % C;
+    *reinterpret_cast<u32x4*>(&ks[j][((c + j) % C) * 8]) = load16(kg + (size_t)j * kv_stride + c * 8);
+    *reinterpret_cast<u32x4*>(&vs[j][c * 8]) = load16(vg + (size_t)j * kv_stride + c * 8);
+  }
+  for (int e = tid; e < kFewRowsPerWg * D; e += 256) {
+    const int w = e / D, d = e % D;
+    const int rl = min(rblk * kFewRowsPerWg + w, nrows - 1);
+    qs[w][d] = (float)p.q[((size_t)b * p.seqlen + s0 + rl) * q_stride + hq * D + d];
+  }
+  __syncthreads();
+  const int wave = tid >> 6, lane = tid & 63;
+  const int row_local = rblk * kFewRowsPerWg + wave;
+  if (row_local >= nrows) return;  // whole waves leave
+  const int r = s0 + row_local;
+  const int nk = CAUSAL ? row_local + 1 : nrows;  // keys s0 .. s0 + nk - 1
+  float sc = -INFINITY;
+  if (lane < nk) {
+    float dot = 0.f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const bf16x8 kv = *reinterpret_cast<const bf16x8*>(&ks[lane][((c + lane) % C) * 8]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(qs[wave][c * 8 + e], (float)kv[e], dot);
+    }
+    sc = dot * p.scale;
+  }
+  float m = sc;
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) m = fmaxf(m, __shfl_xor(m, x));
+  const float pj = lane < nk ? expf(sc - m) : 0.f;
+  float l = pj;
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) l += __shfl_xor(l, x);
+  constexpr int DL = D / 64;  // d per lane
+  float o[DL];
+#pragma unroll
+  for (int i = 0; i < DL; ++i) o[i] = 0.f;
+  for (int j = 0; j < nk; ++j) {
+    const float pb = __shfl(pj, j);
+#pragma unroll
+    for (int i = 0; i < DL; ++i) o[i] = __builtin_fmaf(pb, (float)vs[j][lane + 64 * i], o[i]);
+  }
+  const float inv = 1.0f / l;
+  __bf16* orow = p.o + ((size_t)b * p.seqlen + r) * q_stride + hq * D;
+#pragma unroll
+  for (int i = 0; i < DL; ++i) orow[lane + 64 * i] = (__bf16)(o[i] * inv);
+  if (lane == 0) p.lse[((size_t)b * p.hq + hq) * p.seqlen + r] = m + logf(l);
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
   FwdParams q = p;
@@ -391,8 +464,19 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
   dim3 grid(p.batch * p.hq, q.num_qblk * q.key_split);
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), grid, dim3(kWaves * 64), 0, stream, q);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || q.key_split == 1) return e;
-  return run_fwd_combine(q, stream);
+  if (e != hipSuccess) return e;
+  if (q.key_split > 1) {
+    e = run_fwd_combine(q, stream);
+    if (e != hipSuccess) return e;
+  }
+  // rows with fewer than 64 visible keys: none for a dense non-causal call with S >= 64
+  if (CAUSAL || q.cu_seqlens != nullptr || q.seqlen < kFewKeys) {
+    const int nseg = q.cu_seqlens != nullptr ? q.num_seqs : 1;
+    const dim3 fgrid((unsigned)nseg * kFewBlocks, q.hq, q.batch);
+    hipLaunchKernelGGL((attn_fwd_fewkeys_kernel<D, CAUSAL>), fgrid, dim3(256), 0, stream, q);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 }  // namespace
