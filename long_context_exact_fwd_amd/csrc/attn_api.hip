@@ -60,6 +60,12 @@ attn_status validate_cu(const int32_t* cu, int num_seqs, int seqlen, hipStream_t
 
 namespace mi355attn {
 
+int fwd_block_waves_env() {
+  const char* env = getenv("ATTN_FWD_WAVES");
+  if (env == nullptr) return 0;
+  return atoi(env);
+}
+
 attn_status hip_result(hipError_t e) {
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;

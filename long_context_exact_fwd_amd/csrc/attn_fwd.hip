@@ -9,7 +9,9 @@
 //
 // Work split: one workgroup of 4 waves per (b, h_q, 128 queries), two
 // workgroups per CU (two waves per SIMD, so one wave's softmax overlaps the
-// other's MFMAs; at most 256 VGPRs each).
+// other's MFMAs; at most 256 VGPRs each); or, for long unpacked sequences,
+// 8 waves per (b, h_q, 256 queries), one workgroup per CU sharing each K/V
+// tile (fwd_block_waves()).
 //   * Each wave owns 32 queries. Its Q slice sits in VGPRs as the B operand of
 //     S^T = K Q^T, so every lane owns one query column and the row statistics
 //     need only one exchange between the two lane halves (v_permlane32_swap).
@@ -37,12 +39,15 @@ namespace mi355attn {
 
 namespace {
 
-constexpr int kBN = 64;    // keys per tile
-constexpr int kWaves = 4;  // waves per workgroup
-constexpr int kBM = 32 * kWaves;
+constexpr int kBN = 64;  // keys per tile
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_bf16_kernel(FwdParams p) {
+// WAVES waves of 32 queries per workgroup: 4 (128-query blocks, two
+// workgroups per CU) or 8 (256-query blocks, one workgroup per CU, so each
+// K/V tile is copied into LDS once per CU); fwd_block_waves() picks one.
+template <int D, bool CAUSAL, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void attn_fwd_bf16_kernel(FwdParams p) {
+  constexpr int kWaves = WAVES;
+  constexpr int kBM = 32 * kWaves;
   constexpr int KS = D / 16;     // k-steps of the score product
   constexpr int DB = D / 32;     // 32-wide d blocks of the output
   constexpr int TILE = kBN * D;  // elements of one K or V tile
@@ -459,10 +464,15 @@ __global__ __launch_bounds__(256) void attn_fwd_fewkeys_kernel(FwdParams p) {
 template <int D, bool CAUSAL>
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
   FwdParams q = p;
-  q.num_qblk = (p.seqlen + kBM - 1) / kBM;
   if (q.key_split < 1 || q.part_o == nullptr || q.part_lse == nullptr) q.key_split = 1;
+  const int waves = q.key_split > 1 ? 4 : fwd_block_waves(q.seqlen, D, q.causal, q.cu_seqlens != nullptr);
+  q.num_qblk = (p.seqlen + 32 * waves - 1) / (32 * waves);
   dim3 grid(p.batch * p.hq, q.num_qblk * q.key_split);
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), grid, dim3(kWaves * 64), 0, stream, q);
+  if (waves == 8) {
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 8>), grid, dim3(8 * 64), 0, stream, q);
+  } else {
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 4>), grid, dim3(4 * 64), 0, stream, q);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (q.key_split > 1) {

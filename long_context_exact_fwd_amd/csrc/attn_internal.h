@@ -152,6 +152,29 @@ inline int fwd_key_split(int batch, int hq, int seqlen) {
   if (ks > by_len) ks = by_len;
   return ks < 1 ? 1 : (int)ks;
 }
+// Forward block geometry, picked from the sizes (the tiling matched to the
+// sequence length of the FA-3 paragraph of the FlashAttention page): 4 waves
+// of 32 queries (128-query blocks, two workgroups per CU) or 8 waves
+// (256-query blocks, one per CU, each K/V tile copied into LDS once per CU
+// instead of twice). Both give bitwise the same results. Taller blocks cost
+// more masked work on the causal diagonal and at segment boundaries and fill
+// the CUs less evenly; with D = 64 the 4-wave kernel (161 VGPRs) also runs
+// three waves per SIMD against two. Measured on MI355X (B * S = 32768 tokens,
+// Hq = 28, Hkv = 4), time of 8 waves over 4:
+//   D = 128 causal:     S = 2048 1.11, 4096 0.98, 8192 1.01, 16384 1.00, 32768 0.99
+//   D = 128 non-causal: S = 2048 0.99, 4096 0.92, 8192 0.97, 16384 0.98, 32768 0.97
+//   D = 64:             1.10 - 1.35 at every S, both masks
+//   packed (Hq 14, Hkv 2, seed-4 lengths): D = 128 1.07, D = 64 1.20
+// so 8 waves are taken for D = 128 without packing from S = 16384 (causal) or
+// S = 4096 (non-causal). The environment variable ATTN_FWD_WAVES=4 or 8
+// overrides the choice (for tests and tuning).
+int fwd_block_waves_env();  // 0 when unset
+inline int fwd_block_waves(int seqlen, int head_dim, int causal, bool packed) {
+  const int forced = fwd_block_waves_env();
+  if (forced == 4 || forced == 8) return forced;
+  if (packed || head_dim != 128) return 4;
+  return seqlen >= (causal ? 16384 : 4096) ? 8 : 4;
+}
 // Workspace layout: partial O, then (256-byte aligned) the partial row statistics.
 inline size_t fwd_part_lse_offset(int batch, int hq, int seqlen, int head_dim, int ks) {
   return align256((size_t)4 * ks * batch * seqlen * hq * head_dim);

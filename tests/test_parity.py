@@ -142,3 +142,36 @@ def test_outputs_are_bitwise_deterministic():
             runs.append([t.clone() for t in (o, lse, dq, dk, dv)])
         for a, b in zip(*runs):
             assert torch.equal(a, b)
+
+
+GEOMETRY = [
+    # B, Hq, Hkv, S, D, causal, lengths: 128-query (4 waves) and 256-query (8 waves) forward blocks
+    (1, 4, 2, 1000, 128, True, None),
+    (2, 3, 1, 700, 64, False, None),
+    (1, 7, 1, 1000, 128, True, [100, 1, 1, 64, 65, 500, 269]),
+    (1, 2, 2, 5000, 64, True, None),
+    (1, 2, 1, 4500, 128, False, [4000, 500]),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,D,causal,lengths", GEOMETRY)
+def test_forward_block_geometries_match_oracle_and_each_other(B, Hq, Hkv, S, D, causal, lengths, monkeypatch):
+    """Both forward block geometries (ATTN_FWD_WAVES=4: 128-query blocks, 8: 256-query blocks sharing each
+    K/V tile) meet the oracle bar and give bitwise the same O and LSE: every row is computed in the same order."""
+    import torch
+    lca = _lib()
+    print(f"case B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} causal={causal} lengths={lengths}", flush=True)
+    x = si.make_inputs(B, Hq, Hkv, S, D, 49, lengths=lengths, with_do=False)
+    q, k, v = dev_bf16(x.q_bits), dev_bf16(x.k_bits), dev_bf16(x.v_bits)
+    cu = dev_i32(x.cu_seqlens) if x.cu_seqlens is not None else None
+    scale = 1.0 / np.sqrt(D)
+    ro, rl = oracle.attention_fwd(x.values("q"), x.values("k"), x.values("v"), causal=causal, scale=scale,
+                                  cu_seqlens=x.cu_seqlens, workers=None)
+    outs = []
+    for waves in ("4", "8"):
+        monkeypatch.setenv("ATTN_FWD_WAVES", waves)
+        o, lse = lca.fwd(q, k, v, causal=causal, cu_seqlens=cu, scale=scale, split=False)
+        torch.cuda.synchronize()
+        check_fwd(host(o), host(lse), ro, rl, tag=f"fwd waves={waves}")
+        outs.append((o, lse))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
