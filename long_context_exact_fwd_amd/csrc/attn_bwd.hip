@@ -55,13 +55,6 @@ __device__ int block_tiles(const BwdParams& p, int pass, int blk) {
   return (hi + 63) / 64 - lo / 64;
 }
 
-// Items [lo, hi) of n handled by share `split` of `ns` (query heads of a
-// group in the dK/dV pass, key tiles of a query block in the dQ pass).
-__device__ __forceinline__ void share_range(int n, int ns, int split, int& lo, int& hi) {
-  lo = split * n / ns;
-  hi = (split + 1) * n / ns;
-}
-
 // Entry e of a pass: dK/dV (pass 0) e = key block * head_split + share of the
 // heads; dQ (pass 1) e = query block * key_split + share of the key tiles.
 template <bool CAUSAL>
@@ -268,25 +261,17 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   // the two transposing reads of the Q^T / dO^T fragment of query step 0.
   int qoff[KS];
 #pragma unroll
-  for (int t = 0; t < KS; ++t) qoff[t] = off_dual<D>(perm_rows(n), 2 * t + h);
+  for (int t = 0; t < KS; ++t) qoff[t] = row_frag_dual<D>(lane, t);
   int trlo[DB], trhi[DB];
-  {
-    const int r0 = 8 * h + ((lane & 15) >> 2);
 #pragma unroll
-    for (int d = 0; d < DB; ++d) {
-      const int unit = 8 * d + 4 * ((lane >> 4) & 1) + (lane & 3);
-      trlo[d] = off_dual_unit<D>(r0, unit);
-      trhi[d] = off_dual_unit<D>(r0 + 4, unit);
-    }
+  for (int d = 0; d < DB; ++d) {
+    trlo[d] = tr_frag_dual<D>(lane, d, 0);
+    trhi[d] = tr_frag_dual<D>(lane, d, 1);
   }
   // DMA: instruction i of wave w fills the 1 KiB at (8 i + w) KiB of a tile.
   uint32_t ld_off[NI];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int e = (i * 8 + wave) * 512 + lane * 8;
-    const int row = e / D;
-    ld_off[i] = (uint32_t)(row * q_stride + swz_dual<D>(row, (e % D) / 8) * 8) * 2u;
-  }
+  for (int i = 0; i < NI; ++i) ld_off[i] = dma_src_dual<D>(tile_dma_elem(i, 8, wave, lane), q_stride);
   const size_t stat_b = (size_t)b * p.hq * p.stat_stride;
   // Step order: query tiles from the last one down, the G heads of the group
   // innermost. Every workgroup of a kv head starts on the same tile, so the
@@ -319,7 +304,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
     slot_ptrs(slot_c, qd, gd, sd);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int el = (i * 8 + wave) * 512;
+      const int el = tile_dma_elem(i, 8, wave, 0);
       dma16_buf(rq, ld_off[i], qd + el);
       dma16_buf(rg, ld_off[i], gd + el);
     }
@@ -663,27 +648,21 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   int koff[KS], voff[KS];
 #pragma unroll
   for (int t = 0; t < KS; ++t) {
-    koff[t] = off_dual<D>(perm_rows(n), 2 * t + h);
-    voff[t] = off_b128<D>(perm_rows(n), 2 * t + h);
+    koff[t] = row_frag_dual<D>(lane, t);
+    voff[t] = row_frag_b128<D>(lane, t);
   }
   int ktlo[DB], kthi[DB];  // K^T fragment of key step 0
-  {
-    const int r0 = 8 * h + ((lane & 15) >> 2);
 #pragma unroll
-    for (int d = 0; d < DB; ++d) {
-      const int unit = 8 * d + 4 * ((lane >> 4) & 1) + (lane & 3);
-      ktlo[d] = off_dual_unit<D>(r0, unit);
-      kthi[d] = off_dual_unit<D>(r0 + 4, unit);
-    }
+  for (int d = 0; d < DB; ++d) {
+    ktlo[d] = tr_frag_dual<D>(lane, d, 0);
+    kthi[d] = tr_frag_dual<D>(lane, d, 1);
   }
   uint32_t ld_koff[NI], ld_voff[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int e = (i * 4 + wave) * 512 + lane * 8;
-    const int row = e / D;
-    const int pc = (e % D) / 8;
-    ld_koff[i] = (uint32_t)(row * kv_stride + swz_dual<D>(row, pc) * 8) * 2u;
-    ld_voff[i] = (uint32_t)(row * kv_stride + swz_b128<D>(row, pc) * 8) * 2u;
+    const int e = tile_dma_elem(i, 4, wave, lane);
+    ld_koff[i] = dma_src_dual<D>(e, kv_stride);
+    ld_voff[i] = dma_src_b128<D>(e, kv_stride);
   }
   auto issue_tile = [&](int t0, auto buf_c) {
     __bf16* kd = decltype(buf_c)::value ? k_lds1 : k_lds0;
@@ -693,7 +672,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)t0 * kv_stride, nbytes);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int el = (i * 4 + wave) * 512;
+      const int el = tile_dma_elem(i, 4, wave, 0);
       dma16_buf(rk, ld_koff[i], kd + el);
       dma16_buf(rv, ld_voff[i], vd + el);
     }

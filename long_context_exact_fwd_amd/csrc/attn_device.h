@@ -19,6 +19,8 @@
 
 #include <type_traits>
 
+#include "attn_index.h"
+
 namespace mi355attn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -67,83 +69,12 @@ __device__ __forceinline__ float sum_lane_halves(float x) {
 
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
-// Swap bits 2 and 3 of a row index in [0, 32): the K (or Q, dO) row a lane
-// loads for the score product, so that C-layout register r of lane half h
-// holds key 16 * (r / 8) + 8 * h + r % 8.
-__device__ __forceinline__ int perm_rows(int m) {
-  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
-}
-
-// Key offset (within a 32-key block) of C-layout register r of lane half h
-// when the rows were loaded through perm_rows.
-__device__ __forceinline__ int c_key(int r, int h) { return 16 * (r >> 3) + 8 * h + (r & 7); }
-
-// ---------------------------------------------------------------------------
-// LDS tile layouts: row-major [rows][D] bf16 with XOR swizzles.
-//
-// "B128" tiles are read with 16-byte reads: lane l reads row perm_rows(l % 32)
-// (+32 per block) at chunk 2t + l / 32. The swizzle permutes 16-byte chunks
-// so that any 8 or 16 consecutive lanes hit distinct banks.
-// "TR" tiles are read with transposing 8-byte reads (4 rows x 16 columns per
-// 16 lanes). The swizzle permutes 8-byte units with a 4-row period.
-// Both swizzles keep each 16-byte chunk contiguous, so tiles are written with
-// 16-byte stores.
-// ---------------------------------------------------------------------------
-
-template <int D>
-__device__ __forceinline__ int swz_b128(int row, int chunk) {
-  if constexpr (D == 128) {
-    const int f = (row & 3) | (((row >> 3) & 1) << 2) | (((row >> 2) & 1) << 3);
-    return chunk ^ f;
-  } else {
-    const int f = ((row >> 1) & 1) | (((row >> 3) & 1) << 1) | (((row ^ (row >> 2)) & 1) << 2);
-    return chunk ^ f;
-  }
-}
-
-// 8-byte unit XOR pattern for TR tiles, in units of 16-byte chunks (>> 1).
-template <int D>
-__device__ __forceinline__ int swz_tr_chunk(int row, int chunk) {
-  // unit XOR table {0, 12, 24, 20} (8-byte units), halved to 16-byte chunks
-  // {0, 6, 12, 10}, looked up by shifting a packed byte table (no branches)
-  int x = (0x0A0C0600 >> (8 * (row & 3))) & 0xFF;
-  if constexpr (D == 64) x &= 7;
-  return chunk ^ x;
-}
-
-// Element offset of (row, 16-byte chunk) in a tile.
-template <int D>
-__device__ __forceinline__ int off_b128(int row, int chunk) { return row * D + swz_b128<D>(row, chunk) * 8; }
-template <int D>
-__device__ __forceinline__ int off_tr(int row, int chunk) { return row * D + swz_tr_chunk<D>(row, chunk) * 8; }
-
-// Element offset of (row, 8-byte unit) in a TR tile.
-template <int D>
-__device__ __forceinline__ int off_tr_unit(int row, int unit) {
-  return row * D + swz_tr_chunk<D>(row, unit >> 1) * 8 + (unit & 1) * 4;
-}
-
 __device__ __forceinline__ bf16x8 lds_read_b128(const __bf16* base, int elem_off) {
   return *LDS_PTR(const bf16x8, base + elem_off);
 }
 
 __device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* base, int elem_off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, const_cast<__bf16*>(base) + elem_off));
-}
-
-// A-operand fragment of the transposed tile X^T (m = column of X, k = 8 rows of X):
-// lane l gets X[row0 + 8 * (l / 32) + 0..7][col0 + l % 32] from a TR tile.
-// row0 must be a multiple of 16 and col0 a multiple of 32.
-template <int D>
-__device__ __forceinline__ bf16x8 tr_fragment(const __bf16* tile, int row0, int col0, int lane) {
-  const int r = row0 + 8 * (lane >> 5) + ((lane & 15) >> 2);
-  const int unit = (col0 >> 2) + 4 * ((lane >> 4) & 1) + (lane & 3);
-  const bf16x4 lo = lds_read_tr(tile, off_tr_unit<D>(r, unit));
-  const bf16x4 hi = lds_read_tr(tile, off_tr_unit<D>(r + 4, unit));
-  bf16x8 out;
-  out[0] = lo[0]; out[1] = lo[1]; out[2] = lo[2]; out[3] = lo[3];
-  out[4] = hi[0]; out[5] = hi[1]; out[6] = hi[2]; out[7] = hi[3];
-  return out;
 }
 
 // Two transposing reads, 4 rows apart in a TR tile: elem_off is the first
@@ -177,24 +108,6 @@ __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t vof
 // s_waitcnt vmcnt(0), other counters left alone (expcnt 7, lgkmcnt 15).
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// One layout for tiles read both with 16-byte reads (rows through perm_rows)
-// and with transposing reads (4 consecutive rows): the chunk XOR spreads 16
-// consecutive rows over 16 chunks and 4 consecutive rows over 4 chunk groups.
-template <int D>
-__device__ __forceinline__ int swz_dual(int row, int chunk) {
-  if constexpr (D == 128) {
-    return chunk ^ (((row & 3) << 2) | ((row >> 2) & 3));
-  } else {
-    return chunk ^ (((row & 3) << 1) | ((row >> 2) & 1));
-  }
-}
-template <int D>
-__device__ __forceinline__ int off_dual(int row, int chunk) { return row * D + swz_dual<D>(row, chunk) * 8; }
-template <int D>
-__device__ __forceinline__ int off_dual_unit(int row, int unit) {
-  return row * D + swz_dual<D>(row, unit >> 1) * 8 + (unit & 1) * 4;
-}
-
 // Two transposing reads at independent offsets (dual tiles: the swizzle of
 // row r + 4 differs from that of row r).
 __device__ __forceinline__ bf16x8 tr_read2(const __bf16* tile, int off_lo, int off_hi) {
@@ -224,26 +137,6 @@ __device__ __forceinline__ bf16x8 pack_bf16(float a0, float a1, float a2, float 
   o[0] = (__bf16)a0; o[1] = (__bf16)a1; o[2] = (__bf16)a2; o[3] = (__bf16)a3;
   o[4] = (__bf16)a4; o[5] = (__bf16)a5; o[6] = (__bf16)a6; o[7] = (__bf16)a7;
   return o;
-}
-
-// Segment [start, end) of token i for packed sequences (binary search over
-// the prefix sums cu[0..n]); the whole sequence when cu is null.
-__device__ __forceinline__ void segment_of(const int32_t* cu, int n, int seqlen, int i, int& start, int& end) {
-  if (cu == nullptr) {
-    start = 0;
-    end = seqlen;
-    return;
-  }
-  int lo = 0, hi = n;  // invariant: cu[lo] <= i < cu[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (cu[mid] <= i) lo = mid; else hi = mid;
-  }
-  // Clamped so that 0 <= start <= i < end <= seqlen holds for any array:
-  // a no-op for valid prefix sums, and a malformed one still keeps every
-  // tile range inside the sequence.
-  start = max(0, min(cu[lo], i));
-  end = min(seqlen, max(cu[hi], i + 1));
 }
 
 __device__ __forceinline__ int wave_min(int x) {

@@ -52,13 +52,6 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-// K tile: 64 rows x 8 chunks of 16 bytes; chunk c of row r at c ^ fK(r), where
-// fK spreads the 8 rows perm_rows reads together over 8 chunk positions.
-__device__ __forceinline__ int fk_swz(int row) { return (row & 3) | ((row >> 1) & 4); }
-// V tile: chunk c of row r at c ^ (r & 7): the 8 rows of one transposing read
-// then cover all 32 banks.
-__device__ __forceinline__ int fv_swz(int row) { return row & 7; }
-
 template <bool CAUSAL>
 __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_fp8_kernel(Fp8FwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[kTileBytes];
@@ -135,28 +128,20 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_fp8_kernel(Fp8FwdPara
   }
 
   // LDS byte offsets (tile-relative).
-  const int krow = perm_rows(n);
-  int koff[2][2];  // [t][half of the 32 bytes]: K row krow, chunk 4t + 2h + i
+  int koff[2][2];  // [t][half of the 32 bytes]: K row perm_rows(n), chunk 4t + 2h + i
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) koff[t][i] = krow * kD + ((4 * t + 2 * h + i) ^ fk_swz(krow)) * 16;
+    for (int i = 0; i < 2; ++i) koff[t][i] = fp8_k_frag(lane, t, i);
   int voff[4];  // V^T source address of key step q = 0 for d block db
-  {
-    const int g = (lane >> 4) & 1;  // which 16 d-columns of the 32-wide block this lane group covers
-    const int s = lane & 15;
-    const int row = 8 * h + (s >> 1);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) voff[db] = row * kD + ((2 * db + g) ^ fv_swz(row)) * 16 + 8 * (s & 1);
-  }
+  for (int db = 0; db < 4; ++db) voff[db] = fp8_v_frag(lane, db);
   uint32_t ld_koff[NI], ld_voff[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int off = (i * kWaves + wave) * 1024 + lane * 16;
-    const int row = off / kD;
-    const int pc = (off % kD) / 16;
-    ld_koff[i] = (uint32_t)(row * kv_stride + (pc ^ fk_swz(row)) * 16);
-    ld_voff[i] = (uint32_t)(row * kv_stride + (pc ^ fv_swz(row)) * 16);
+    const int off = fp8_dma_byte(i, kWaves, wave, lane);
+    ld_koff[i] = fp8_dma_src_k(off, kv_stride);
+    ld_voff[i] = fp8_dma_src_v(off, kv_stride);
   }
   auto issue_tile = [&](int t0, auto buf_c) {
     uint8_t* kd = decltype(buf_c)::value ? k_lds1 : k_lds0;
@@ -166,7 +151,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_fp8_kernel(Fp8FwdPara
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)t0 * kv_stride, nbytes);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int el = (i * kWaves + wave) * 1024;
+      const int el = fp8_dma_byte(i, kWaves, wave, 0);
       dma16_buf(rk, ld_koff[i], kd + el);
       dma16_buf(rv, ld_voff[i], vd + el);
     }
