@@ -22,7 +22,8 @@ bounded sample of the same workload on the host cores. ``workloads`` holds
 the other configurations measured the same way (mid: bf16 forward; packed32k:
 packed fwd+bwd; fp8_64k: fp8 forward against the fp8 dense peak; ring4_gqa32k:
 the gqa32k forward as a 4-chunk Ring-Attention pass with attn_merge, plus the
-merge kernel's HBM rate).
+merge kernel's HBM rate; key_split_1h32k: a small-grid forward with and
+without the key split; fp8_64k_fwd_bwd: the fp8 forward and its backward).
 
     python bench.py [--steps 20] [--warmup 3] [--gpus 1] [--no-secondary]
 """
@@ -54,16 +55,17 @@ def _pairs(seqlen: int, causal: bool, cu=None) -> float:
 
 
 KERNEL_SOURCES = {
-    "attn_fwd_bf16_kernel": ("attn_fwd.hip", "attn_device.h", "attn_internal.h"),
-    "attn_fwd_combine_kernel": ("attn_fwd.hip", "attn_device.h", "attn_internal.h"),
-    "attn_fwd_fewkeys_kernel": ("attn_fwd.hip", "attn_device.h", "attn_internal.h"),
-    "attn_bwd_dkdv_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h"),
-    "attn_bwd_dq_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h"),
-    "attn_bwd_delta_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h"),
-    "attn_fwd_fp8_kernel": ("attn_fwd_fp8.hip", "attn_device.h", "attn_internal.h"),
-    "attn_merge_kernel": ("attn_merge.hip", "attn_device.h", "attn_internal.h"),
-    "attn_bwd_dkdv_reduce_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h"),
-    "attn_bwd_dq_reduce_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h"),
+    "attn_fwd_bf16_kernel": ("attn_fwd.hip", "attn_device.h", "attn_internal.h", "attn_index.h"),
+    "attn_fwd_combine_kernel": ("attn_fwd.hip", "attn_device.h", "attn_internal.h", "attn_index.h"),
+    "attn_fwd_fewkeys_kernel": ("attn_fwd.hip", "attn_device.h", "attn_internal.h", "attn_index.h"),
+    "attn_bwd_dkdv_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h", "attn_index.h"),
+    "attn_bwd_dq_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h", "attn_index.h"),
+    "attn_bwd_delta_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h", "attn_index.h"),
+    "attn_fwd_fp8_kernel": ("attn_fwd_fp8.hip", "attn_device.h", "attn_internal.h", "attn_index.h"),
+    "attn_merge_kernel": ("attn_merge.hip", "attn_device.h", "attn_internal.h", "attn_index.h"),
+    "attn_widen_fp8_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h", "attn_index.h"),
+    "attn_bwd_dkdv_reduce_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h", "attn_index.h"),
+    "attn_bwd_dq_reduce_kernel": ("attn_bwd.hip", "attn_device.h", "attn_internal.h", "attn_index.h"),
 }
 KERNEL_OF_PHASE = {"attn_fwd": "attn_fwd_bf16_kernel", "bwd_delta": "attn_bwd_delta_kernel",
                    "bwd_dkdv": "attn_bwd_dkdv_kernel", "bwd_dq": "attn_bwd_dq_kernel"}
@@ -263,6 +265,52 @@ def fp8_case(w, x, dev):
             tm.mark(i, 1)
 
     return step, ["attn_fwd_fp8"]
+
+
+def fp8_train_case(steps, warmup, dev):
+    """fp8_64k's inputs (B=1, Hq=8, Hkv=1, S=65536, D=128 causal, E4M3 with per-tensor scales) through
+    attn_fwd_fp8 and then attn_bwd_fp8 (widening of the codes to bf16 + the bf16 backward kernels with
+    the scales folded in), with a seeded bf16 dO."""
+    import torch
+    import seeded_inputs as si
+    import long_context_exact_fwd_amd as lca
+    w = si.WORKLOADS["fp8_64k"]
+    x = si.workload_inputs(w, with_do=True)
+    q8, k8, v8 = (torch.from_numpy(b).to(dev) for b in (x.q_bits, x.k_bits, x.v_bits))
+    ds = [torch.tensor([float(d)], dtype=torch.float32, device=dev) for d in x.descale]
+    do = lca.bf16_from_bits(x.do_bits, dev)
+    B, S, Hq, D = q8.shape
+    Hkv = k8.shape[2]
+    o = torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(o), torch.empty((B, S, Hkv, D), dtype=torch.bfloat16, device=dev), None
+    dv = torch.empty_like(dk)
+    ws = torch.empty((lca.bwd_fp8_workspace_bytes(B, Hq, Hkv, S, D) + 3) // 4, dtype=torch.float32, device=dev)
+
+    def step(tm, i):
+        if tm is not None:
+            tm.mark(i, 0)
+        lca.fwd_fp8(q8, k8, v8, *ds, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        if tm is not None:
+            tm.mark(i, 1)
+        lca.bwd_fp8(q8, k8, v8, *ds, o, lse, do, causal=w.causal, scale=w.scale, workspace=ws, dq=dq, dk=dk, dv=dv)
+        if tm is not None:
+            tm.mark(i, 2)
+
+    ms, per = run_steps(step, ["attn_fwd_fp8", "attn_bwd_fp8"], steps, warmup)
+    pairs = _pairs(S, True) * B * Hq
+    tf_f = 4.0 * D * pairs / (per["attn_fwd_fp8"] * 1e-3) / 1e12
+    tf_b = 10.0 * D * pairs / (per["attn_bwd_fp8"] * 1e-3) / 1e12
+    return {
+        "config": f"fp8_64k inputs (B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} causal, E4M3 per-tensor scales) fwd_fp8 + "
+                  f"bwd_fp8, bf16 dO, N(0,1) seed {w.seed}",
+        "tflops": round(14.0 * D * pairs / (ms * 1e-3) / 1e12, 2), "ms_per_step": round(ms, 4), "steps": steps,
+        "phases_ms": {n: round(t, 4) for n, t in per.items()},
+        "fwd_fp8": {"tflops": round(tf_f, 2), "pct_of_peak": round(100.0 * tf_f / PEAK_FP8_TFLOPS, 2),
+                    "peak_tflops": PEAK_FP8_TFLOPS},
+        "bwd_fp8": {"tflops": round(tf_b, 2), "pct_of_peak": round(100.0 * tf_b / PEAK_BF16_TFLOPS, 2),
+                    "peak_tflops": PEAK_BF16_TFLOPS, "note": "bf16 MFMAs on the widened codes"},
+    }
 
 
 def secondary(name, steps, warmup, dev):
@@ -505,6 +553,9 @@ def main(argv=None) -> int:
         print("bench: ring4_gqa32k done", file=sys.stderr, flush=True)
         result["workloads"]["key_split_1h32k"] = key_split_case(sec_steps, min(2, a.warmup), dev)
         print("bench: key_split_1h32k done", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        result["workloads"]["fp8_64k_fwd_bwd"] = fp8_train_case(sec_steps, min(2, a.warmup), dev)
+        print("bench: fp8_64k_fwd_bwd done", file=sys.stderr, flush=True)
     if not a.no_cpu_baseline:
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, x, a.cpu_sample_len)

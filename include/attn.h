@@ -179,6 +179,31 @@ attn_status attn_bwd_phases(unsigned phases, const void* q, const void* k, const
                             int causal, const int32_t* cu_seqlens, int num_seqs,
                             float scale, attn_stream_t stream);
 
+/* Backward of attn_fwd_fp8: dq, dk, dv (bf16) of attention over the
+ * dequantised inputs Q = q8 * descale_q, K = k8 * descale_k,
+ * V = v8 * descale_v, from the forward's o (bf16) and lse and the upstream
+ * gradient dout (bf16). FP8 is named in the FA-3 paragraph of the
+ * FlashAttention page ("那么FlashAttention-2 和 -3 又改进了什么"), per-tensor
+ * scaling of E4M3 data in the Q-Galore section of
+ * "ms-swift支持GPU显存碎片整理提升利用率"; the pages give no FP8 backward,
+ * so this one is the exact gradient of the forward's definition.
+ * An E4M3 code is exact in bf16, so a first kernel widens q8, k8, v8 to bf16
+ * copies in the workspace and the bf16 backward kernels run on them with the
+ * descales folded into their constants (scores: scale * d_q * d_k; Delta
+ * divided by d_v; dK times scale * d_q * d_v; dQ times scale * d_k * d_v).
+ * Arguments as attn_fwd_fp8 and attn_bwd; head_dim must be 128. workspace: at
+ * least attn_bwd_fp8_workspace_bytes() bytes, 16-byte aligned, owned by the
+ * caller: the bf16 copies of q, k, v (each 256-byte aligned) and then the
+ * workspace attn_bwd uses. Returns 0 for unsupported sizes. */
+size_t attn_bwd_fp8_workspace_bytes(int batch, int hq, int hkv, int seqlen, int head_dim);
+attn_status attn_bwd_fp8(const void* q8, const void* k8, const void* v8,
+                         const float* descale_q, const float* descale_k, const float* descale_v,
+                         const void* o, const float* lse, const void* dout,
+                         void* dq, void* dk, void* dv, void* workspace,
+                         int batch, int hq, int hkv, int seqlen, int head_dim,
+                         int causal, const int32_t* cu_seqlens, int num_seqs,
+                         float scale, attn_stream_t stream);
+
 /* Backward without any allocation, for callers that cannot allocate device
  * memory: code under HIP graph capture, allocation-free serving loops,
  * harnesses that forbid hipMalloc. Same arguments, kernels and results as

@@ -8,6 +8,7 @@ library is missing; there is no fallback implementation.
     o, lse = fwd(q, k, v, causal=True)                       # bf16 [B,S,H,D]
     o, lse = fwd_fp8(q8, k8, v8, dq, dk, dv, causal=True)    # uint8 E4M3 codes
     dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True)
+    dq, dk, dv = bwd_fp8(q8, k8, v8, ds_q, ds_k, ds_v, o, lse, do, causal=True)
 """
 from __future__ import annotations
 
@@ -54,6 +55,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_bwd_phases.argtypes = [ctypes.c_uint, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i,
                                     f, st]
     lib.attn_bwd_phases.restype = i
+    lib.attn_bwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, f, st]
+    lib.attn_bwd_fp8.restype = i
+    lib.attn_bwd_fp8_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.attn_bwd_fp8_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i, f, st]
     lib.attn_bwd_noalloc.restype = i
     lib.attn_merge.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, st]
@@ -72,7 +77,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
 
 
 EXPORTED = ("attn_fwd", "attn_fwd_workspace_bytes", "attn_fwd_fp8", "attn_bwd", "attn_bwd_phases",
-            "attn_bwd_workspace_bytes", "attn_bwd_noalloc", "attn_merge", "attn_status_str", "attn_last_hip_error")
+            "attn_bwd_workspace_bytes", "attn_bwd_fp8", "attn_bwd_fp8_workspace_bytes", "attn_bwd_noalloc",
+            "attn_merge", "attn_status_str", "attn_last_hip_error")
 
 BWD_DELTA, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 
@@ -269,4 +275,34 @@ def bwd_noalloc(q, k, v, o, lse, do, *, causal: bool, cu_seqlens=None, scale: Op
                                          _ptr(dv), B, Hq, Hkv, S, D, int(bool(causal)), _ptr(cu_seqlens), n,
                                          float(scale), _stream())
     _check(st, "attn_bwd_noalloc")
+    return dq, dk, dv
+
+
+def bwd_fp8_workspace_bytes(batch: int, hq: int, hkv: int, seqlen: int, head_dim: int) -> int:
+    return int(load_library().attn_bwd_fp8_workspace_bytes(batch, hq, hkv, seqlen, head_dim))
+
+
+def bwd_fp8(q8, k8, v8, descale_q, descale_k, descale_v, o, lse, do, *, causal: bool, cu_seqlens=None,
+            scale: Optional[float] = None, workspace=None, dq=None, dk=None, dv=None):
+    """Backward of fwd_fp8: bf16 (dq, dk, dv) of attention over the dequantised inputs."""
+    import torch
+    _check_tensors(q8, k8, v8, dtype=torch.uint8)
+    _check_tensors(descale_q, descale_k, descale_v, lse, dtype=torch.float32)
+    _check_tensors(o, do, dtype=torch.bfloat16)
+    B, S, Hq, Hkv, D, n = _shape(q8, k8, cu_seqlens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = dq if dq is not None else torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device=q8.device)
+    dk = dk if dk is not None else torch.empty((B, S, Hkv, D), dtype=torch.bfloat16, device=q8.device)
+    dv = dv if dv is not None else torch.empty((B, S, Hkv, D), dtype=torch.bfloat16, device=q8.device)
+    nbytes = bwd_fp8_workspace_bytes(B, Hq, Hkv, S, D)
+    if workspace is None:
+        workspace = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=q8.device)
+    elif not (workspace.is_contiguous() and workspace.numel() * workspace.element_size() >= nbytes
+              and workspace.device == q8.device):
+        raise ValueError(f"workspace must be a contiguous tensor of at least {nbytes} bytes on {q8.device}")
+    st = load_library().attn_bwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(descale_q), _ptr(descale_k), _ptr(descale_v),
+                                     _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                     B, Hq, Hkv, S, D, int(bool(causal)), _ptr(cu_seqlens), n, float(scale), _stream())
+    _check(st, "attn_bwd_fp8")
     return dq, dk, dv

@@ -93,7 +93,8 @@ attn_status bwd_check(unsigned phases, const void* q, const void* k, const void*
 attn_status bwd_launch(unsigned phases, const void* q, const void* k, const void* v, const void* o, const float* lse,
                        const void* dout, void* dq, void* dk, void* dv, void* workspace, int head_split, int key_split,
                        int batch, int hq, int hkv, int seqlen, int head_dim, int causal, const int32_t* cu_seqlens,
-                       int num_seqs, float scale, hipStream_t stream) {
+                       int num_seqs, float scale, hipStream_t stream, const float* descale_q, const float* descale_k,
+                       const float* descale_v) {
   const attn_status st = validate_cu(cu_seqlens, num_seqs, seqlen, stream);
   if (st != ATTN_OK) return st;
   BwdParams p{};
@@ -128,6 +129,9 @@ attn_status bwd_launch(unsigned phases, const void* q, const void* k, const void
   p.causal = causal;
   p.scale = scale;
   p.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  p.descale_q = descale_q;
+  p.descale_k = descale_k;
+  p.descale_v = descale_v;
   return hip_result(run_bwd(p, phases, stream));
 }
 
@@ -255,6 +259,46 @@ attn_status attn_bwd_phases(unsigned phases, const void* q, const void* k, const
                                mi355attn::bwd_head_split(batch, hq, hkv, seqlen),
                                mi355attn::bwd_key_split(batch, hq, seqlen), batch, hq, hkv, seqlen, head_dim, causal,
                                cu_seqlens, num_seqs, scale, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t attn_bwd_fp8_workspace_bytes(int batch, int hq, int hkv, int seqlen, int head_dim) {
+  const size_t bf = attn_bwd_workspace_bytes(batch, hq, hkv, seqlen, head_dim);
+  if (bf == 0 || head_dim != 128) return 0;
+  return mi355attn::bwd_fp8_ws_offset(batch, hq, hkv, seqlen, head_dim) + bf;
+}
+
+attn_status attn_bwd_fp8(const void* q8, const void* k8, const void* v8, const float* descale_q,
+                         const float* descale_k, const float* descale_v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, void* workspace, int batch, int hq, int hkv,
+                         int seqlen, int head_dim, int causal, const int32_t* cu_seqlens, int num_seqs, float scale,
+                         attn_stream_t stream) {
+  if (!q8 || !k8 || !v8 || !descale_q || !descale_k || !descale_v) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8)) return ATTN_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(descale_q) & 3u) || (reinterpret_cast<uintptr_t>(descale_k) & 3u) ||
+      (reinterpret_cast<uintptr_t>(descale_v) & 3u))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  // q, k, v of the bf16 checks stand for the widened copies in the workspace
+  attn_status st = mi355attn::bwd_check(ATTN_BWD_ALL, q8, k8, v8, o, lse, dout, dq, dk, dv, workspace, true, batch,
+                                        hq, hkv, seqlen, head_dim, causal, cu_seqlens, num_seqs, scale);
+  if (st != ATTN_OK) return st;
+  if (head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = validate_cu(cu_seqlens, num_seqs, seqlen, s);  // before the first launch
+  if (st != ATTN_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  __bf16* qw = reinterpret_cast<__bf16*>(ws);
+  __bf16* kw = reinterpret_cast<__bf16*>(ws + mi355attn::bwd_fp8_k_offset(batch, hq, seqlen, head_dim));
+  __bf16* vw = reinterpret_cast<__bf16*>(ws + mi355attn::bwd_fp8_v_offset(batch, hq, hkv, seqlen, head_dim));
+  void* bws = ws + mi355attn::bwd_fp8_ws_offset(batch, hq, hkv, seqlen, head_dim);
+  const size_t nq = (size_t)batch * seqlen * hq * head_dim, nkv = (size_t)batch * seqlen * hkv * head_dim;
+  st = mi355attn::hip_result(mi355attn::run_widen_fp8(static_cast<const uint8_t*>(q8), qw, nq, s));
+  if (st == ATTN_OK) st = mi355attn::hip_result(mi355attn::run_widen_fp8(static_cast<const uint8_t*>(k8), kw, nkv, s));
+  if (st == ATTN_OK) st = mi355attn::hip_result(mi355attn::run_widen_fp8(static_cast<const uint8_t*>(v8), vw, nkv, s));
+  if (st != ATTN_OK) return st;
+  return mi355attn::bwd_launch(ATTN_BWD_ALL, qw, kw, vw, o, lse, dout, dq, dk, dv, bws,
+                               mi355attn::bwd_head_split(batch, hq, hkv, seqlen),
+                               mi355attn::bwd_key_split(batch, hq, seqlen), batch, hq, hkv, seqlen, head_dim, causal,
+                               cu_seqlens, num_seqs, scale, s, descale_q, descale_k, descale_v);
 }
 
 attn_status attn_merge(float* o_acc, float* lse_acc, const void* o_part, const float* lse_part, void* o_out,

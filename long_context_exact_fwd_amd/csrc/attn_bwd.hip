@@ -136,6 +136,13 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
   const int tid = threadIdx.x;
   const int sub = tid % LPR;
   const long r0 = (long)wg * RPW + tid / LPR;
+  // fp8 inputs: dP in the other kernels is dO . V8^T without descale_v, so
+  // Delta is stored divided by it (V = 0 gives dS = 0 either way)
+  float dv_inv = 1.f;
+  if (p.descale_v != nullptr) {
+    const float dv = p.descale_v[0];
+    dv_inv = dv != 0.f ? 1.f / dv : 0.f;
+  }
   bf16x8 av[kDeltaRows], gv[kDeltaRows];
 #pragma unroll
   for (int k = 0; k < kDeltaRows; ++k) {
@@ -156,7 +163,7 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
       const long bs = r / p.hq;
       const long i = bs % p.seqlen;
       const long bh = (bs / p.seqlen) * p.hq + hq;
-      p.delta[bh * p.stat_stride + i] = acc;
+      p.delta[bh * p.stat_stride + i] = dv_inv == 1.f ? acc : acc * dv_inv;
       p.lse2[bh * p.stat_stride + i] = p.lse[bh * p.seqlen + i] * kLog2e;
     }
   }
@@ -319,7 +326,14 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   f32x16 acc[DB];  // dV^T (role A) or dK^T (role B)
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
-  const float c = p.scale_log2e;
+  float c = p.scale_log2e, dk_mul = p.scale;
+  if (p.descale_q != nullptr) {
+    // fp8 inputs: scores of the codes times scale * d_q * d_k (as the fp8
+    // forward computes them); dK = scale * d_q * d_v * sum dS'^T Q8
+    const float dq = p.descale_q[0], dk = p.descale_k[0], dv = p.descale_v[0];
+    c = p.scale * dq * dk * kLog2e;
+    dk_mul = p.scale * dq * dv;
+  }
 
   int nx_g = g_lo, nx_ti = tile_end - 1;  // head and query tile of the next step to load
   if (nsteps > 0) {
@@ -510,7 +524,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   }
 
   if (k_ok) {
-    const float mul = role == 0 ? 1.0f : p.scale;
+    const float mul = role == 0 ? 1.0f : dk_mul;
     const size_t row = ((size_t)b * p.seqlen + my_k) * kv_stride + hk * D;
     if (ns == 1) {
       __bf16* dst = (role == 0 ? p.dv : p.dk) + row;
@@ -681,7 +695,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   f32x16 acc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
-  const float c = p.scale_log2e;
+  float c = p.scale_log2e, dq_mul = p.scale;
+  if (p.descale_q != nullptr) {
+    // fp8 inputs: dQ = scale * d_k * d_v * sum dS' K8
+    const float dq = p.descale_q[0], dk = p.descale_k[0], dv = p.descale_v[0];
+    c = p.scale * dq * dk * kLog2e;
+    dq_mul = p.scale * dk * dv;
+  }
 
   if (tile_begin < tile_end) issue_tile(tile_begin * kKT, std::integral_constant<int, 0>{});
   wait_dma();
@@ -765,7 +785,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
         for (int g = 0; g < 4; ++g) {
           bf16x4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[d][4 * g + e] * p.scale);
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[d][4 * g + e] * dq_mul);
           *reinterpret_cast<bf16x4*>(row + 32 * d + 8 * g + 4 * h) = w;
         }
     } else {
@@ -777,7 +797,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
         for (int g = 0; g < 4; ++g) {
           f32x4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = acc[d][4 * g + e] * p.scale;
+          for (int e = 0; e < 4; ++e) w[e] = acc[d][4 * g + e] * dq_mul;
           *reinterpret_cast<f32x4*>(row + 32 * d + 8 * g + 4 * h) = w;
         }
     }
@@ -798,6 +818,43 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_reduce_kernel(BwdParams p) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) w[e] = (__bf16)sum[e];
   *reinterpret_cast<bf16x4*>(p.dq + i) = w;
+}
+
+// ---------------------------------------------------------------------------
+// E4M3FN code -> bf16, exactly: a code is (-1)^s 2^(e-7) (1 + m/8) for
+// exponent field e > 0 and (-1)^s 2^-6 (m/8) for e = 0; e = 15, m = 7 is NaN.
+// Every such value has at most 4 significant bits and an exponent in
+// [-9, 8], so bf16 holds it exactly. 16 codes per thread.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ __bf16 e4m3_to_bf16(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  float v;
+  if (e == 15u && m == 7u) {
+    v = __builtin_nanf("");
+  } else if (e == 0u) {
+    v = (float)m * 0.001953125f;  // m * 2^-9
+  } else {
+    v = __uint_as_float(((e + 120u) << 23) | (m << 20));  // 2^(e-7) (1 + m/8)
+  }
+  return (__bf16)((b & 0x80u) ? -v : v);
+}
+
+__global__ __launch_bounds__(256) void attn_widen_fp8_kernel(const uint8_t* src, __bf16* dst, size_t n) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 16;
+  if (i >= n) return;
+  if (i + 16 <= n) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(src + i);
+    bf16x8 lo, hi;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      lo[k] = e4m3_to_bf16((w[k / 4] >> (8 * (k % 4))) & 0xFFu);
+      hi[k] = e4m3_to_bf16((w[2 + k / 4] >> (8 * (k % 4))) & 0xFFu);
+    }
+    *reinterpret_cast<bf16x8*>(dst + i) = lo;
+    *reinterpret_cast<bf16x8*>(dst + i + 8) = hi;
+  } else {
+    for (size_t k = i; k < n; ++k) dst[k] = e4m3_to_bf16(src[k]);
+  }
 }
 
 template <int D, bool CAUSAL>
@@ -843,6 +900,12 @@ hipError_t launch_bwd(const BwdParams& p_in, unsigned phases, hipStream_t stream
 }
 
 }  // namespace
+
+hipError_t run_widen_fp8(const uint8_t* src, __bf16* dst, size_t n, hipStream_t stream) {
+  const size_t threads = (n + 15) / 16;
+  hipLaunchKernelGGL(attn_widen_fp8_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, src, dst, n);
+  return hipGetLastError();
+}
 
 hipError_t run_bwd(const BwdParams& p, unsigned phases, hipStream_t stream) {
   if (p.head_dim == 128) {

@@ -73,6 +73,12 @@ struct BwdParams {
   float scale;
   float scale_log2e;
   int num_blk;  // 128-row blocks along the sequence; set by the launcher
+  // fp8 inputs (null for bf16): q, k, v then hold the E4M3 codes widened to
+  // bf16 (exact), and the real inputs are code * descale. The kernels fold the
+  // descales into their constants (scores, Delta and the dK, dQ outputs).
+  const float* descale_q;
+  const float* descale_k;
+  const float* descale_v;
 };
 
 // Forward block geometry, picked from the sizes (the tiling matched to the
@@ -116,6 +122,8 @@ hipError_t run_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream);
 constexpr unsigned kBwdDelta = 1u, kBwdDkDv = 2u, kBwdDq = 4u;
 hipError_t run_bwd(const BwdParams& p, unsigned phases, hipStream_t stream);
 hipError_t run_merge(const MergeParams& p, hipStream_t stream);
+// E4M3 codes -> bf16 (exact), n bytes from src to n bf16 values at dst.
+hipError_t run_widen_fp8(const uint8_t* src, __bf16* dst, size_t n, hipStream_t stream);
 
 // ATTN_OK for hipSuccess; otherwise records e for attn_last_hip_error() and
 // returns ATTN_ERR_HIP.
@@ -133,6 +141,19 @@ attn_status bwd_check(unsigned phases, const void* q, const void* k, const void*
 attn_status bwd_launch(unsigned phases, const void* q, const void* k, const void* v, const void* o, const float* lse,
                        const void* dout, void* dq, void* dk, void* dv, void* workspace, int head_split, int key_split,
                        int batch, int hq, int hkv, int seqlen, int head_dim, int causal, const int32_t* cu_seqlens,
-                       int num_seqs, float scale, hipStream_t stream);
+                       int num_seqs, float scale, hipStream_t stream, const float* descale_q = nullptr,
+                       const float* descale_k = nullptr, const float* descale_v = nullptr);
+
+// fp8 backward workspace: the bf16 copies of the E4M3 codes of Q, K and V,
+// each 256-byte aligned, then the bf16 backward's workspace.
+inline size_t bwd_fp8_k_offset(int batch, int hq, int seqlen, int head_dim) {
+  return align256((size_t)2 * batch * seqlen * hq * head_dim);
+}
+inline size_t bwd_fp8_v_offset(int batch, int hq, int hkv, int seqlen, int head_dim) {
+  return bwd_fp8_k_offset(batch, hq, seqlen, head_dim) + align256((size_t)2 * batch * seqlen * hkv * head_dim);
+}
+inline size_t bwd_fp8_ws_offset(int batch, int hq, int hkv, int seqlen, int head_dim) {
+  return bwd_fp8_v_offset(batch, hq, hkv, seqlen, head_dim) + align256((size_t)2 * batch * seqlen * hkv * head_dim);
+}
 
 }  // namespace mi355attn

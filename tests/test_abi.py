@@ -251,3 +251,29 @@ def test_noalloc_size_limits():
     assert 8 * 1 * 64 * 131072 >= lca.NOALLOC_SCRATCH_BYTES
     assert _noalloc(D=96) == lca.ATTN_ERR_UNSUPPORTED
     assert _noalloc(S=1 << 20, Hq=16, Hkv=4, D=128) == lca.ATTN_ERR_UNSUPPORTED
+
+
+def _bwd8(**kw):
+    a = dict(q=P, k=P, v=P, dq_s=P, dk_s=P, dv_s=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, ws=P, B=1, Hq=4, Hkv=2, S=128,
+             D=128, causal=1, cu=NULL, n=0, scale=0.088)
+    a.update(kw)
+    return lca.load_library().attn_bwd_fp8(a["q"], a["k"], a["v"], a["dq_s"], a["dk_s"], a["dv_s"], a["o"], a["lse"],
+                                           a["do"], a["dq"], a["dk"], a["dv"], a["ws"], a["B"], a["Hq"], a["Hkv"],
+                                           a["S"], a["D"], a["causal"], a["cu"], a["n"], a["scale"], S0)
+
+
+@pytest.mark.parametrize("kw", BAD + [dict(ws=NULL), dict(ws=PM), dict(dq_s=NULL), dict(dv_s=ctypes.c_void_p((1 << 20) + 2)),
+                                      dict(do=PM)])
+def test_bwd_fp8_arguments_rejected(kw):
+    assert _bwd8(**kw) == lca.ATTN_ERR_INVALID_ARGUMENT
+
+
+def test_bwd_fp8_workspace_and_head_dims():
+    lib = lca.load_library()
+    a256 = lambda x: -(-x // 256) * 256
+    for (B, Hq, Hkv, S) in [(1, 8, 1, 65536), (2, 3, 1, 77), (1, 14, 2, 2048)]:
+        want = a256(2 * B * S * Hq * 128) + 2 * a256(2 * B * S * Hkv * 128) + _ws(B, Hq, Hkv, S, 128)
+        assert lib.attn_bwd_fp8_workspace_bytes(B, Hq, Hkv, S, 128) == want
+    assert lib.attn_bwd_fp8_workspace_bytes(1, 4, 2, 128, 64) == 0
+    assert _bwd8(D=64) == lca.ATTN_ERR_UNSUPPORTED
+    assert _bwd8(S=1 << 20, Hq=16, Hkv=4) == lca.ATTN_ERR_UNSUPPORTED

@@ -74,3 +74,61 @@ def test_fp8_forward_key_split(B, Hq, Hkv, S, causal, lengths, ks):
 def test_fp8_peaky_scores_exercise_rescaling():
     """Q and K scaled by 3: the running maximum moves often, so the 0.5 (log2) rescale path runs."""
     _run_fp8(1, 4, 1, 1500, 128, True, seed=22, qk_std=3.0)
+
+
+BWD_CASES = [
+    # B, Hq, Hkv, S, causal, lengths
+    (1, 2, 2, 256, True, None),
+    (2, 3, 1, 77, False, None),
+    (1, 8, 1, 1000, True, None),
+    (1, 4, 1, 700, True, [300, 1, 399]),
+    (1, 14, 2, 2048, True, None),
+]
+
+
+def _fp8_bwd_case(B, Hq, Hkv, S, causal, lengths, exact_o):
+    import torch
+    import long_context_exact_fwd_amd as lca
+    from tests.gpu_helpers import TOL_GRAD_REL, check_grads
+    D = 128
+    print(f"fp8 bwd case B={B} Hq={Hq} Hkv={Hkv} S={S} causal={causal} lengths={lengths} exact_o={exact_o}",
+          flush=True)
+    x = si.make_inputs(B, Hq, Hkv, S, D, 23, lengths=lengths, fp8=True, with_do=True)
+    q8, k8, v8 = dev_u8(x.q_bits), dev_u8(x.k_bits), dev_u8(x.v_bits)
+    ds = [torch.tensor([float(d)], dtype=torch.float32, device="cuda") for d in x.descale]
+    cu = dev_i32(x.cu_seqlens) if x.cu_seqlens is not None else None
+    do = lca.bf16_from_bits(x.do_bits, "cuda")
+    scale = 1.0 / np.sqrt(D)
+    qv = oracle.e4m3_decode(x.q_bits) * float(x.descale[0])
+    kv = oracle.e4m3_decode(x.k_bits) * float(x.descale[1])
+    vv = oracle.e4m3_decode(x.v_bits) * float(x.descale[2])
+    if exact_o:
+        ro, rl = oracle.attention_fwd(qv, kv, vv, causal=causal, scale=scale, cu_seqlens=x.cu_seqlens, workers=None)
+        o = torch.from_numpy(ro).to(torch.bfloat16).cuda()
+        lse = torch.from_numpy(rl).to(torch.float32).cuda()
+    else:
+        o, lse = lca.fwd_fp8(q8, k8, v8, *ds, causal=causal, cu_seqlens=cu, scale=scale)
+    dq, dk, dv = lca.bwd_fp8(q8, k8, v8, *ds, o, lse, do, causal=causal, cu_seqlens=cu, scale=scale)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_bwd(qv, kv, vv, x.values("do"), causal=causal, scale=scale,
+                                      cu_seqlens=x.cu_seqlens, workers=None)
+    if exact_o:
+        check_grads([("dQ", host(dq), rq), ("dK", host(dk), rk), ("dV", host(dv), rv)], tag="fp8 bwd")
+    else:
+        errs = [rel_l2(host(g), r) for g, r in ((dq, rq), (dk, rk), (dv, rv))]
+        print(f"fp8 fwd+bwd: dQ {errs[0]:.3e} dK {errs[1]:.3e} dV {errs[2]:.3e}", flush=True)
+        assert max(errs) <= TOL_FP8_REL
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,causal,lengths", BWD_CASES)
+def test_fp8_backward(B, Hq, Hkv, S, causal, lengths):
+    """attn_bwd_fp8 against the oracle's backward on the dequantised inputs, given the exact O (bf16) and
+    LSE: the exact gradient, so the bf16 gradient bound applies, rel-L2 <= 1e-2 per tensor."""
+    _fp8_bwd_case(B, Hq, Hkv, S, causal, lengths, exact_o=True)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,causal,lengths", [BWD_CASES[2], BWD_CASES[3]])
+def test_fp8_forward_then_backward(B, Hq, Hkv, S, causal, lengths):
+    """attn_fwd_fp8 then attn_bwd_fp8 on its own O and LSE: the forward's fp8 probabilities enter the
+    gradient through Delta = rowsum(dO * O), so the fp8 bound applies, rel-L2 <= 5e-2 per tensor."""
+    _fp8_bwd_case(B, Hq, Hkv, S, causal, lengths, exact_o=False)

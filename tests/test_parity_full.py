@@ -189,3 +189,37 @@ def test_long_sequence_256k_sampled():
     print(f"long bwd: dQ relL2={e_q:.3e} ({len(picks)} rows); |sum dK|/|dK|={e_k:.3e}; sum dV vs sum dO "
           f"relL2={e_v:.3e}", flush=True)
     assert e_q <= TOL_GRAD_REL and e_k <= 1e-2 and e_v <= 1e-2
+
+
+def test_fp8_64k_full_forward_backward_sampled():
+    """B=1, Hq=8, Hkv=1, S=65536, D=128 causal fp8 forward then its backward (attn_bwd_fp8), as bench.py's
+    fp8_64k_fwd_bwd workload runs them. dQ on sampled rows against the oracle on the dequantised inputs, at
+    the fp8 bound (the forward's fp8 probabilities reach the gradient through Delta = dO . O); whole-tensor
+    sums: sum_j dV_j = sum_i dO_i (exact for any O) and |sum_j dK_j| small against |dK|."""
+    import torch
+    import long_context_exact_fwd_amd as lca
+    w = si.WORKLOADS["fp8_64k"]
+    print(f"full-size case fp8_64k fwd+bwd: Hq={w.hq} Hkv={w.hkv} S={w.seqlen} seed={w.seed}", flush=True)
+    x = si.workload_inputs(w, with_do=True)
+    q8, k8, v8 = dev_u8(x.q_bits), dev_u8(x.k_bits), dev_u8(x.v_bits)
+    ds = [torch.tensor([float(d)], dtype=torch.float32, device="cuda") for d in x.descale]
+    do = lca.bf16_from_bits(x.do_bits, "cuda")
+    o, lse = lca.fwd_fp8(q8, k8, v8, *ds, causal=True, scale=w.scale)
+    dq, dk, dv = lca.bwd_fp8(q8, k8, v8, *ds, o, lse, do, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    print("fp8_64k fwd+bwd: GPU done", flush=True)
+    dq_h, dk_h, dv_h = host(dq), host(dk), host(dv)
+    assert np.all(np.isfinite(dq_h)) and np.all(np.isfinite(dk_h)) and np.all(np.isfinite(dv_h))
+    rows = _sample_rows(w, None, w.seed, 64)
+    picks = [(0, h, int(i)) for h in _sample_heads(w.hq, w.seed) for i in rows]
+    qv = oracle.e4m3_decode(x.q_bits) * float(x.descale[0])
+    kv = oracle.e4m3_decode(x.k_bits) * float(x.descale[1])
+    vv = oracle.e4m3_decode(x.v_bits) * float(x.descale[2])
+    dov = x.values("do")
+    rq = oracle.attention_dq_rows(qv, kv, vv, dov, picks, causal=True, scale=w.scale)
+    e_q = rel_l2(np.stack([dq_h[0, i, h] for _, h, i in picks]), rq)
+    sk = float(np.linalg.norm(dk_h[0, :, 0].sum(axis=0)) / np.linalg.norm(dk_h[0, :, 0]))
+    sv = rel_l2(dv_h[0, :, 0].sum(axis=0), dov[0].sum(axis=(0, 1)))
+    print(f"fp8_64k bwd: dQ relL2={e_q:.3e} ({len(picks)} rows); |sum dK|/|dK|={sk:.3e}; sum dV vs sum dO "
+          f"relL2={sv:.3e}", flush=True)
+    assert e_q <= TOL_FP8_REL and sk <= TOL_FP8_REL and sv <= 1e-2
