@@ -21,8 +21,8 @@ largest share of the step time. ``cpu_baseline`` times the fp64 oracle on a
 bounded sample of the same workload on the host cores. ``workloads`` holds
 the other configurations measured the same way (mid: bf16 forward; packed32k:
 packed fwd+bwd; fp8_64k: fp8 forward against the fp8 dense peak; ring4_gqa32k:
-the gqa32k forward as a 4-chunk Ring-Attention pass with attn_merge, plus the
-merge kernel's HBM rate; key_split_1h32k: a small-grid forward with and
+the gqa32k forward as a 4-chunk Ring-Attention pass with attn_fwd_merge, the
+same with attn_fwd + attn_merge, and the merge kernel's HBM rate; key_split_1h32k: a small-grid forward with and
 without the key split; fp8_64k_fwd_bwd: the fp8 forward and its backward).
 
     python bench.py [--steps 20] [--warmup 3] [--gpus 1] [--no-secondary]
@@ -371,9 +371,11 @@ def ring_case(nchunk, steps, warmup, dev):
     """Ring-Attention forward of the gqa32k shape on one GPU, plus the merge kernel on its own.
 
     Query chunk r attends to key chunks 0..r (non-causal for c < r, causal for
-    c = r) with attn_fwd, and attn_merge folds each partial into the chunk's
-    running fp32 result, in ring order. All chunks' work runs on this GPU, so
-    the visible pairs are those of the full causal sequence.
+    c = r), and each key chunk's result is folded into the query chunk's
+    running fp32 result, in ring order: by attn_fwd_merge itself (the headline
+    figure), and for comparison by attn_fwd followed by attn_merge. All
+    chunks' work runs on this GPU, so the visible pairs are those of the full
+    causal sequence.
     """
     import torch
     import seeded_inputs as si
@@ -394,6 +396,16 @@ def ring_case(nchunk, steps, warmup, dev):
     l_acc = [torch.empty((B, Hq, L), dtype=torch.float32, device=dev) for _ in range(nchunk)]
     o_out = [torch.empty((B, L, Hq, D), dtype=torch.bfloat16, device=dev) for _ in range(nchunk)]
 
+    def step_fused(tm, i):
+        if tm is not None:
+            tm.mark(i, 0)
+        for r in range(nchunk):
+            for c in range(r + 1):
+                lca.fwd_merge(qs[r], ks[c], vs[c], o_acc[r], l_acc[r], causal=(c == r), scale=w.scale,
+                              accumulate=(c > 0), o_out=o_out[r] if c == r else None)
+        if tm is not None:
+            tm.mark(i, 1)
+
     def step(tm, i):
         if tm is not None:
             tm.mark(i, 0)
@@ -404,8 +416,10 @@ def ring_case(nchunk, steps, warmup, dev):
         if tm is not None:
             tm.mark(i, 1)
 
-    ms, _ = run_steps(step, ["ring_fwd"], steps, warmup)
     pairs = _pairs(S, True) * B * Hq
+    ms_f, _ = run_steps(step_fused, ["ring_fwd_merge"], steps, warmup)
+    tf_f = 4.0 * D * pairs / (ms_f * 1e-3) / 1e12
+    ms, _ = run_steps(step, ["ring_fwd"], steps, warmup)
     tf = 4.0 * D * pairs / (ms * 1e-3) / 1e12
 
     # the merge kernel alone: accumulate into chunk 0's running result, no bf16 copy
@@ -425,10 +439,12 @@ def ring_case(nchunk, steps, warmup, dev):
     gbs = m_bytes / (m_ms * 1e-3) / 1e9
     return {
         "config": f"ring forward of gqa32k (B={B} Hq={Hq} Hkv={w.hkv} S={S} D={D} causal bf16) in {nchunk} chunks "
-                  f"of {L}: attn_fwd per (query chunk, key chunk <= it) + attn_merge, all on one GPU, "
+                  f"of {L}: attn_fwd_merge per (query chunk, key chunk <= it), all on one GPU, "
                   f"N(0,1) seed {w.seed}",
-        "tflops": round(tf, 2), "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2), "peak_tflops": PEAK_BF16_TFLOPS,
-        "ms_per_step": round(ms, 4), "steps": steps,
+        "tflops": round(tf_f, 2), "pct_of_peak": round(100.0 * tf_f / PEAK_BF16_TFLOPS, 2),
+        "peak_tflops": PEAK_BF16_TFLOPS, "ms_per_step": round(ms_f, 4), "steps": steps,
+        "unfused": {"what": "attn_fwd (bf16 partial O) + attn_merge per chunk pair", "tflops": round(tf, 2),
+                    "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2), "ms_per_step": round(ms, 4)},
         "merge": {"kernel": "attn_merge_kernel", "bound": "hbm", "avg_launch_ms": round(m_ms, 5),
                   "algorithmic_bytes_per_launch": m_bytes, "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                   "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),

@@ -251,6 +251,31 @@ attn_status attn_bwd_noalloc(const void* q, const void* k, const void* v, const 
 attn_status attn_merge(float* o_acc, float* lse_acc, const void* o_part, const float* lse_part, void* o_out,
                        int batch, int seqlen, int heads, int head_dim, int accumulate, attn_stream_t stream);
 
+/* Ring-Attention step fused into the forward: the attention of q over this
+ * call's k and v (the same function attn_fwd computes, with the same causal,
+ * GQA and packing rules) is merged straight into a running result with the
+ * attn_merge formula, so the partial never leaves the chip in bf16 and no
+ * separate merge kernel runs. The ring itself (FlashAttention page,
+ * sequence-parallel section, Ring-Attention paragraph) is the caller's: per
+ * arriving K/V block, one call with accumulate = 1 (0 for the first block).
+ * q, k, v: bfloat16, as for attn_fwd (read only).
+ * o_acc: float32 [B,S,Hq,D], lse_acc: float32 [B,Hq,S] (natural log): read
+ * if accumulate, then overwritten with the merged result. accumulate = 0
+ * treats the running result as empty (its contents are not read).
+ * o_out: bfloat16 [B,S,Hq,D] copy of the merged O (nearest-even), or NULL.
+ * workspace: as for attn_fwd (NULL, or attn_fwd_workspace_bytes() bytes);
+ * with a key split the combine kernel does the merge.
+ * No array may overlap another. Rounding: the partial result stays fp32 up
+ * to the merge; the bf16 probabilities in the PV product and the fp32
+ * recomputation of rows that see fewer than 64 keys are as in attn_fwd.
+ * Every element of o_acc and lse_acc is read and written by one wave, so the
+ * update is in place; calls on one running result must be ordered (one
+ * stream).
+ */
+attn_status attn_fwd_merge(const void* q, const void* k, const void* v, float* o_acc, float* lse_acc, void* o_out,
+                           int accumulate, void* workspace, int batch, int hq, int hkv, int seqlen, int head_dim,
+                           int causal, const int32_t* cu_seqlens, int num_seqs, float scale, attn_stream_t stream);
+
 /* Static string naming a status code ("ATTN_OK", ...). Never NULL. */
 const char* attn_status_str(attn_status s);
 

@@ -63,6 +63,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_bwd_noalloc.restype = i
     lib.attn_merge.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, st]
     lib.attn_merge.restype = i
+    lib.attn_fwd_merge.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, vp, i, f, st]
+    lib.attn_fwd_merge.restype = i
     lib.attn_fwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.attn_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
@@ -78,7 +80,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
 
 EXPORTED = ("attn_fwd", "attn_fwd_workspace_bytes", "attn_fwd_fp8", "attn_bwd", "attn_bwd_phases",
             "attn_bwd_workspace_bytes", "attn_bwd_fp8", "attn_bwd_fp8_workspace_bytes", "attn_bwd_noalloc",
-            "attn_merge", "attn_status_str", "attn_last_hip_error")
+            "attn_merge", "attn_fwd_merge", "attn_status_str", "attn_last_hip_error")
 
 BWD_DELTA, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 
@@ -217,6 +219,34 @@ def merge(o_acc, lse_acc, o_part, lse_part, *, accumulate: bool = True, o_out=No
     st = load_library().attn_merge(_ptr(o_acc), _ptr(lse_acc), _ptr(o_part), _ptr(lse_part), _ptr(o_out), B, S, H,
                                    D, int(bool(accumulate)), _stream())
     _check(st, "attn_merge")
+    return o_acc, lse_acc
+
+
+def fwd_merge(q, k, v, o_acc, lse_acc, *, causal: bool, accumulate: bool = True, o_out=None, cu_seqlens=None,
+              scale: Optional[float] = None, workspace=None, split: bool = True):
+    """Ring-Attention step fused into the forward: attention of q over (k, v) merged into (o_acc, lse_acc) in place.
+
+    o_acc [B,S,Hq,D] fp32, lse_acc [B,Hq,S] fp32; accumulate=False treats them
+    as empty. o_out (bf16 [B,S,Hq,D]) also receives the merged output if given.
+    ``workspace`` and ``split`` work as in fwd(). Returns (o_acc, lse_acc).
+    """
+    import torch
+    _check_tensors(q, k, v, dtype=torch.bfloat16)
+    _check_tensors(o_acc, lse_acc, dtype=torch.float32)
+    B, S, Hq, Hkv, D, n = _shape(q, k, cu_seqlens)
+    if tuple(o_acc.shape) != (B, S, Hq, D) or tuple(lse_acc.shape) != (B, Hq, S):
+        raise ValueError("o_acc must be [B, S, Hq, D] and lse_acc [B, Hq, S]")
+    if o_out is not None:
+        _check_tensors(o_out, dtype=torch.bfloat16)
+        if tuple(o_out.shape) != (B, S, Hq, D):
+            raise ValueError("o_out must be [B, S, Hq, D]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    ws = _fwd_workspace(B, Hq, Hkv, S, D, q.device, workspace, split)
+    st = load_library().attn_fwd_merge(_ptr(q), _ptr(k), _ptr(v), _ptr(o_acc), _ptr(lse_acc), _ptr(o_out),
+                                       int(bool(accumulate)), _ptr(ws), B, Hq, Hkv, S, D, int(bool(causal)),
+                                       _ptr(cu_seqlens), n, float(scale), _stream())
+    _check(st, "attn_fwd_merge")
     return o_acc, lse_acc
 
 

@@ -203,6 +203,49 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   return mi355attn::hip_result(mi355attn::run_fwd_bf16(p, reinterpret_cast<hipStream_t>(stream)));
 }
 
+attn_status attn_fwd_merge(const void* q, const void* k, const void* v, float* o_acc, float* lse_acc, void* o_out,
+                           int accumulate, void* workspace, int batch, int hq, int hkv, int seqlen, int head_dim,
+                           int causal, const int32_t* cu_seqlens, int num_seqs, float scale, attn_stream_t stream) {
+  if (!q || !k || !v || !o_acc || !lse_acc) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_acc) || (o_out && !aligned16(o_out)))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (reinterpret_cast<uintptr_t>(lse_acc) & 3u) return ATTN_ERR_INVALID_ARGUMENT;
+  if (workspace && !aligned16(workspace)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (accumulate != 0 && accumulate != 1) return ATTN_ERR_INVALID_ARGUMENT;
+  attn_status st = check_common(batch, hq, hkv, seqlen, head_dim, causal, cu_seqlens, num_seqs, scale);
+  if (st != ATTN_OK) return st;
+  if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  st = validate_cu(cu_seqlens, num_seqs, seqlen, reinterpret_cast<hipStream_t>(stream));
+  if (st != ATTN_OK) return st;
+  mi355attn::FwdParams p{};
+  p.q = static_cast<const __bf16*>(q);
+  p.k = static_cast<const __bf16*>(k);
+  p.v = static_cast<const __bf16*>(v);
+  p.o_acc = o_acc;
+  p.lse_acc = lse_acc;
+  p.o_out = static_cast<__bf16*>(o_out);
+  p.accumulate = accumulate;
+  p.cu_seqlens = cu_seqlens;
+  p.num_seqs = num_seqs;
+  p.batch = batch;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.seqlen = seqlen;
+  p.head_dim = head_dim;
+  p.causal = causal;
+  p.scale = scale;
+  p.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  p.key_split = 1;
+  const int ks = mi355attn::fwd_key_split(batch, hq, seqlen);
+  if (workspace != nullptr && ks > 1) {
+    p.key_split = ks;
+    p.part_o = static_cast<float*>(workspace);
+    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          mi355attn::fwd_part_lse_offset(batch, hq, seqlen, head_dim, ks));
+  }
+  return mi355attn::hip_result(mi355attn::run_fwd_bf16(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
 attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* descale_q,
                          const float* descale_k, const float* descale_v, void* o, float* lse, void* workspace,
                          int batch, int hq, int hkv, int seqlen, int head_dim, int causal,

@@ -40,13 +40,18 @@ namespace mi355attn {
 namespace {
 
 constexpr int kBN = 64;  // keys per tile
+// Rows that see fewer keys than this are recomputed (or, in a ring merge,
+// merged) by attn_fwd_fewkeys_kernel, not by the tiled kernel.
+constexpr int kFewKeys = 64;
 
 // WAVES waves of 32 queries per workgroup: 4 (128-query blocks, two
 // workgroups per CU) or 8 (256-query blocks, one workgroup per CU, so each
 // K/V tile is copied into LDS once per CU); fwd_block_waves() picks one.
 // With D = 64 the kernel is held to 128 VGPRs so that four waves run per SIMD
 // (it spills 20 bytes per lane; 1-4 % faster than three waves at 161 VGPRs).
-template <int D, bool CAUSAL, int WAVES>
+// MERGE: the epilogue folds the result into the running (o_acc, lse_acc)
+// of a ring step instead of writing o and lse.
+template <int D, bool CAUSAL, int WAVES, bool MERGE>
 __global__ __launch_bounds__(WAVES * 64, (D == 64 ? 16 : 8) / WAVES) void attn_fwd_bf16_kernel(FwdParams p) {
   constexpr int kWaves = WAVES;
   constexpr int kBM = 32 * kWaves;
@@ -275,7 +280,8 @@ __global__ __launch_bounds__(WAVES * 64, (D == 64 ? 16 : 8) / WAVES) void attn_f
   }
 
   // epilogue: O = acc / l, LSE = (m + log2 l) * ln 2; with a key split the
-  // share's fp32 O and m + log2 l, combined by attn_fwd_combine_kernel
+  // share's fp32 O and m + log2 l, combined by attn_fwd_combine_kernel; in a
+  // ring merge, the merge of (acc / l, m + log2 l) into the running result
   const float l_tot = sum_lane_halves(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   if (q_ok && ks > 1) {
@@ -293,6 +299,44 @@ __global__ __launch_bounds__(WAVES * 64, (D == 64 ? 16 : 8) / WAVES) void attn_f
     if (h == 0) {
       p.part_lse[(((size_t)share * p.batch + b) * p.hq + hq) * p.seqlen + my_q] =
           l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
+    }
+  } else if (MERGE) {
+    // A row that sees at least 64 keys has l > 0. With the running result's
+    // L_a = LSE_acc log2 e and this call's L_p = m + log2 l, M = max(L_a, L_p),
+    // w_a = 2^(L_a - M), w_p = 2^(L_p - M), T = w_a + w_p:
+    //   O = (w_a O_acc + w_p acc / l) / T = (w_a / T) O_acc + (2^(m - M) / T) acc,
+    //   LSE = (M + log2 T) ln 2.
+    // The two lanes of a row both read LSE_acc before the h = 0 lane stores
+    // the new one (the store depends on the loaded value).
+    if (q_ok && kend - kstart >= kFewKeys) {
+      const size_t ri = ((size_t)b * p.seqlen + my_q) * q_stride + hq * D;
+      const size_t li = ((size_t)b * p.hq + hq) * p.seqlen + my_q;
+      const float la = p.accumulate ? p.lse_acc[li] * kLog2e : -INFINITY;
+      const float lp = m_run + __log2f(l_tot);
+      const float mm = fmaxf(la, lp);
+      const float wa = fast_exp2(la - mm);  // 0 for an empty running result
+      const float tot = wa + fast_exp2(lp - mm);
+      const float rt = 1.0f / tot;
+      const float ca = wa * rt, cp = fast_exp2(m_run - mm) * rt;
+      float* arow = p.o_acc + ri;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4* dst = reinterpret_cast<f32x4*>(arow + 32 * db + 8 * g + 4 * h);
+          const f32x4 old = p.accumulate ? *dst : f32x4{};
+          f32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = ca * old[e] + cp * acc[db][4 * g + e];
+          *dst = w;
+          if (p.o_out != nullptr) {
+            bf16x4 wb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wb[e] = (__bf16)w[e];
+            *reinterpret_cast<bf16x4*>(p.o_out + ri + 32 * db + 8 * g + 4 * h) = wb;
+          }
+        }
+      if (h == 0) p.lse_acc[li] = (mm + __log2f(tot)) * kLn2;
     }
   } else if (q_ok) {
     __bf16* orow = p.o + ((size_t)b * p.seqlen + my_q) * q_stride + hq * D;
@@ -321,6 +365,9 @@ __global__ __launch_bounds__(WAVES * 64, (D == 64 ? 16 : 8) / WAVES) void attn_f
 //   LSE = (M + log2 sum_s 2^(L_s - M)) ln 2.
 // One thread per 8 consecutive d of a row; the D / 8 threads of a row sit in
 // one wave. HBM-bound: 4 ks bytes read and 2 written per output element.
+// In a ring merge (o_acc set) the combined (O, L) is folded into the running
+// result as the tiled kernel's merge epilogue does, and rows with fewer than
+// 64 visible keys are left to attn_fwd_fewkeys_kernel.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void attn_fwd_combine_kernel(FwdParams p) {
@@ -337,6 +384,11 @@ __global__ __launch_bounds__(256) void attn_fwd_combine_kernel(FwdParams p) {
   const int ks = p.key_split;
   const size_t lstride = (size_t)p.batch * p.hq * p.seqlen;
   const size_t li = ((size_t)b * p.hq + hq) * p.seqlen + s;
+  if (p.o_acc != nullptr) {
+    int s0, s1;
+    segment_of(p.cu_seqlens, p.num_seqs, p.seqlen, s, s0, s1);
+    if ((p.causal ? s + 1 : s1) - s0 < kFewKeys) return;  // whole rows, so no lane waits on another
+  }
   float m = -INFINITY;
   for (int sp = 0; sp < ks; ++sp) m = fmaxf(m, p.part_lse[sp * lstride + li]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -354,6 +406,38 @@ __global__ __launch_bounds__(256) void attn_fwd_combine_kernel(FwdParams p) {
         acc[4 + e] += w * c[e];
       }
     }
+  }
+  if (p.o_acc != nullptr) {
+    // the row sees at least 64 keys, so tot > 0; acc / tot and m + log2 tot
+    // merged with the running result, coefficients as in the tiled kernel
+    const float la = p.accumulate ? p.lse_acc[li] * kLog2e : -INFINITY;
+    const float lp = m + __log2f(tot);
+    const float mm = fmaxf(la, lp);
+    const float wa = fast_exp2(la - mm);
+    const float t2 = wa + fast_exp2(lp - mm);
+    const float rt = 1.0f / t2;
+    const float ca = wa * rt, cp = fast_exp2(m - mm) * rt;
+    f32x4* dst = reinterpret_cast<f32x4*>(p.o_acc + row * D + 8 * sub);
+    const f32x4 a0 = p.accumulate ? dst[0] : f32x4{}, a1 = p.accumulate ? dst[1] : f32x4{};
+    f32x4 r0, r1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      r0[e] = ca * a0[e] + cp * acc[e];
+      r1[e] = ca * a1[e] + cp * acc[4 + e];
+    }
+    dst[0] = r0;
+    dst[1] = r1;
+    if (p.o_out != nullptr) {
+      bf16x8 ob;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ob[e] = (__bf16)r0[e];
+        ob[4 + e] = (__bf16)r1[e];
+      }
+      *reinterpret_cast<bf16x8*>(p.o_out + row * D + 8 * sub) = ob;
+    }
+    if (sub == 0) p.lse_acc[li] = (mm + __log2f(t2)) * kLn2;
+    return;
   }
   const float inv = tot > 0.f ? 1.0f / tot : 0.f;
   bf16x8 out;
@@ -376,8 +460,11 @@ __global__ __launch_bounds__(256) void attn_fwd_combine_kernel(FwdParams p) {
 // most 63) go to LDS, then one wave per row: lane j computes the score of key
 // j, the wave takes the exact maximum and sum, and lane t accumulates
 // O[d] = sum_j p_j v_j[d] for d = t, t + 64.
+// In a ring merge (o_acc set) the exact (O, LSE) of the row is merged into the
+// running result instead (the tiled kernel and the combine leave these rows
+// alone): M = max(LSE_acc, LSE), w = e^(LSE - M) for each, O = (w_acc O_acc +
+// w O) / (w_acc + w), LSE = M + ln(w_acc + w).
 // ---------------------------------------------------------------------------
-constexpr int kFewKeys = 64;    // rows with fewer visible keys are recomputed
 constexpr int kFewRowsPerWg = 4;  // one wave per row
 constexpr int kFewBlocks = (kFewKeys + kFewRowsPerWg - 1) / kFewRowsPerWg;
 
@@ -451,11 +538,40 @@ __global__ __launch_bounds__(256) void attn_fwd_fewkeys_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < DL; ++i) o[i] = __builtin_fmaf(pb, (float)vs[j][lane + 64 * i], o[i]);
   }
-  const float inv = 1.0f / l;
-  __bf16* orow = p.o + ((size_t)b * p.seqlen + r) * q_stride + hq * D;
+  const size_t ri = ((size_t)b * p.seqlen + r) * q_stride + hq * D;
+  const size_t li = ((size_t)b * p.hq + hq) * p.seqlen + r;
+  if (p.o_acc != nullptr) {
+    // o / l has LSE m + ln l; its weight over the total is e^(m - M) l / T, so
+    // its term is e^(m - M) o / T. Lane 0 stores LSE after every lane has read it.
+    const float la = p.accumulate ? p.lse_acc[li] : -INFINITY;
+    const float lp = m + logf(l);
+    const float mm = fmaxf(la, lp);
+    const float wa = expf(la - mm);  // 0 for an empty running result
+    const float tot = wa + expf(lp - mm);
+    const float ca = wa / tot, cp = expf(m - mm) / tot;
 #pragma unroll
-  for (int i = 0; i < DL; ++i) orow[lane + 64 * i] = (__bf16)(o[i] * inv);
-  if (lane == 0) p.lse[((size_t)b * p.hq + hq) * p.seqlen + r] = m + logf(l);
+    for (int i = 0; i < DL; ++i) {
+      float* dst = p.o_acc + ri + lane + 64 * i;
+      const float res = ca * (p.accumulate ? *dst : 0.f) + cp * o[i];
+      *dst = res;
+      if (p.o_out != nullptr) p.o_out[ri + lane + 64 * i] = (__bf16)res;
+    }
+    if (lane == 0) p.lse_acc[li] = mm + logf(tot);
+    return;
+  }
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int i = 0; i < DL; ++i) p.o[ri + lane + 64 * i] = (__bf16)(o[i] * inv);
+  if (lane == 0) p.lse[li] = m + logf(l);
+}
+
+template <int D, bool CAUSAL, bool MERGE>
+void launch_tiled(const FwdParams& q, int waves, dim3 grid, hipStream_t stream) {
+  if (waves == 8) {
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 8, MERGE>), grid, dim3(8 * 64), 0, stream, q);
+  } else {
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 4, MERGE>), grid, dim3(4 * 64), 0, stream, q);
+  }
 }
 
 template <int D, bool CAUSAL>
@@ -465,10 +581,11 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
   const int waves = q.key_split > 1 ? 4 : fwd_block_waves(q.seqlen, D, q.causal, q.cu_seqlens != nullptr);
   q.num_qblk = (p.seqlen + 32 * waves - 1) / (32 * waves);
   dim3 grid(p.batch * p.hq, q.num_qblk * q.key_split);
-  if (waves == 8) {
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 8>), grid, dim3(8 * 64), 0, stream, q);
+  // with a key split the tiled kernel writes only partials, which the combine merges
+  if (q.o_acc != nullptr && q.key_split == 1) {
+    launch_tiled<D, CAUSAL, true>(q, waves, grid, stream);
   } else {
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 4>), grid, dim3(4 * 64), 0, stream, q);
+    launch_tiled<D, CAUSAL, false>(q, waves, grid, stream);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -26,6 +26,12 @@ struct FwdParams {
   int key_split;      // shares of each query block's key tiles (1: no split)
   float* part_o;      // key_split > 1: fp32 partial O [ks][B][S][Hq][D], each normalised by its share's sum
   float* part_lse;    // key_split > 1: fp32 m + log2 l [ks][B][Hq][S] (-inf for a share without visible keys)
+  // Ring merge (attn_fwd_merge), when o_acc is not null: the call's result is
+  // folded into a running one instead of being written to o and lse.
+  float* o_acc;     // fp32 [B][S][Hq][D], read if accumulate, then overwritten
+  float* lse_acc;   // fp32 [B][Hq][S], natural log, the same
+  __bf16* o_out;    // bf16 copy of the merged O, or null
+  int accumulate;   // 0: the running result starts empty
 };
 
 struct Fp8FwdParams {

@@ -10,14 +10,20 @@
 * the matching backward: attn_bwd on every (query chunk, key chunk) pair with
   the final O and LSE gives the global probabilities restricted to that
   chunk pair, so the pair gradients summed over chunks must equal the
-  oracle's full gradients (rel-L2 <= 1e-2).
+  oracle's full gradients (rel-L2 <= 1e-2);
+* attn_fwd_merge, the forward that merges its result into the running one
+  itself: one step against the oracle's merge of a random running result
+  with the oracle's attention (causal or not, GQA, packed, the key split whose
+  combine does the merge, accumulate off, the bf16 copy), rows with fewer
+  than 64 visible keys to fp32 accuracy; and the whole ring built from it,
+  forward and backward, as above.
 """
 import numpy as np
 import pytest
 
 import oracle
 import seeded_inputs as si
-from tests.gpu_helpers import check_fwd, check_grads, dev_bf16, host, max_abs
+from tests.gpu_helpers import check_fwd, check_grads, dev_bf16, dev_i32, host, max_abs
 
 pytestmark = pytest.mark.gpu
 
@@ -103,6 +109,29 @@ def ring_forward(q, k, v, nchunk, causal, scale):
     return o, lse
 
 
+def ring_forward_fused(q, k, v, nchunk, causal, scale):
+    """ring_forward with attn_fwd_merge: each key chunk's result goes straight into the running one."""
+    import torch
+    lca = _lib()
+    B, S, Hq, D = q.shape
+    L = S // nchunk
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    for r in range(nchunk):
+        qr = q[:, r * L:(r + 1) * L].contiguous()
+        o_acc = torch.empty((B, L, Hq, D), dtype=torch.float32, device=q.device)
+        l_acc = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+        o_r = torch.empty((B, L, Hq, D), dtype=torch.bfloat16, device=q.device)
+        chunks = list(range(r + 1)) if causal else list(range(nchunk))
+        for i, c in enumerate(chunks):
+            lca.fwd_merge(qr, k[:, c * L:(c + 1) * L].contiguous(), v[:, c * L:(c + 1) * L].contiguous(), o_acc,
+                          l_acc, causal=(causal and c == r), accumulate=(i > 0), scale=scale,
+                          o_out=o_r if i == len(chunks) - 1 else None)
+        o[:, r * L:(r + 1) * L] = o_r
+        lse[:, :, r * L:(r + 1) * L] = l_acc
+    return o, lse
+
+
 def ring_backward(q, k, v, o, lse, do, nchunk, causal, scale):
     """Pair backward with the final O and LSE; gradients summed over chunk pairs in fp32."""
     import torch
@@ -135,13 +164,14 @@ RING_CASES = [
 ]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["fwd+merge", "fwd_merge"])
 @pytest.mark.parametrize("B,Hq,Hkv,S,D,nchunk,causal", RING_CASES)
-def test_ring_forward_and_backward_equal_full_attention(B, Hq, Hkv, S, D, nchunk, causal):
+def test_ring_forward_and_backward_equal_full_attention(B, Hq, Hkv, S, D, nchunk, causal, fused):
     import torch
-    print(f"ring B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} N={nchunk} causal={causal}", flush=True)
+    print(f"ring B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} N={nchunk} causal={causal} fused={fused}", flush=True)
     x, q, k, v, do = _ring_inputs(B, Hq, Hkv, S, D, seed=90 + nchunk)
     scale = 1.0 / np.sqrt(D)
-    o, lse = ring_forward(q, k, v, nchunk, causal, scale)
+    o, lse = (ring_forward_fused if fused else ring_forward)(q, k, v, nchunk, causal, scale)
     torch.cuda.synchronize()
     qv, kv, vv = x.values("q"), x.values("k"), x.values("v")
     ro, rl = oracle.attention_fwd(qv, kv, vv, causal=causal, scale=scale, workers=None)
@@ -150,3 +180,60 @@ def test_ring_forward_and_backward_equal_full_attention(B, Hq, Hkv, S, D, nchunk
     torch.cuda.synchronize()
     rq, rk, rv = oracle.attention_bwd(qv, kv, vv, x.values("do"), causal=causal, scale=scale, workers=None)
     check_grads([("dQ", host(dq), rq), ("dK", host(dk), rk), ("dV", host(dv), rv)], tag="ring bwd")
+
+
+FUSED_CASES = [
+    # B, Hq, Hkv, S, D, causal, packed lengths, accumulate, bf16 copy, key split
+    (1, 4, 2, 300, 128, True, None, True, True, False),
+    (2, 2, 1, 200, 64, False, None, False, False, False),
+    (1, 2, 2, 300, 128, True, [37, 63, 200], True, False, False),
+    (1, 3, 1, 250, 64, False, [10, 50, 64, 126], True, True, False),
+    (1, 2, 1, 4500, 128, True, None, True, True, True),
+    (1, 2, 2, 4400, 64, True, [50, 4000, 350], True, False, True),
+    (1, 2, 1, 4200, 128, False, None, False, True, True),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,D,causal,lengths,acc,with_out,split", FUSED_CASES)
+def test_fwd_merge_step_matches_oracle(B, Hq, Hkv, S, D, causal, lengths, acc, with_out, split):
+    import torch
+    lca = _lib()
+    print(f"fwd_merge B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} causal={causal} lengths={lengths} accumulate={acc} "
+          f"out={with_out} split={split}", flush=True)
+    if split:
+        assert lca.fwd_workspace_bytes(B, Hq, Hkv, S, D) > 0, "case meant to run the key split"
+    x = si.make_inputs(B, Hq, Hkv, S, D, seed=S + 7 * Hq + D, lengths=lengths, with_do=False)
+    rng = np.random.default_rng(S * 3 + D)
+    o1 = rng.standard_normal((B, S, Hq, D)).astype(np.float32)
+    # running LSEs around the new part's (ln of the visible key count, plus about 0.5)
+    l1 = rng.uniform(-2.0, 10.0, (B, Hq, S)).astype(np.float32)
+    l1.reshape(-1)[::9] = -np.inf  # rows whose running result is still empty
+    dev = torch.device("cuda")
+    q, k, v = dev_bf16(x.q_bits), dev_bf16(x.k_bits), dev_bf16(x.v_bits)
+    cu = dev_i32(x.cu_seqlens) if x.cu_seqlens is not None else None
+    o_acc = torch.from_numpy(o1.copy()).to(dev)
+    lse_acc = torch.from_numpy(l1.copy()).to(dev)
+    o_out = torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device=dev) if with_out else None
+    scale = 1.0 / np.sqrt(D)
+    lca.fwd_merge(q, k, v, o_acc, lse_acc, causal=causal, accumulate=acc, o_out=o_out, cu_seqlens=cu, scale=scale,
+                  split=split)
+    torch.cuda.synchronize()
+    po, pl = oracle.attention_fwd(x.values("q"), x.values("k"), x.values("v"), causal=causal, scale=scale,
+                                  cu_seqlens=x.cu_seqlens, workers=None)
+    r_o1 = o1.astype(np.float64) if acc else np.zeros_like(o1, dtype=np.float64)
+    r_l1 = l1.astype(np.float64) if acc else np.full(l1.shape, -np.inf)
+    ro, rl = oracle.merge_partials(r_o1, r_l1, po, pl)
+    go, gl = host(o_acc), host(lse_acc)
+    check_fwd(go, gl, ro, rl, tag="fwd_merge")
+    # rows with fewer than 64 visible keys: exact fp32 partial and fp32 merge
+    s0, s1 = oracle.segment_bounds(S, x.cu_seqlens)
+    pos = np.arange(S)
+    few = ((pos + 1 if causal else s1) - s0) < 64
+    if few.any():
+        e_o = max_abs(go[:, few], ro[:, few])
+        e_l = max_abs(gl[:, :, few], rl[:, :, few])
+        print(f"fwd_merge few-key rows: {int(few.sum())} O maxabs={e_o:.3e} LSE maxabs={e_l:.3e}", flush=True)
+        assert e_o <= 1e-5 and e_l <= 1e-5
+    if with_out:
+        gb = host(o_out)
+        assert np.max(np.abs(gb - go) - np.abs(go) * 2.0 ** -8) <= 0.0
