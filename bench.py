@@ -24,6 +24,8 @@ packed fwd+bwd; fp8_64k: fp8 forward against the fp8 dense peak; ring4_gqa32k:
 the gqa32k forward as a 4-chunk Ring-Attention pass with attn_fwd_merge, the
 same with attn_fwd + attn_merge, and the merge kernel's HBM rate; key_split_1h32k: a small-grid forward with and
 without the key split; fp8_64k_fwd_bwd: the fp8 forward and its backward).
+``mfma_ceiling`` is the rate a register-only MFMA loop sustains on the same
+GPU and its clock, the practical ceiling the kernels' fractions compare with.
 
     python bench.py [--steps 20] [--warmup 3] [--gpus 1] [--no-secondary]
 """
@@ -452,6 +454,61 @@ def ring_case(nchunk, steps, warmup, dev):
     }
 
 
+def mfma_ceiling_case(dev, iters=40000, reps=5):
+    """The bf16 matrix pipe's sustained rate on this GPU under a pure MFMA load, and its clock.
+
+    Runs the probe of csrc/probe/mfma_ceiling.hip (one 8-wave workgroup per
+    CU, 8 independent register-only v_mfma_f32_32x32x16_bf16 chains per wave)
+    and times it with HIP events on the launch stream, once with N(0, 1)-like
+    operands that change from one MFMA to the next (the figure the kernels
+    compare with: their operands are such data) and once with constant
+    low-entropy operands. The clock is the ratio of the shader-clock counter
+    to the 100 MHz counter around each wave's loop (median over workgroups).
+    """
+    import ctypes
+    import numpy as np
+    import torch
+    from long_context_exact_fwd_amd import build as bld
+    lib = ctypes.CDLL(bld.PROBE_LIB)
+    lib.mfma_ceiling_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p]
+    lib.mfma_ceiling_launch.restype = ctypes.c_int
+    lib.mfma_ceiling_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.mfma_ceiling_flops.restype = ctypes.c_double
+    groups = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(groups * 512, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(2 * groups, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run(random_operands):
+        def launch():
+            rc = lib.mfma_ceiling_launch(ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(clocks.data_ptr()), groups,
+                                         iters, int(random_operands), ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"mfma_ceiling_launch returned {rc}")
+
+        launch()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = lib.mfma_ceiling_flops(groups, iters) / (ms * 1e-3) / 1e12
+        ck = clocks.view(groups, 2).cpu().numpy().astype(np.float64)
+        ghz = float(np.median(ck[:, 0] / np.maximum(ck[:, 1], 1.0))) * 0.1
+        return {"ms": round(ms, 4), "tflops": round(tf, 1), "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
+                "clock_ghz": round(ghz, 3)}
+
+    res = {"what": f"register-only v_mfma_f32_32x32x16_bf16 loop, {groups} workgroups x 8 waves (2 per SIMD), "
+                   f"8 chains x {iters} per wave, operands N(0,1)-like and different for every MFMA"}
+    res.update(run(True))
+    res["low_entropy_operands"] = run(False)
+    return res
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -572,6 +629,14 @@ def main(argv=None) -> int:
         torch.cuda.empty_cache()
         result["workloads"]["fp8_64k_fwd_bwd"] = fp8_train_case(sec_steps, min(2, a.warmup), dev)
         print("bench: fp8_64k_fwd_bwd done", file=sys.stderr, flush=True)
+        try:
+            ceil = mfma_ceiling_case(dev)
+        except (OSError, RuntimeError) as e:  # probe library missing or launch refused: no ceiling figure
+            ceil = {"error": str(e)}
+        result["mfma_ceiling"] = ceil
+        if "tflops" in ceil:
+            result["roofline"]["frac_of_mfma_ceiling"] = round(roofline["achieved"] / ceil["tflops"], 4)
+        print("bench: mfma ceiling done", file=sys.stderr, flush=True)
     if not a.no_cpu_baseline:
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, x, a.cpu_sample_len)

@@ -3,9 +3,10 @@
     python -m long_context_exact_fwd_amd.build [--jobs N]
 
 Every HIP source under csrc/ is compiled for gfx950 and linked into
-long_context_exact_fwd_amd/libmi355attn.so. Packed fp32 VALU instructions are
-disabled (``-packed-fp32-ops``); hipcc's host pass warns that it does not know
-that feature, which is harmless.
+long_context_exact_fwd_amd/libmi355attn.so. The measurement probes under
+csrc/probe/ (not part of the attention library) go into libmi355probe.so.
+Packed fp32 VALU instructions are disabled (``-packed-fp32-ops``); hipcc's
+host pass warns that it does not know that feature, which is harmless.
 """
 from __future__ import annotations
 
@@ -20,6 +21,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmi355attn.so")
+PROBE_LIB = os.path.join(PKG, "libmi355probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -40,18 +42,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 0) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    jobs = jobs or min(8, len(srcs), os.cpu_count() or 1)
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int = 0) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    probes = sorted(glob.glob(os.path.join(CSRC, "probe", "*.hip")))
+    jobs = jobs or min(8, len(srcs) + len(probes), os.cpu_count() or 1)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, srcs + probes))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     return LIB
 
 
