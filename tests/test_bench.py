@@ -4,6 +4,7 @@ HBM-traffic records are keyed on."""
 import os
 
 import numpy as np
+import pytest
 
 import bench
 import seeded_inputs as si
@@ -66,3 +67,33 @@ def test_cpu_baseline_fields_and_extrapolation():
     assert "extrapolated" in ex["note"]
     assert abs(ex["threads"] - r["seconds"] * full / pairs) <= 0.01 + 0.01 * ex["threads"]
     assert r["single_thread"]["seconds"] > 0 and r["single_thread"]["value"] > 0
+
+
+def test_mfma_ceiling_probe_library_exports():
+    """The ceiling probe is its own library (not part of the attention ABI); its flop count is 8 waves x
+    8 chains x 2*32*32*16 per workgroup and iteration."""
+    import ctypes
+    from long_context_exact_fwd_amd import build as bld
+    if not os.path.exists(bld.PROBE_LIB):
+        pytest.skip("probe library not built")
+    lib = ctypes.CDLL(bld.PROBE_LIB)
+    lib.mfma_ceiling_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.mfma_ceiling_flops.restype = ctypes.c_double
+    assert lib.mfma_ceiling_flops(1, 1) == 8 * 8 * 2 * 32 * 32 * 16
+    assert lib.mfma_ceiling_flops(256, 1000) == 256 * 1000 * 8 * 8 * 2 * 32 * 32 * 16
+    lib.mfma_ceiling_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p]
+    lib.mfma_ceiling_launch.restype = ctypes.c_int
+    # argument checks run before any HIP call
+    assert lib.mfma_ceiling_launch(None, None, 1, 1, 1, None) == -1
+    assert lib.mfma_ceiling_launch(ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 20), 0, 1, 1, None) == -1
+
+
+@pytest.mark.gpu
+def test_mfma_ceiling_probe_runs():
+    import torch
+    r = bench.mfma_ceiling_case(torch.device("cuda"), iters=2000, reps=2)
+    print("mfma ceiling (short run):", r, flush=True)
+    for k in (r, r["low_entropy_operands"]):
+        assert 100.0 < k["tflops"] < 1.05 * bench.PEAK_BF16_TFLOPS
+        assert 0.5 < k["clock_ghz"] < 3.0
