@@ -44,6 +44,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
+SECONDARY_WARM_MS = 200.0  # least warmup before a secondary workload's timed steps
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA peak
 PEAK_HBM_GBS = 8000.0
 
@@ -198,12 +199,28 @@ class Timer:
         return out
 
 
-def run_steps(step, names, steps, warmup):
-    """Warm up, then time exactly `steps` steps between two synchronisations; returns (ms/step, per-phase ms)."""
+def run_steps(step, names, steps, warmup, min_warm_ms=0.0):
+    """Warm up, then time exactly `steps` steps between two synchronisations; returns (ms/step, per-phase ms).
+
+    ``min_warm_ms`` > 0 adds warmup steps until the warmup has taken that long
+    (the secondary workloads: after seconds of host-side input generation the
+    GPU's power management needs tens of milliseconds of load to settle, and
+    a 1 ms kernel timed inside that transient reads up to 25 % slow). The
+    number of warmup steps run is left in ``run_steps.last_warmup``.
+    """
     import torch
+    n_warm = 0
+    t0 = time.perf_counter()
     for _ in range(warmup):
         step(None, 0)
+        n_warm += 1
     torch.cuda.synchronize()
+    while min_warm_ms > 0 and (time.perf_counter() - t0) * 1e3 < min_warm_ms:
+        for _ in range(max(1, n_warm)):
+            step(None, 0)
+            n_warm += 1
+        torch.cuda.synchronize()
+    run_steps.last_warmup = n_warm
     tm = Timer(names, steps)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -299,7 +316,7 @@ def fp8_train_case(steps, warmup, dev):
         if tm is not None:
             tm.mark(i, 2)
 
-    ms, per = run_steps(step, ["attn_fwd_fp8", "attn_bwd_fp8"], steps, warmup)
+    ms, per = run_steps(step, ["attn_fwd_fp8", "attn_bwd_fp8"], steps, warmup, SECONDARY_WARM_MS)
     pairs = _pairs(S, True) * B * Hq
     tf_f = 4.0 * D * pairs / (per["attn_fwd_fp8"] * 1e-3) / 1e12
     tf_b = 10.0 * D * pairs / (per["attn_bwd_fp8"] * 1e-3) / 1e12
@@ -321,7 +338,7 @@ def secondary(name, steps, warmup, dev):
     w = si.WORKLOADS[name]
     x = si.workload_inputs(w)
     step, names = (fp8_case if w.fp8 else bf16_case)(w, x, dev)
-    ms, per = run_steps(step, names, steps, warmup)
+    ms, per = run_steps(step, names, steps, warmup, SECONDARY_WARM_MS)
     pairs = _pairs(w.seqlen, w.causal, x.cu_seqlens) * w.batch * w.hq
     flops = (14.0 if w.backward else 4.0) * w.head_dim * pairs
     peak = PEAK_FP8_TFLOPS if w.fp8 else PEAK_BF16_TFLOPS
@@ -362,7 +379,7 @@ def key_split_case(steps, warmup, dev):
                     split=split)
             if tm is not None:
                 tm.mark(i, 1)
-        ms, _ = run_steps(step, ["attn_fwd"], steps, warmup)
+        ms, _ = run_steps(step, ["attn_fwd"], steps, warmup, SECONDARY_WARM_MS)
         tf = flops / (ms * 1e-3) / 1e12
         out[label] = {"ms": round(ms, 4), "tflops": round(tf, 2), "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2)}
     out["key_split"] = nf // (4 * B * Hq * S * (D + 1))  # workspace = ks partial O planes + ks row-stat planes
@@ -419,9 +436,9 @@ def ring_case(nchunk, steps, warmup, dev):
             tm.mark(i, 1)
 
     pairs = _pairs(S, True) * B * Hq
-    ms_f, _ = run_steps(step_fused, ["ring_fwd_merge"], steps, warmup)
+    ms_f, _ = run_steps(step_fused, ["ring_fwd_merge"], steps, warmup, SECONDARY_WARM_MS)
     tf_f = 4.0 * D * pairs / (ms_f * 1e-3) / 1e12
-    ms, _ = run_steps(step, ["ring_fwd"], steps, warmup)
+    ms, _ = run_steps(step, ["ring_fwd"], steps, warmup, SECONDARY_WARM_MS)
     tf = 4.0 * D * pairs / (ms * 1e-3) / 1e12
 
     # the merge kernel alone: accumulate into chunk 0's running result, no bf16 copy
