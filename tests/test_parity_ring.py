@@ -237,3 +237,40 @@ def test_fwd_merge_step_matches_oracle(B, Hq, Hkv, S, D, causal, lengths, acc, w
     if with_out:
         gb = host(o_out)
         assert np.max(np.abs(gb - go) - np.abs(go) * 2.0 ** -8) <= 0.0
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,D,causal,lengths", [
+    (1, 4, 2, 700, 128, True, None),
+    (2, 3, 1, 333, 64, False, None),
+    (1, 2, 2, 600, 128, True, [100, 37, 463]),
+])
+def test_fwd_merge_block_geometries(B, Hq, Hkv, S, D, causal, lengths, monkeypatch):
+    """attn_fwd_merge with 128-query blocks (4 waves) and 256-query blocks (8 waves): both meet the oracle bar
+    and give bitwise the same running result (each row is computed and merged in the same order)."""
+    import torch
+    lca = _lib()
+    print(f"fwd_merge geometry B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} causal={causal} lengths={lengths}", flush=True)
+    x = si.make_inputs(B, Hq, Hkv, S, D, seed=S + D, lengths=lengths, with_do=False)
+    rng = np.random.default_rng(S + 1)
+    o1 = rng.standard_normal((B, S, Hq, D)).astype(np.float32)
+    l1 = rng.uniform(-2.0, 8.0, (B, Hq, S)).astype(np.float32)
+    dev = torch.device("cuda")
+    q, k, v = dev_bf16(x.q_bits), dev_bf16(x.k_bits), dev_bf16(x.v_bits)
+    cu = dev_i32(x.cu_seqlens) if x.cu_seqlens is not None else None
+    scale = 1.0 / np.sqrt(D)
+    po, pl = oracle.attention_fwd(x.values("q"), x.values("k"), x.values("v"), causal=causal, scale=scale,
+                                  cu_seqlens=x.cu_seqlens, workers=None)
+    ro, rl = oracle.merge_partials(o1.astype(np.float64), l1.astype(np.float64), po, pl)
+    outs = []
+    for waves in ("4", "8"):
+        monkeypatch.setenv("ATTN_FWD_WAVES", waves)
+        o_acc = torch.from_numpy(o1.copy()).to(dev)
+        lse_acc = torch.from_numpy(l1.copy()).to(dev)
+        o_out = torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device=dev)
+        lca.fwd_merge(q, k, v, o_acc, lse_acc, causal=causal, accumulate=True, o_out=o_out, cu_seqlens=cu,
+                      scale=scale, split=False)
+        torch.cuda.synchronize()
+        check_fwd(host(o_acc), host(lse_acc), ro, rl, tag=f"fwd_merge waves={waves}")
+        outs.append((o_acc, lse_acc, o_out))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
