@@ -1,6 +1,6 @@
 """ATTN_VALIDATE=1: malformed cu_seqlens arrays are rejected on the host before
-anything is launched (no kernel ever sees them here); a valid array gives the
-same bits as an unvalidated call."""
+anything is launched (no kernel ever sees them here), by every entry point that
+takes one; a valid array gives the same bits as an unvalidated call."""
 import numpy as np
 import pytest
 
@@ -40,9 +40,14 @@ def test_validate_rejects_malformed_cu_seqlens(monkeypatch):
     for bad in BAD:
         print(f"case malformed cu_seqlens {bad}", flush=True)
         cu = dev_i32(np.array(bad, dtype=np.int32))
+        o_acc = torch.zeros((1, S, 2, 128), dtype=torch.float32, device="cuda")
+        l_acc = torch.zeros((1, 2, S), dtype=torch.float32, device="cuda")
         calls = [lambda: lca.fwd(q, k, v, causal=True, cu_seqlens=cu),
                  lambda: lca.fwd_fp8(q8, k8, v8, *ds, causal=True, cu_seqlens=cu),
-                 lambda: lca.bwd(q, k, v, o, lse, do, causal=True, cu_seqlens=cu)]
+                 lambda: lca.fwd_merge(q, k, v, o_acc, l_acc, causal=True, cu_seqlens=cu),
+                 lambda: lca.bwd(q, k, v, o, lse, do, causal=True, cu_seqlens=cu),
+                 lambda: lca.bwd_noalloc(q, k, v, o, lse, do, causal=True, cu_seqlens=cu),
+                 lambda: lca.bwd_fp8(q8, k8, v8, *ds, o, lse, do, causal=True, cu_seqlens=cu)]
         for call in calls:
             with pytest.raises(lca.AttnError) as err:
                 call()
