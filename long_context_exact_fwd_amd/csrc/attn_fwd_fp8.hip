@@ -9,9 +9,10 @@
 //   l summed from the fp32 probabilities.
 //
 // Both products run on v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 operands, unit
-// block scales, fp32 accumulate). Work split as in the bf16 kernel: 4 waves of
-// 32 queries per workgroup, two workgroups per CU, 64-key K/V tiles copied
-// into LDS by buffer loads, double-buffered.
+// block scales, fp32 accumulate). Work split as in the bf16 kernel: waves of
+// 32 queries, 4 per workgroup with two workgroups per CU, or 8 per workgroup
+// with one per CU (fwd_fp8_block_waves()), 64-key K/V tiles copied into LDS
+// by buffer loads, double-buffered.
 //   * S^T = K Q^T: lane (n, h) supplies bytes [64t + 32h, +32) of its row for
 //     both operands (the lane-to-k order of an MFMA is the same for A and B,
 //     so any common byte choice contracts every d exactly once).
@@ -41,8 +42,6 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;       // head dim (bytes per fp8 row)
 constexpr int kBN = 64;       // keys per tile
-constexpr int kWaves = 4;
-constexpr int kBM = 32 * kWaves;
 constexpr int kTileBytes = kBN * kD;
 constexpr float kP8Offset = 8.0f;       // log2 units subtracted from the running maximum
 constexpr float kP8Threshold = 0.5f;    // lazy rescale threshold for the fp8 path
@@ -52,8 +51,10 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-template <bool CAUSAL>
-__global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_fp8_kernel(Fp8FwdParams p) {
+template <bool CAUSAL, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void attn_fwd_fp8_kernel(Fp8FwdParams p) {
+  constexpr int kWaves = WAVES;
+  constexpr int kBM = 32 * kWaves;
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[kTileBytes];
@@ -296,10 +297,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void attn_fwd_fp8_kernel(Fp8FwdPara
 template <bool CAUSAL>
 hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream) {
   Fp8FwdParams q = p;
-  q.num_qblk = (p.seqlen + kBM - 1) / kBM;
   if (q.key_split < 1 || q.part_o == nullptr || q.part_lse == nullptr) q.key_split = 1;
+  const int waves = q.key_split > 1 ? 4 : fwd_fp8_block_waves(q.seqlen, q.causal, q.cu_seqlens != nullptr);
+  q.num_qblk = (p.seqlen + 32 * waves - 1) / (32 * waves);
   dim3 grid(p.batch * p.hq, q.num_qblk * q.key_split);
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL>), grid, dim3(kWaves * 64), 0, stream, q);
+  if (waves == 8) {
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL, 8>), grid, dim3(8 * 64), 0, stream, q);
+  } else {
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL, 4>), grid, dim3(4 * 64), 0, stream, q);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || q.key_split == 1) return e;
   FwdParams c{};

@@ -110,6 +110,15 @@ inline int fwd_block_waves(int seqlen, int head_dim, int causal, bool packed) {
   if (packed || head_dim != 128) return 4;
   return seqlen >= (causal ? 16384 : 4096) ? 8 : 4;
 }
+// The fp8 forward's block height: 128 queries (4 waves) or 256 (8 waves), same override.
+inline int fwd_fp8_block_waves(int seqlen, int causal, bool packed) {
+  const int forced = fwd_block_waves_env();
+  if (forced == 4 || forced == 8) return forced;
+  (void)seqlen;
+  (void)causal;
+  (void)packed;
+  return 4;
+}
 struct MergeParams {
   float* o_acc;            // [B, S, H, D] fp32, read if accumulate, written
   float* lse_acc;          // [B, H, S] fp32, read if accumulate, written

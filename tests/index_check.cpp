@@ -209,7 +209,7 @@ std::vector<Tag> fill_fp8_tile(bool is_v, int waves) {
 }
 
 void check_fp8() {
-  for (int waves : {4}) {
+  for (int waves : {4, 8}) {
     const std::vector<Tag> kt = fill_fp8_tile(false, waves), vt = fill_fp8_tile(true, waves);
     // K row fragments: 32 bytes per lane, k-step t, key block kb
     for (int kb = 0; kb < 2; ++kb)

@@ -38,6 +38,7 @@ def _run_fp8(B, Hq, Hkv, S, D, causal, lengths=None, seed=21, qk_std=1.0, split=
     print(msg, flush=True)
     assert np.all(np.isfinite(o_h)) and np.all(np.isfinite(l_h)), msg
     assert rr <= TOL_FP8_REL and rlse <= TOL_LSE, msg
+    return o, lse
 
 
 CASES = [
@@ -57,6 +58,19 @@ CASES = [
 @pytest.mark.parametrize("B,Hq,Hkv,S,D,causal,lengths", CASES)
 def test_fp8_forward(B, Hq, Hkv, S, D, causal, lengths):
     _run_fp8(B, Hq, Hkv, S, D, causal, lengths=lengths)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,causal,lengths", [(1, 4, 2, 1000, True, None), (2, 3, 1, 333, False, None),
+                                                       (1, 2, 2, 700, True, [100, 37, 563])])
+def test_fp8_forward_block_geometries(B, Hq, Hkv, S, causal, lengths, monkeypatch):
+    """Both fp8 forward geometries (ATTN_FWD_WAVES=4: 128-query blocks, 8: 256-query blocks) meet the oracle
+    bar and give bitwise the same O and LSE."""
+    import torch
+    outs = []
+    for waves in ("4", "8"):
+        monkeypatch.setenv("ATTN_FWD_WAVES", waves)
+        outs.append(_run_fp8(B, Hq, Hkv, S, 128, causal, lengths=lengths, seed=23, split=False))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,S,causal,lengths,ks", [(1, 1, 1, 8192, True, None, 4),
