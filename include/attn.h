@@ -276,6 +276,20 @@ attn_status attn_fwd_merge(const void* q, const void* k, const void* v, float* o
                            int accumulate, void* workspace, int batch, int hq, int hkv, int seqlen, int head_dim,
                            int causal, const int32_t* cu_seqlens, int num_seqs, float scale, attn_stream_t stream);
 
+/* attn_fwd_merge for the fp8 forward: the attention attn_fwd_fp8 computes
+ * (E4M3 q8, k8, v8 with per-tensor descales, head_dim 128) merged into the
+ * running fp32 (o_acc, lse_acc) in the forward's epilogue, with the formula,
+ * arguments and workspace of attn_fwd_merge. The fp8 path has no fp32
+ * recomputation of rows that see few keys: every row's probabilities enter
+ * the PV product rounded to E4M3, as in attn_fwd_fp8.
+ */
+attn_status attn_fwd_fp8_merge(const void* q8, const void* k8, const void* v8,
+                               const float* descale_q, const float* descale_k, const float* descale_v,
+                               float* o_acc, float* lse_acc, void* o_out, int accumulate, void* workspace,
+                               int batch, int hq, int hkv, int seqlen, int head_dim,
+                               int causal, const int32_t* cu_seqlens, int num_seqs,
+                               float scale, attn_stream_t stream);
+
 /* Static string naming a status code ("ATTN_OK", ...). Never NULL. */
 const char* attn_status_str(attn_status s);
 

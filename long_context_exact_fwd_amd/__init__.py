@@ -65,6 +65,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_merge.restype = i
     lib.attn_fwd_merge.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, vp, i, f, st]
     lib.attn_fwd_merge.restype = i
+    lib.attn_fwd_fp8_merge.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, vp, i, f, st]
+    lib.attn_fwd_fp8_merge.restype = i
     lib.attn_fwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.attn_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
@@ -80,7 +82,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
 
 EXPORTED = ("attn_fwd", "attn_fwd_workspace_bytes", "attn_fwd_fp8", "attn_bwd", "attn_bwd_phases",
             "attn_bwd_workspace_bytes", "attn_bwd_fp8", "attn_bwd_fp8_workspace_bytes", "attn_bwd_noalloc",
-            "attn_merge", "attn_fwd_merge", "attn_status_str", "attn_last_hip_error")
+            "attn_merge", "attn_fwd_merge", "attn_fwd_fp8_merge", "attn_status_str", "attn_last_hip_error")
 
 BWD_DELTA, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 
@@ -247,6 +249,31 @@ def fwd_merge(q, k, v, o_acc, lse_acc, *, causal: bool, accumulate: bool = True,
                                        int(bool(accumulate)), _ptr(ws), B, Hq, Hkv, S, D, int(bool(causal)),
                                        _ptr(cu_seqlens), n, float(scale), _stream())
     _check(st, "attn_fwd_merge")
+    return o_acc, lse_acc
+
+
+def fwd_fp8_merge(q8, k8, v8, descale_q, descale_k, descale_v, o_acc, lse_acc, *, causal: bool,
+                  accumulate: bool = True, o_out=None, cu_seqlens=None, scale: Optional[float] = None, workspace=None,
+                  split: bool = True):
+    """fwd_merge for the fp8 forward: E4M3 codes (uint8) with fp32 device descales; o_acc, lse_acc updated in place."""
+    import torch
+    _check_tensors(q8, k8, v8, dtype=torch.uint8)
+    _check_tensors(descale_q, descale_k, descale_v, o_acc, lse_acc, dtype=torch.float32)
+    B, S, Hq, Hkv, D, n = _shape(q8, k8, cu_seqlens)
+    if tuple(o_acc.shape) != (B, S, Hq, D) or tuple(lse_acc.shape) != (B, Hq, S):
+        raise ValueError("o_acc must be [B, S, Hq, D] and lse_acc [B, Hq, S]")
+    if o_out is not None:
+        _check_tensors(o_out, dtype=torch.bfloat16)
+        if tuple(o_out.shape) != (B, S, Hq, D):
+            raise ValueError("o_out must be [B, S, Hq, D]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    ws = _fwd_workspace(B, Hq, Hkv, S, D, q8.device, workspace, split) if D == 128 else None
+    st = load_library().attn_fwd_fp8_merge(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(descale_q), _ptr(descale_k),
+                                           _ptr(descale_v), _ptr(o_acc), _ptr(lse_acc), _ptr(o_out),
+                                           int(bool(accumulate)), _ptr(ws), B, Hq, Hkv, S, D, int(bool(causal)),
+                                           _ptr(cu_seqlens), n, float(scale), _stream())
+    _check(st, "attn_fwd_fp8_merge")
     return o_acc, lse_acc
 
 

@@ -225,6 +225,7 @@ attn_status attn_fwd_merge(const void* q, const void* k, const void* v, float* o
   p.lse_acc = lse_acc;
   p.o_out = static_cast<__bf16*>(o_out);
   p.accumulate = accumulate;
+  p.few_rows_apart = 1;
   p.cu_seqlens = cu_seqlens;
   p.num_seqs = num_seqs;
   p.batch = batch;
@@ -271,6 +272,56 @@ attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const f
   p.descale_v = descale_v;
   p.o = static_cast<__bf16*>(o);
   p.lse = lse;
+  p.cu_seqlens = cu_seqlens;
+  p.num_seqs = num_seqs;
+  p.batch = batch;
+  p.hq = hq;
+  p.hkv = hkv;
+  p.seqlen = seqlen;
+  p.head_dim = head_dim;
+  p.causal = causal;
+  p.scale = scale;
+  p.key_split = 1;
+  const int ks = mi355attn::fwd_key_split(batch, hq, seqlen);
+  if (workspace != nullptr && ks > 1) {
+    p.key_split = ks;
+    p.part_o = static_cast<float*>(workspace);
+    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          mi355attn::fwd_part_lse_offset(batch, hq, seqlen, head_dim, ks));
+  }
+  return mi355attn::hip_result(mi355attn::run_fwd_fp8(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_fwd_fp8_merge(const void* q8, const void* k8, const void* v8, const float* descale_q,
+                               const float* descale_k, const float* descale_v, float* o_acc, float* lse_acc,
+                               void* o_out, int accumulate, void* workspace, int batch, int hq, int hkv, int seqlen,
+                               int head_dim, int causal, const int32_t* cu_seqlens, int num_seqs, float scale,
+                               attn_stream_t stream) {
+  if (!q8 || !k8 || !v8 || !descale_q || !descale_k || !descale_v || !o_acc || !lse_acc)
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o_acc) || (o_out && !aligned16(o_out)))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(descale_q) & 3u) || (reinterpret_cast<uintptr_t>(descale_k) & 3u) ||
+      (reinterpret_cast<uintptr_t>(descale_v) & 3u) || (reinterpret_cast<uintptr_t>(lse_acc) & 3u))
+    return ATTN_ERR_INVALID_ARGUMENT;
+  if (workspace && !aligned16(workspace)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (accumulate != 0 && accumulate != 1) return ATTN_ERR_INVALID_ARGUMENT;
+  attn_status st = check_common(batch, hq, hkv, seqlen, head_dim, causal, cu_seqlens, num_seqs, scale);
+  if (st != ATTN_OK) return st;
+  if (head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  st = validate_cu(cu_seqlens, num_seqs, seqlen, reinterpret_cast<hipStream_t>(stream));
+  if (st != ATTN_OK) return st;
+  mi355attn::Fp8FwdParams p{};
+  p.q = static_cast<const uint8_t*>(q8);
+  p.k = static_cast<const uint8_t*>(k8);
+  p.v = static_cast<const uint8_t*>(v8);
+  p.descale_q = descale_q;
+  p.descale_k = descale_k;
+  p.descale_v = descale_v;
+  p.o_acc = o_acc;
+  p.lse_acc = lse_acc;
+  p.o_out = static_cast<__bf16*>(o_out);
+  p.accumulate = accumulate;
   p.cu_seqlens = cu_seqlens;
   p.num_seqs = num_seqs;
   p.batch = batch;

@@ -366,8 +366,9 @@ __global__ __launch_bounds__(WAVES * 64, (D == 64 ? 16 : 8) / WAVES) void attn_f
 // One thread per 8 consecutive d of a row; the D / 8 threads of a row sit in
 // one wave. HBM-bound: 4 ks bytes read and 2 written per output element.
 // In a ring merge (o_acc set) the combined (O, L) is folded into the running
-// result as the tiled kernel's merge epilogue does, and rows with fewer than
-// 64 visible keys are left to attn_fwd_fewkeys_kernel.
+// result as the tiled kernel's merge epilogue does; for the bf16 forward
+// (few_rows_apart) rows with fewer than 64 visible keys are left to
+// attn_fwd_fewkeys_kernel.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void attn_fwd_combine_kernel(FwdParams p) {
@@ -384,7 +385,7 @@ __global__ __launch_bounds__(256) void attn_fwd_combine_kernel(FwdParams p) {
   const int ks = p.key_split;
   const size_t lstride = (size_t)p.batch * p.hq * p.seqlen;
   const size_t li = ((size_t)b * p.hq + hq) * p.seqlen + s;
-  if (p.o_acc != nullptr) {
+  if (p.o_acc != nullptr && p.few_rows_apart) {
     int s0, s1;
     segment_of(p.cu_seqlens, p.num_seqs, p.seqlen, s, s0, s1);
     if ((p.causal ? s + 1 : s1) - s0 < kFewKeys) return;  // whole rows, so no lane waits on another
@@ -408,8 +409,9 @@ __global__ __launch_bounds__(256) void attn_fwd_combine_kernel(FwdParams p) {
     }
   }
   if (p.o_acc != nullptr) {
-    // the row sees at least 64 keys, so tot > 0; acc / tot and m + log2 tot
-    // merged with the running result, coefficients as in the tiled kernel
+    // every share of a row that sees keys has l > 0, so tot > 0 for such a
+    // row; acc / tot and m + log2 tot merged with the running result,
+    // coefficients as in the tiled kernel
     const float la = p.accumulate ? p.lse_acc[li] * kLog2e : -INFINITY;
     const float lp = m + __log2f(tot);
     const float mm = fmaxf(la, lp);

@@ -51,7 +51,9 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-template <bool CAUSAL, int WAVES>
+// MERGE: the epilogue folds the result into the running (o_acc, lse_acc) of a
+// ring step instead of writing o and lse.
+template <bool CAUSAL, int WAVES, bool MERGE>
 __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void attn_fwd_fp8_kernel(Fp8FwdParams p) {
   constexpr int kWaves = WAVES;
   constexpr int kBM = 32 * kWaves;
@@ -274,6 +276,41 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void attn_fwd_fp8_kernel(Fp8
       p.part_lse[(((size_t)share * p.batch + b) * p.hq + hq) * p.seqlen + my_q] =
           l_tot > 0.f ? m_run - kP8Offset + __log2f(l_tot) : -INFINITY;
     }
+  } else if (MERGE) {
+    // With L_a = LSE_acc log2 e and this call's L_p = m - offset + log2 l,
+    // M = max(L_a, L_p), T = 2^(L_a - M) + 2^(L_p - M):
+    //   O = (2^(L_a - M) / T) O_acc + (2^(m - offset - M) d_v / T) acc,
+    //   LSE = (M + log2 T) ln 2;
+    // both lanes of a row read LSE_acc before the h = 0 lane stores it.
+    if (q_ok && l_tot > 0.f) {
+      const size_t ri = ((size_t)b * p.seqlen + my_q) * (size_t)(p.hq * kD) + hq * kD;
+      const size_t li = ((size_t)b * p.hq + hq) * p.seqlen + my_q;
+      const float la = p.accumulate ? p.lse_acc[li] * kLog2e : -INFINITY;
+      const float lp = m_run - kP8Offset + __log2f(l_tot);
+      const float mm = fmaxf(la, lp);
+      const float wa = fast_exp2(la - mm);
+      const float tot = wa + fast_exp2(lp - mm);
+      const float rt = 1.0f / tot;
+      const float ca = wa * rt, cp = fast_exp2(m_run - kP8Offset - mm) * dv * rt;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4* dst = reinterpret_cast<f32x4*>(p.o_acc + ri + 32 * db + 8 * g + 4 * h);
+          const f32x4 old = p.accumulate ? *dst : f32x4{};
+          f32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = ca * old[e] + cp * acc[db][4 * g + e];
+          *dst = w;
+          if (p.o_out != nullptr) {
+            bf16x4 wb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wb[e] = (__bf16)w[e];
+            *reinterpret_cast<bf16x4*>(p.o_out + ri + 32 * db + 8 * g + 4 * h) = wb;
+          }
+        }
+      if (h == 0) p.lse_acc[li] = (mm + __log2f(tot)) * kLn2;
+    }
   } else if (q_ok) {
     __bf16* orow = p.o + ((size_t)b * p.seqlen + my_q) * (size_t)(p.hq * kD) + hq * kD;
 #pragma unroll
@@ -301,10 +338,20 @@ hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream) {
   const int waves = q.key_split > 1 ? 4 : fwd_fp8_block_waves(q.seqlen, q.causal, q.cu_seqlens != nullptr);
   q.num_qblk = (p.seqlen + 32 * waves - 1) / (32 * waves);
   dim3 grid(p.batch * p.hq, q.num_qblk * q.key_split);
+  // with a key split the kernel writes only partials, which the combine merges
+  const bool merge = q.o_acc != nullptr && q.key_split == 1;
   if (waves == 8) {
-    hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL, 8>), grid, dim3(8 * 64), 0, stream, q);
+    if (merge) {
+      hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL, 8, true>), grid, dim3(8 * 64), 0, stream, q);
+    } else {
+      hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL, 8, false>), grid, dim3(8 * 64), 0, stream, q);
+    }
   } else {
-    hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL, 4>), grid, dim3(4 * 64), 0, stream, q);
+    if (merge) {
+      hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL, 4, true>), grid, dim3(4 * 64), 0, stream, q);
+    } else {
+      hipLaunchKernelGGL((attn_fwd_fp8_kernel<CAUSAL, 4, false>), grid, dim3(4 * 64), 0, stream, q);
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || q.key_split == 1) return e;
@@ -318,6 +365,11 @@ hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream) {
   c.hq = q.hq;
   c.head_dim = kD;
   c.key_split = q.key_split;
+  c.o_acc = q.o_acc;  // ring merge: the combine merges every row (the fp8 path has no few-key kernel)
+  c.lse_acc = q.lse_acc;
+  c.o_out = q.o_out;
+  c.accumulate = q.accumulate;
+  c.few_rows_apart = 0;
   return run_fwd_combine(c, stream);
 }
 

@@ -32,6 +32,7 @@ struct FwdParams {
   float* lse_acc;   // fp32 [B][Hq][S], natural log, the same
   __bf16* o_out;    // bf16 copy of the merged O, or null
   int accumulate;   // 0: the running result starts empty
+  int few_rows_apart;  // ring merge: rows with < 64 visible keys are merged by the few-key kernel (bf16 path)
 };
 
 struct Fp8FwdParams {
@@ -52,6 +53,11 @@ struct Fp8FwdParams {
   int key_split;    // as in FwdParams (1: no split)
   float* part_o;    // key_split > 1: fp32 partial O [ks][B][S][Hq][D]
   float* part_lse;  // key_split > 1: fp32 m + log2 l [ks][B][Hq][S], in log2 units of the scores
+  // Ring merge (attn_fwd_fp8_merge), when o_acc is not null: as in FwdParams
+  float* o_acc;
+  float* lse_acc;
+  __bf16* o_out;
+  int accumulate;
 };
 
 struct BwdParams {

@@ -274,3 +274,97 @@ def test_fwd_merge_block_geometries(B, Hq, Hkv, S, D, causal, lengths, monkeypat
         outs.append((o_acc, lse_acc, o_out))
     for a, b in zip(outs[0], outs[1]):
         assert torch.equal(a, b)
+
+
+FP8_MERGE_CASES = [
+    # B, Hq, Hkv, S, causal, packed lengths, accumulate, bf16 copy, key split
+    (1, 4, 2, 300, True, None, True, True, False),
+    (2, 2, 1, 200, False, None, False, False, False),
+    (1, 2, 2, 300, True, [37, 63, 200], True, False, False),
+    (1, 2, 1, 4500, True, None, True, True, True),
+    (1, 2, 2, 4400, False, [50, 4000, 350], True, False, True),
+]
+
+
+def _fp8_dev(x):
+    import torch
+    from tests.gpu_helpers import dev_u8
+    q8, k8, v8 = dev_u8(x.q_bits), dev_u8(x.k_bits), dev_u8(x.v_bits)
+    ds = [torch.tensor([float(d)], dtype=torch.float32, device="cuda") for d in x.descale]
+    deq = [oracle.e4m3_decode(b) * float(d) for b, d in zip((x.q_bits, x.k_bits, x.v_bits), x.descale)]
+    return (q8, k8, v8), ds, deq
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,causal,lengths,acc,with_out,split", FP8_MERGE_CASES)
+def test_fwd_fp8_merge_step_matches_oracle(B, Hq, Hkv, S, causal, lengths, acc, with_out, split):
+    """attn_fwd_fp8_merge against the oracle's merge of a random running result with the oracle's attention over
+    the dequantised inputs: O rel-L2 <= 5e-2 (the fp8 bound), LSE max-abs <= 1e-3."""
+    import torch
+    from tests.gpu_helpers import TOL_FP8_REL, TOL_LSE, rel_l2
+    lca = _lib()
+    D = 128
+    print(f"fwd_fp8_merge B={B} Hq={Hq} Hkv={Hkv} S={S} causal={causal} lengths={lengths} accumulate={acc} "
+          f"out={with_out} split={split}", flush=True)
+    if split:
+        assert lca.fwd_workspace_bytes(B, Hq, Hkv, S, D) > 0, "case meant to run the key split"
+    x = si.make_inputs(B, Hq, Hkv, S, D, seed=S + 11, lengths=lengths, fp8=True, with_do=False)
+    (q8, k8, v8), ds, (qv, kv, vv) = _fp8_dev(x)
+    rng = np.random.default_rng(S * 5 + 1)
+    o1 = rng.standard_normal((B, S, Hq, D)).astype(np.float32)
+    l1 = rng.uniform(-2.0, 10.0, (B, Hq, S)).astype(np.float32)
+    l1.reshape(-1)[::9] = -np.inf
+    dev = torch.device("cuda")
+    cu = dev_i32(x.cu_seqlens) if x.cu_seqlens is not None else None
+    o_acc = torch.from_numpy(o1.copy()).to(dev)
+    lse_acc = torch.from_numpy(l1.copy()).to(dev)
+    o_out = torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device=dev) if with_out else None
+    scale = 1.0 / np.sqrt(D)
+    lca.fwd_fp8_merge(q8, k8, v8, *ds, o_acc, lse_acc, causal=causal, accumulate=acc, o_out=o_out, cu_seqlens=cu,
+                      scale=scale, split=split)
+    torch.cuda.synchronize()
+    po, pl = oracle.attention_fwd(qv, kv, vv, causal=causal, scale=scale, cu_seqlens=x.cu_seqlens, workers=None)
+    r_o1 = o1.astype(np.float64) if acc else np.zeros_like(o1, dtype=np.float64)
+    r_l1 = l1.astype(np.float64) if acc else np.full(l1.shape, -np.inf)
+    ro, rl = oracle.merge_partials(r_o1, r_l1, po, pl)
+    go, gl = host(o_acc), host(lse_acc)
+    rr, el = rel_l2(go, ro), max_abs(gl, rl)
+    print(f"fwd_fp8_merge O relL2={rr:.3e} LSE maxabs={el:.3e}", flush=True)
+    assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl))
+    assert rr <= TOL_FP8_REL and el <= TOL_LSE
+    if with_out:
+        gb = host(o_out)
+        assert np.max(np.abs(gb - go) - np.abs(go) * 2.0 ** -8) <= 0.0
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,nchunk,causal", [(1, 4, 2, 512, 4, True), (1, 3, 3, 384, 3, False)])
+def test_fp8_ring_forward_equals_full_attention(B, Hq, Hkv, S, nchunk, causal):
+    """A ring of attn_fwd_fp8_merge calls over the chunks equals the oracle's full attention on the dequantised
+    inputs (fp8 bounds)."""
+    import torch
+    from tests.gpu_helpers import TOL_FP8_REL, TOL_LSE, rel_l2
+    lca = _lib()
+    D = 128
+    print(f"fp8 ring B={B} Hq={Hq} Hkv={Hkv} S={S} N={nchunk} causal={causal}", flush=True)
+    x = si.make_inputs(B, Hq, Hkv, S, D, seed=70 + nchunk, fp8=True, with_do=False)
+    (q8, k8, v8), ds, (qv, kv, vv) = _fp8_dev(x)
+    scale = 1.0 / np.sqrt(D)
+    L = S // nchunk
+    o = torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    for r in range(nchunk):
+        qr = q8[:, r * L:(r + 1) * L].contiguous()
+        o_acc = torch.empty((B, L, Hq, D), dtype=torch.float32, device="cuda")
+        l_acc = torch.empty((B, Hq, L), dtype=torch.float32, device="cuda")
+        o_r = torch.empty((B, L, Hq, D), dtype=torch.bfloat16, device="cuda")
+        chunks = list(range(r + 1)) if causal else list(range(nchunk))
+        for i, c in enumerate(chunks):
+            lca.fwd_fp8_merge(qr, k8[:, c * L:(c + 1) * L].contiguous(), v8[:, c * L:(c + 1) * L].contiguous(), *ds,
+                              o_acc, l_acc, causal=(causal and c == r), accumulate=(i > 0), scale=scale,
+                              o_out=o_r if i == len(chunks) - 1 else None)
+        o[:, r * L:(r + 1) * L] = o_r
+        lse[:, :, r * L:(r + 1) * L] = l_acc
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_fwd(qv, kv, vv, causal=causal, scale=scale, workers=None)
+    rr, el = rel_l2(host(o), ro), max_abs(host(lse), rl)
+    print(f"fp8 ring O relL2={rr:.3e} LSE maxabs={el:.3e}", flush=True)
+    assert rr <= TOL_FP8_REL and el <= TOL_LSE

@@ -45,6 +45,7 @@ def test_validate_rejects_malformed_cu_seqlens(monkeypatch):
         calls = [lambda: lca.fwd(q, k, v, causal=True, cu_seqlens=cu),
                  lambda: lca.fwd_fp8(q8, k8, v8, *ds, causal=True, cu_seqlens=cu),
                  lambda: lca.fwd_merge(q, k, v, o_acc, l_acc, causal=True, cu_seqlens=cu),
+                 lambda: lca.fwd_fp8_merge(q8, k8, v8, *ds, o_acc, l_acc, causal=True, cu_seqlens=cu),
                  lambda: lca.bwd(q, k, v, o, lse, do, causal=True, cu_seqlens=cu),
                  lambda: lca.bwd_noalloc(q, k, v, o, lse, do, causal=True, cu_seqlens=cu),
                  lambda: lca.bwd_fp8(q8, k8, v8, *ds, o, lse, do, causal=True, cu_seqlens=cu)]
