@@ -22,7 +22,8 @@ bounded sample of the same workload on the host cores. ``workloads`` holds
 the other configurations measured the same way (mid: bf16 forward; packed32k:
 packed fwd+bwd; fp8_64k: fp8 forward against the fp8 dense peak; ring4_gqa32k:
 the gqa32k forward as a 4-chunk Ring-Attention pass with attn_fwd_merge, the
-same with attn_fwd + attn_merge, and the merge kernel's HBM rate; key_split_1h32k: a small-grid forward with and
+same with attn_fwd + attn_merge, the ring's forward + backward (attn_bwd_accumulate
+per chunk pair), and the merge kernel's HBM rate; key_split_1h32k: a small-grid forward with and
 without the key split; fp8_64k_fwd_bwd: the fp8 forward and its backward).
 ``mfma_ceiling`` is the rate a register-only MFMA loop sustains on the same
 GPU and its clock, the practical ceiling the kernels' fractions compare with.
@@ -394,21 +395,24 @@ def ring_case(nchunk, steps, warmup, dev):
     running fp32 result, in ring order: by attn_fwd_merge itself (the headline
     figure), and for comparison by attn_fwd followed by attn_merge. All
     chunks' work runs on this GPU, so the visible pairs are those of the full
-    causal sequence.
+    causal sequence. ``fwd_bwd`` adds the ring's backward: attn_bwd_accumulate
+    on every (query chunk, key chunk) pair with the query chunk's final O and
+    LSE, summing the gradients in fp32.
     """
     import torch
     import seeded_inputs as si
     import long_context_exact_fwd_amd as lca
     w = si.WORKLOADS["gqa32k"]
-    x = si.workload_inputs(w, with_do=False)
+    x = si.workload_inputs(w, with_do=True)
     up = lca.bf16_from_bits
-    q, k, v = up(x.q_bits, dev), up(x.k_bits, dev), up(x.v_bits, dev)
+    q, k, v, do = up(x.q_bits, dev), up(x.k_bits, dev), up(x.v_bits, dev), up(x.do_bits, dev)
     B, S, Hq, D = q.shape
     L = S // nchunk
     qs = [q[:, r * L:(r + 1) * L].contiguous() for r in range(nchunk)]
     ks = [k[:, c * L:(c + 1) * L].contiguous() for c in range(nchunk)]
     vs = [v[:, c * L:(c + 1) * L].contiguous() for c in range(nchunk)]
-    del q, k, v
+    dos = [do[:, r * L:(r + 1) * L].contiguous() for r in range(nchunk)]
+    del q, k, v, do
     po = torch.empty((B, L, Hq, D), dtype=torch.bfloat16, device=dev)
     pl = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
     o_acc = [torch.empty((B, L, Hq, D), dtype=torch.float32, device=dev) for _ in range(nchunk)]
@@ -436,8 +440,33 @@ def ring_case(nchunk, steps, warmup, dev):
             tm.mark(i, 1)
 
     pairs = _pairs(S, True) * B * Hq
+    # the ring's backward: fp32 gradient sums per chunk, the final O (bf16) and LSE of each query chunk
+    dq_acc = [torch.empty((B, L, Hq, D), dtype=torch.float32, device=dev) for _ in range(nchunk)]
+    dk_acc = [torch.empty(tuple(ks[0].shape), dtype=torch.float32, device=dev) for _ in range(nchunk)]
+    dv_acc = [torch.empty(tuple(vs[0].shape), dtype=torch.float32, device=dev) for _ in range(nchunk)]
+    bws = torch.empty((lca.bwd_workspace_bytes(B, Hq, w.hkv, L, D) + 3) // 4, dtype=torch.float32, device=dev)
+
+    def step_fwd_bwd(tm, i):
+        if tm is not None:
+            tm.mark(i, 0)
+        step_fused(None, i)
+        if tm is not None:
+            tm.mark(i, 1)
+        for r in range(nchunk):
+            # diagonal pair first: it is the first pair of query chunk r and (rows in order) of key chunk r,
+            # so it writes the three sums and every other pair adds to them
+            for c in range(r, -1, -1):
+                lca.bwd_accumulate(qs[r], ks[c], vs[c], o_out[r], l_acc[r], dos[r], dq_acc[r], dk_acc[c], dv_acc[c],
+                                   causal=(c == r), accumulate=(c != r), scale=w.scale, workspace=bws)
+        if tm is not None:
+            tm.mark(i, 2)
+
     ms_f, _ = run_steps(step_fused, ["ring_fwd_merge"], steps, warmup, SECONDARY_WARM_MS)
     tf_f = 4.0 * D * pairs / (ms_f * 1e-3) / 1e12
+    ms_fb, per_fb = run_steps(step_fwd_bwd, ["ring_fwd_merge", "ring_bwd_accumulate"], steps, warmup,
+                              SECONDARY_WARM_MS)
+    tf_fb = 14.0 * D * pairs / (ms_fb * 1e-3) / 1e12
+    del dq_acc, dk_acc, dv_acc, bws
     ms, _ = run_steps(step, ["ring_fwd"], steps, warmup, SECONDARY_WARM_MS)
     tf = 4.0 * D * pairs / (ms * 1e-3) / 1e12
 
@@ -462,6 +491,10 @@ def ring_case(nchunk, steps, warmup, dev):
                   f"N(0,1) seed {w.seed}",
         "tflops": round(tf_f, 2), "pct_of_peak": round(100.0 * tf_f / PEAK_BF16_TFLOPS, 2),
         "peak_tflops": PEAK_BF16_TFLOPS, "ms_per_step": round(ms_f, 4), "steps": steps,
+        "fwd_bwd": {"what": "the fused ring forward, then attn_bwd_accumulate per chunk pair (fp32 gradient sums)",
+                    "tflops": round(tf_fb, 2), "pct_of_peak": round(100.0 * tf_fb / PEAK_BF16_TFLOPS, 2),
+                    "ms_per_step": round(ms_fb, 4), "phases_ms": {n: round(t, 4) for n, t in per_fb.items()},
+                    "flops": "14 D per visible pair, as the gqa32k step"},
         "unfused": {"what": "attn_fwd (bf16 partial O) + attn_merge per chunk pair", "tflops": round(tf, 2),
                     "pct_of_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2), "ms_per_step": round(ms, 4)},
         "merge": {"kernel": "attn_merge_kernel", "bound": "hbm", "avg_launch_ms": round(m_ms, 5),

@@ -162,6 +162,24 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      int causal, const int32_t* cu_seqlens, int num_seqs,
                      float scale, attn_stream_t stream);
 
+/* attn_bwd with fp32 gradient accumulators, for the backward of a
+ * Ring-Attention forward: the gradients of one (query chunk, key chunk) pair,
+ * computed as attn_bwd does from the final o and lse of the query chunk
+ * (Ring-Attention paragraph of the FlashAttention page's sequence-parallel
+ * section: the backward of a ring step is the same recomputation with the
+ * given LSE), are added to running sums instead of being rounded to bf16.
+ * dq_acc float32 [B,S,Hq,D], dk_acc and dv_acc float32 [B,S,Hkv,D], 16-byte
+ * aligned: accumulate = 1 adds the pair's gradients to them, 0 overwrites
+ * them (the first pair). Other arguments and the workspace as attn_bwd.
+ * Every element of the three arrays is read and written by one thread, and
+ * calls on the same arrays must be ordered (one stream). Rounded to bf16, the
+ * result of accumulate = 0 equals attn_bwd's output bit for bit. */
+attn_status attn_bwd_accumulate(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                const void* dout, float* dq_acc, float* dk_acc, float* dv_acc, int accumulate,
+                                void* workspace, int batch, int hq, int hkv, int seqlen, int head_dim,
+                                int causal, const int32_t* cu_seqlens, int num_seqs,
+                                float scale, attn_stream_t stream);
+
 /* One or more of the three backward kernels, in the fixed order Delta, dK/dV,
  * dQ: attn_bwd(...) is attn_bwd_phases(ATTN_BWD_ALL, ...). Running the
  * phases as separate calls on one stream (Delta first) gives bitwise the

@@ -67,6 +67,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_fwd_merge.restype = i
     lib.attn_fwd_fp8_merge.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, vp, i, f, st]
     lib.attn_fwd_fp8_merge.restype = i
+    lib.attn_bwd_accumulate.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, vp, i, f, st]
+    lib.attn_bwd_accumulate.restype = i
     lib.attn_fwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.attn_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
@@ -82,7 +84,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
 
 EXPORTED = ("attn_fwd", "attn_fwd_workspace_bytes", "attn_fwd_fp8", "attn_bwd", "attn_bwd_phases",
             "attn_bwd_workspace_bytes", "attn_bwd_fp8", "attn_bwd_fp8_workspace_bytes", "attn_bwd_noalloc",
-            "attn_merge", "attn_fwd_merge", "attn_fwd_fp8_merge", "attn_status_str", "attn_last_hip_error")
+            "attn_merge", "attn_fwd_merge", "attn_fwd_fp8_merge", "attn_bwd_accumulate", "attn_status_str",
+            "attn_last_hip_error")
 
 BWD_DELTA, BWD_DKDV, BWD_DQ, BWD_ALL = 1, 2, 4, 7
 
@@ -310,6 +313,33 @@ def bwd(q, k, v, o, lse, do, *, causal: bool, cu_seqlens=None, scale: Optional[f
     else:
         _check(load_library().attn_bwd_phases(int(phases), *args), "attn_bwd_phases")
     return dq, dk, dv
+
+
+def bwd_accumulate(q, k, v, o, lse, do, dq_acc, dk_acc, dv_acc, *, causal: bool, accumulate: bool = True,
+                   cu_seqlens=None, scale: Optional[float] = None, workspace=None):
+    """Backward with fp32 accumulators: the gradients are added to dq_acc, dk_acc, dv_acc (or written to them with
+    accumulate=False). Shapes as q, k, v. Returns (dq_acc, dk_acc, dv_acc)."""
+    import torch
+    _check_tensors(q, k, v, o, do, dtype=torch.bfloat16)
+    _check_tensors(lse, dq_acc, dk_acc, dv_acc, dtype=torch.float32)
+    B, S, Hq, Hkv, D, n = _shape(q, k, cu_seqlens)
+    if tuple(dq_acc.shape) != tuple(q.shape) or tuple(dk_acc.shape) != tuple(k.shape) or \
+            tuple(dv_acc.shape) != tuple(v.shape):
+        raise ValueError("dq_acc, dk_acc, dv_acc must have the shapes of q, k, v")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    nbytes = bwd_workspace_bytes(B, Hq, Hkv, S, D)
+    if workspace is None:
+        workspace = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=q.device)
+    elif not (workspace.is_contiguous() and workspace.numel() * workspace.element_size() >= nbytes
+              and workspace.device == q.device):
+        raise ValueError(f"workspace must be a contiguous tensor of at least {nbytes} bytes on {q.device}")
+    st = load_library().attn_bwd_accumulate(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq_acc),
+                                            _ptr(dk_acc), _ptr(dv_acc), int(bool(accumulate)), _ptr(workspace), B, Hq,
+                                            Hkv, S, D, int(bool(causal)), _ptr(cu_seqlens), n, float(scale),
+                                            _stream())
+    _check(st, "attn_bwd_accumulate")
+    return dq_acc, dk_acc, dv_acc
 
 
 def bwd_noalloc(q, k, v, o, lse, do, *, causal: bool, cu_seqlens=None, scale: Optional[float] = None, dq=None,

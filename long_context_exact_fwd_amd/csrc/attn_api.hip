@@ -94,7 +94,7 @@ attn_status bwd_launch(unsigned phases, const void* q, const void* k, const void
                        const void* dout, void* dq, void* dk, void* dv, void* workspace, int head_split, int key_split,
                        int batch, int hq, int hkv, int seqlen, int head_dim, int causal, const int32_t* cu_seqlens,
                        int num_seqs, float scale, hipStream_t stream, const float* descale_q, const float* descale_k,
-                       const float* descale_v) {
+                       const float* descale_v, int accumulate) {
   const attn_status st = validate_cu(cu_seqlens, num_seqs, seqlen, stream);
   if (st != ATTN_OK) return st;
   BwdParams p{};
@@ -104,9 +104,16 @@ attn_status bwd_launch(unsigned phases, const void* q, const void* k, const void
   p.o = static_cast<const __bf16*>(o);
   p.lse = lse;
   p.dout = static_cast<const __bf16*>(dout);
-  p.dq = static_cast<__bf16*>(dq);
-  p.dk = static_cast<__bf16*>(dk);
-  p.dv = static_cast<__bf16*>(dv);
+  if (accumulate >= 0) {
+    p.dq_acc = static_cast<float*>(dq);
+    p.dk_acc = static_cast<float*>(dk);
+    p.dv_acc = static_cast<float*>(dv);
+    p.accumulate = accumulate;
+  } else {
+    p.dq = static_cast<__bf16*>(dq);
+    p.dk = static_cast<__bf16*>(dk);
+    p.dv = static_cast<__bf16*>(dv);
+  }
   p.stat_stride = stat_stride_for(seqlen);
   char* ws = static_cast<char*>(workspace);
   p.delta = reinterpret_cast<float*>(ws);
@@ -417,6 +424,22 @@ attn_status attn_merge(float* o_acc, float* lse_acc, const void* o_part, const f
   p.head_dim = head_dim;
   p.accumulate = accumulate;
   return mi355attn::hip_result(mi355attn::run_merge(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_bwd_accumulate(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                const void* dout, float* dq_acc, float* dk_acc, float* dv_acc, int accumulate,
+                                void* workspace, int batch, int hq, int hkv, int seqlen, int head_dim, int causal,
+                                const int32_t* cu_seqlens, int num_seqs, float scale, attn_stream_t stream) {
+  if (accumulate != 0 && accumulate != 1) return ATTN_ERR_INVALID_ARGUMENT;
+  const attn_status st = mi355attn::bwd_check(ATTN_BWD_ALL, q, k, v, o, lse, dout, dq_acc, dk_acc, dv_acc, workspace,
+                                              true, batch, hq, hkv, seqlen, head_dim, causal, cu_seqlens, num_seqs,
+                                              scale);
+  if (st != ATTN_OK) return st;
+  return mi355attn::bwd_launch(ATTN_BWD_ALL, q, k, v, o, lse, dout, dq_acc, dk_acc, dv_acc, workspace,
+                               mi355attn::bwd_head_split(batch, hq, hkv, seqlen),
+                               mi355attn::bwd_key_split(batch, hq, seqlen), batch, hq, hkv, seqlen, head_dim, causal,
+                               cu_seqlens, num_seqs, scale, reinterpret_cast<hipStream_t>(stream), nullptr, nullptr,
+                               nullptr, accumulate);
 }
 
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,

@@ -172,7 +172,9 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dK / dV
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+// ACC: dK and dV are added to (or written to) the fp32 accumulators of
+// attn_bwd_accumulate instead of being rounded to bf16.
+template <int D, bool CAUSAL, bool ACC>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -526,7 +528,20 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   if (k_ok) {
     const float mul = role == 0 ? 1.0f : dk_mul;
     const size_t row = ((size_t)b * p.seqlen + my_k) * kv_stride + hk * D;
-    if (ns == 1) {
+    if (ACC && ns == 1) {
+      // fp32 accumulators: added to (or written when accumulate = 0)
+      float* dst = (role == 0 ? p.dv_acc : p.dk_acc) + row;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4* cell = reinterpret_cast<f32x4*>(dst + 32 * d + 8 * g + 4 * h);
+          f32x4 w = p.accumulate ? *cell : f32x4{};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] += acc[d][4 * g + e] * mul;
+          *cell = w;
+        }
+    } else if (ns == 1) {
       __bf16* dst = (role == 0 ? p.dv : p.dk) + row;
 #pragma unroll
       for (int d = 0; d < DB; ++d)
@@ -555,7 +570,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV = sum of the head-share partials, rounded to bf16 (head_split > 1)
+// dK, dV = sum of the head-share partials, rounded to bf16 (head_split > 1),
+// or added to the fp32 accumulators of attn_bwd_accumulate
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_reduce_kernel(BwdParams p) {
   const size_t plane = (size_t)p.batch * p.seqlen * p.hkv * p.head_dim;
@@ -567,6 +583,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_reduce_kernel(BwdParams p) 
     const float* src = p.part + (size_t)t * ns * plane + i;
     f32x4 sum = *reinterpret_cast<const f32x4*>(src);
     for (int sp = 1; sp < ns; ++sp) sum += *reinterpret_cast<const f32x4*>(src + (size_t)sp * plane);
+    if (p.dk_acc != nullptr) {
+      f32x4* cell = reinterpret_cast<f32x4*>((t == 0 ? p.dk_acc : p.dv_acc) + i);
+      *cell = p.accumulate ? *cell + sum : sum;
+      continue;
+    }
     bf16x4 w;
 #pragma unroll
     for (int e = 0; e < 4; ++e) w[e] = (__bf16)sum[e];
@@ -577,7 +598,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_reduce_kernel(BwdParams p) 
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+// ACC: dQ is added to (or written to) the fp32 accumulator of
+// attn_bwd_accumulate instead of being rounded to bf16.
+template <int D, bool CAUSAL, bool ACC>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
@@ -777,7 +800,20 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
 
   if (q_ok) {
     const size_t roff = ((size_t)b * p.seqlen + my_q) * q_stride + hq * D;
-    if (nks == 1) {
+    if (ACC && nks == 1) {
+      // fp32 accumulator: added to (or written when accumulate = 0)
+      float* row = p.dq_acc + roff;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4* cell = reinterpret_cast<f32x4*>(row + 32 * d + 8 * g + 4 * h);
+          f32x4 w = p.accumulate ? *cell : f32x4{};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] += acc[d][4 * g + e] * dq_mul;
+          *cell = w;
+        }
+    } else if (nks == 1) {
       __bf16* row = p.dq + roff;
 #pragma unroll
       for (int d = 0; d < DB; ++d)
@@ -805,7 +841,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ = sum of the key-share partials, rounded to bf16 (key_split > 1)
+// dQ = sum of the key-share partials, rounded to bf16 (key_split > 1), or
+// added to the fp32 accumulator of attn_bwd_accumulate
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void attn_bwd_dq_reduce_kernel(BwdParams p) {
   const size_t plane = (size_t)p.batch * p.seqlen * p.hq * p.head_dim;
@@ -814,6 +851,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_reduce_kernel(BwdParams p) {
   const float* src = p.dq_part + i;
   f32x4 sum = *reinterpret_cast<const f32x4*>(src);
   for (int sp = 1; sp < p.key_split; ++sp) sum += *reinterpret_cast<const f32x4*>(src + (size_t)sp * plane);
+  if (p.dq_acc != nullptr) {
+    f32x4* cell = reinterpret_cast<f32x4*>(p.dq_acc + i);
+    *cell = p.accumulate ? *cell + sum : sum;
+    return;
+  }
   bf16x4 w;
 #pragma unroll
   for (int e = 0; e < 4; ++e) w[e] = (__bf16)sum[e];
@@ -874,7 +916,11 @@ hipError_t launch_bwd(const BwdParams& p_in, unsigned phases, hipStream_t stream
   }
   if (phases & kBwdDkDv) {
     dim3 grid(q.batch * q.hkv, q.num_blk * q.head_split);
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL>), grid, dim3(512), 0, stream, q);
+    if (q.dk_acc != nullptr) {
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, true>), grid, dim3(512), 0, stream, q);
+    } else {
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, false>), grid, dim3(512), 0, stream, q);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (q.head_split > 1) {
@@ -886,7 +932,11 @@ hipError_t launch_bwd(const BwdParams& p_in, unsigned phases, hipStream_t stream
   }
   if (phases & kBwdDq) {
     dim3 grid(q.batch * q.hq, q.num_blk * q.key_split);
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), grid, dim3(256), 0, stream, q);
+    if (q.dq_acc != nullptr) {
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL, true>), grid, dim3(256), 0, stream, q);
+    } else {
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL, false>), grid, dim3(256), 0, stream, q);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (q.key_split > 1) {

@@ -91,6 +91,13 @@ struct BwdParams {
   const float* descale_q;
   const float* descale_k;
   const float* descale_v;
+  // attn_bwd_accumulate, when dq_acc is not null: fp32 dQ, dK, dV [shapes of
+  // q, k, v] that the gradients are added to (accumulate = 1) or written to
+  // (accumulate = 0) instead of the bf16 outputs
+  float* dq_acc;
+  float* dk_acc;
+  float* dv_acc;
+  int accumulate;
 };
 
 // Forward block geometry, picked from the sizes (the tiling matched to the
@@ -163,7 +170,9 @@ attn_status bwd_launch(unsigned phases, const void* q, const void* k, const void
                        const void* dout, void* dq, void* dk, void* dv, void* workspace, int head_split, int key_split,
                        int batch, int hq, int hkv, int seqlen, int head_dim, int causal, const int32_t* cu_seqlens,
                        int num_seqs, float scale, hipStream_t stream, const float* descale_q = nullptr,
-                       const float* descale_k = nullptr, const float* descale_v = nullptr);
+                       const float* descale_k = nullptr, const float* descale_v = nullptr, int accumulate = -1);
+// accumulate >= 0: dq, dk, dv are fp32 arrays the gradients are added to (1)
+// or written to (0) instead of bf16 outputs (attn_bwd_accumulate).
 
 // fp8 backward workspace: the bf16 copies of the E4M3 codes of Q, K and V,
 // each 256-byte aligned, then the bf16 backward's workspace.

@@ -134,6 +134,16 @@ def _fp8_merge(**kw):
                                                  a["D"], a["causal"], a["cu"], a["n"], a["scale"], S0)
 
 
+def _bwd_acc(**kw):
+    """attn_bwd_accumulate with dq, dk, dv standing for the fp32 accumulators."""
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, acc=1, ws=P, B=1, Hq=4, Hkv=2, S=128, D=128, causal=1,
+             cu=NULL, n=0, scale=0.088)
+    a.update(kw)
+    return lca.load_library().attn_bwd_accumulate(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                                                  a["dv"], a["acc"], a["ws"], a["B"], a["Hq"], a["Hkv"], a["S"],
+                                                  a["D"], a["causal"], a["cu"], a["n"], a["scale"], S0)
+
+
 BAD = [
     dict(q=NULL), dict(lse=NULL), dict(B=0), dict(Hq=0), dict(Hkv=0), dict(S=0), dict(S=-5), dict(D=0),
     dict(Hq=6, Hkv=4), dict(causal=2), dict(scale=0.0), dict(scale=-1.0), dict(scale=float("inf")),
@@ -149,9 +159,11 @@ def test_invalid_arguments_rejected(kw):
     assert _fp8(**kw) == lca.ATTN_ERR_INVALID_ARGUMENT
     assert _fwd_merge(**kw) == lca.ATTN_ERR_INVALID_ARGUMENT
     assert _fp8_merge(**kw) == lca.ATTN_ERR_INVALID_ARGUMENT
+    assert _bwd_acc(**kw) == lca.ATTN_ERR_INVALID_ARGUMENT
 
 
-@pytest.mark.parametrize("fn,kw", [(_fp8_merge, dict(out=PM)), (_fp8_merge, dict(acc=2)), (_fp8_merge, dict(dv=NULL)),
+@pytest.mark.parametrize("fn,kw", [(_bwd_acc, dict(acc=2)), (_bwd_acc, dict(acc=-1)), (_bwd_acc, dict(ws=NULL)),
+                                   (_bwd_acc, dict(dk=NULL)), (_bwd_acc, dict(dq=PM)), (_bwd_acc, dict(ws=PM)),(_fp8_merge, dict(out=PM)), (_fp8_merge, dict(acc=2)), (_fp8_merge, dict(dv=NULL)),
                                    (_fp8_merge, dict(lse=ctypes.c_void_p((1 << 20) + 2))),
                                    (_fp8_merge, dict(dq=ctypes.c_void_p((1 << 20) + 2))), (_fp8_merge, dict(ws=PM)),(_fwd_merge, dict(out=PM)), (_fwd_merge, dict(acc=2)), (_fwd_merge, dict(acc=-1)),
                                    (_fwd_merge, dict(lse=ctypes.c_void_p((1 << 20) + 2))),
@@ -171,6 +183,7 @@ def test_unsupported_head_dims(D):
     assert _fwd_merge(D=D) == lca.ATTN_ERR_UNSUPPORTED
     assert _fp8_merge(D=D) == lca.ATTN_ERR_UNSUPPORTED
     assert _fp8_merge(D=64) == lca.ATTN_ERR_UNSUPPORTED
+    assert _bwd_acc(D=D) == lca.ATTN_ERR_UNSUPPORTED
 
 
 def test_binding_raises_without_library(tmp_path):
@@ -205,6 +218,7 @@ def test_oversized_requests_unsupported():
     assert _fp8(**big) == lca.ATTN_ERR_UNSUPPORTED
     assert _fwd_merge(**big) == lca.ATTN_ERR_UNSUPPORTED
     assert _fp8_merge(**big) == lca.ATTN_ERR_UNSUPPORTED
+    assert _bwd_acc(**big) == lca.ATTN_ERR_UNSUPPORTED
     lib = lca.load_library()
     assert lib.attn_bwd_workspace_bytes(1, 16, 4, 1 << 20, 128) == 0
     # merge: more than 2^40 elements in total

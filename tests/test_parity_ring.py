@@ -16,7 +16,13 @@
   with the oracle's attention (causal or not, GQA, packed, the key split whose
   combine does the merge, accumulate off, the bf16 copy), rows with fewer
   than 64 visible keys to fp32 accuracy; and the whole ring built from it,
-  forward and backward, as above.
+  forward and backward (the backward with attn_bwd_accumulate), as above;
+* attn_fwd_fp8_merge, one step and an fp8 ring, against the oracle on the
+  dequantised inputs;
+* attn_bwd_accumulate against attn_bwd: with accumulate off its fp32 result
+  rounds to attn_bwd's bf16 output bit for bit, and with accumulate on it is
+  the running sum plus that result (one fp32 rounding), with and without the
+  head and key splits.
 """
 import numpy as np
 import pytest
@@ -155,6 +161,27 @@ def ring_backward(q, k, v, o, lse, do, nchunk, causal, scale):
     return dq, dk, dv
 
 
+def ring_backward_accumulate(q, k, v, o, lse, do, nchunk, causal, scale):
+    """ring_backward with attn_bwd_accumulate: each pair's gradients are added to per-chunk fp32 sums by the
+    kernels (sums start at zero; accumulate=False is covered on its own below)."""
+    import torch
+    lca = _lib()
+    B, S, Hq, D = q.shape
+    L = S // nchunk
+    dq_c = [torch.zeros((B, L, Hq, D), dtype=torch.float32, device=q.device) for _ in range(nchunk)]
+    dk_c = [torch.zeros((B, L) + tuple(k.shape[2:]), dtype=torch.float32, device=q.device) for _ in range(nchunk)]
+    dv_c = [torch.zeros((B, L) + tuple(v.shape[2:]), dtype=torch.float32, device=q.device) for _ in range(nchunk)]
+    for r in range(nchunk):
+        rs = slice(r * L, (r + 1) * L)
+        qr, orr, dor = q[:, rs].contiguous(), o[:, rs].contiguous(), do[:, rs].contiguous()
+        lr = lse[:, :, rs].contiguous()
+        for c in (range(r + 1) if causal else range(nchunk)):
+            cs = slice(c * L, (c + 1) * L)
+            lca.bwd_accumulate(qr, k[:, cs].contiguous(), v[:, cs].contiguous(), orr, lr, dor, dq_c[r], dk_c[c],
+                               dv_c[c], causal=(causal and c == r), accumulate=True, scale=scale)
+    return torch.cat(dq_c, dim=1), torch.cat(dk_c, dim=1), torch.cat(dv_c, dim=1)
+
+
 RING_CASES = [
     # B, Hq, Hkv, S, D, nchunk, causal
     (1, 4, 2, 512, 128, 2, True),
@@ -176,7 +203,7 @@ def test_ring_forward_and_backward_equal_full_attention(B, Hq, Hkv, S, D, nchunk
     qv, kv, vv = x.values("q"), x.values("k"), x.values("v")
     ro, rl = oracle.attention_fwd(qv, kv, vv, causal=causal, scale=scale, workers=None)
     check_fwd(host(o), host(lse), ro, rl, tag="ring fwd")
-    dq, dk, dv = ring_backward(q, k, v, o, lse, do, nchunk, causal, scale)
+    dq, dk, dv = (ring_backward_accumulate if fused else ring_backward)(q, k, v, o, lse, do, nchunk, causal, scale)
     torch.cuda.synchronize()
     rq, rk, rv = oracle.attention_bwd(qv, kv, vv, x.values("do"), causal=causal, scale=scale, workers=None)
     check_grads([("dQ", host(dq), rq), ("dK", host(dk), rk), ("dV", host(dv), rv)], tag="ring bwd")
@@ -368,3 +395,37 @@ def test_fp8_ring_forward_equals_full_attention(B, Hq, Hkv, S, nchunk, causal):
     rr, el = rel_l2(host(o), ro), max_abs(host(lse), rl)
     print(f"fp8 ring O relL2={rr:.3e} LSE maxabs={el:.3e}", flush=True)
     assert rr <= TOL_FP8_REL and el <= TOL_LSE
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,D,causal,lengths", [
+    (1, 4, 2, 300, 128, True, None),           # both splits (partials + reduce kernels)
+    (2, 3, 1, 200, 64, False, None),
+    (1, 2, 2, 500, 128, True, [120, 380]),
+    (8, 8, 8, 2048, 128, True, None),          # no split: the kernels' own epilogues
+])
+def test_bwd_accumulate_matches_bwd(B, Hq, Hkv, S, D, causal, lengths):
+    import torch
+    lca = _lib()
+    print(f"bwd_accumulate B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} causal={causal} lengths={lengths}", flush=True)
+    x = si.make_inputs(B, Hq, Hkv, S, D, seed=S + 3, lengths=lengths)
+    q, k, v, do = dev_bf16(x.q_bits), dev_bf16(x.k_bits), dev_bf16(x.v_bits), dev_bf16(x.do_bits)
+    cu = dev_i32(x.cu_seqlens) if x.cu_seqlens is not None else None
+    scale = 1.0 / np.sqrt(D)
+    o, lse = lca.fwd(q, k, v, causal=causal, cu_seqlens=cu, scale=scale)
+    ref = lca.bwd(q, k, v, o, lse, do, causal=causal, cu_seqlens=cu, scale=scale)
+    acc = [torch.full(t.shape, float("nan"), dtype=torch.float32, device=t.device) for t in ref]
+    lca.bwd_accumulate(q, k, v, o, lse, do, *acc, causal=causal, accumulate=False, cu_seqlens=cu, scale=scale)
+    torch.cuda.synchronize()
+    for a, r, name in zip(acc, ref, ("dQ", "dK", "dV")):
+        assert torch.equal(a.to(torch.bfloat16), r), f"{name}: accumulate=False does not round to attn_bwd's output"
+    g = torch.Generator(device="cpu").manual_seed(S)
+    init = [torch.randn(t.shape, generator=g).to(t.device) for t in acc]
+    run = [t.clone() for t in init]
+    lca.bwd_accumulate(q, k, v, o, lse, do, *run, causal=causal, accumulate=True, cu_seqlens=cu, scale=scale)
+    torch.cuda.synchronize()
+    for a, i0, r0, name in zip(run, init, acc, ("dQ", "dK", "dV")):
+        want = i0 + r0
+        bound = (i0.abs() + r0.abs()) * 2.0 ** -23 + 1e-30
+        excess = float(((a - want).abs() - bound).max())
+        print(f"{name} accumulate=True max excess over one fp32 rounding {excess:.3e}", flush=True)
+        assert excess <= 0.0, name

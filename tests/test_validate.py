@@ -48,6 +48,9 @@ def test_validate_rejects_malformed_cu_seqlens(monkeypatch):
                  lambda: lca.fwd_fp8_merge(q8, k8, v8, *ds, o_acc, l_acc, causal=True, cu_seqlens=cu),
                  lambda: lca.bwd(q, k, v, o, lse, do, causal=True, cu_seqlens=cu),
                  lambda: lca.bwd_noalloc(q, k, v, o, lse, do, causal=True, cu_seqlens=cu),
+                 lambda: lca.bwd_accumulate(q, k, v, o, lse, do, torch.zeros_like(q, dtype=torch.float32),
+                                            torch.zeros_like(k, dtype=torch.float32),
+                                            torch.zeros_like(v, dtype=torch.float32), causal=True, cu_seqlens=cu),
                  lambda: lca.bwd_fp8(q8, k8, v8, *ds, o, lse, do, causal=True, cu_seqlens=cu)]
         for call in calls:
             with pytest.raises(lca.AttnError) as err:
