@@ -13,9 +13,10 @@
 //     each 32 keys: wave A holds K, computes S and P and accumulates dV^T;
 //     wave B holds V, computes dP and, with A's P handed over through LDS,
 //     dS and dK^T. Each wave then needs one accumulator and one operand set,
-//     under 256 VGPRs, so two waves run per SIMD. B runs one step behind A,
-//     so within a step the two are independent and each one's VALU work can
-//     hide under the other's MFMAs. The loop covers every query head of the
+//     within 256 VGPRs, so two waves run per SIMD. B's dS and dK trail A's P
+//     by one step, so within a step the two are independent, and their MFMA
+//     and VALU phases alternate (one wave's exponentials or dS run under the
+//     other's MFMAs). The loop covers every query head of the
 //     GQA group and every visible 64-query tile, so the group sum needs no
 //     reduction across workgroups.
 //   * dQ: the forward's layout (4 waves of 32 queries, two workgroups per CU):
