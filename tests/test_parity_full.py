@@ -223,3 +223,47 @@ def test_fp8_64k_full_forward_backward_sampled():
     print(f"fp8_64k bwd: dQ relL2={e_q:.3e} ({len(picks)} rows); |sum dK|/|dK|={sk:.3e}; sum dV vs sum dO "
           f"relL2={sv:.3e}", flush=True)
     assert e_q <= TOL_FP8_REL and sk <= TOL_FP8_REL and sv <= 1e-2
+
+
+def test_ring4_gqa32k_full_forward_backward_sampled():
+    """The gqa32k workload as a 4-chunk Ring-Attention pass on one GPU, as bench.py times it: the forward with
+    attn_fwd_merge per (query chunk, key chunk <= it) and the backward with attn_bwd_accumulate per pair.
+    Sampled forward rows, dQ rows and one kv group's dK/dV keys against the oracle (bars as above), and the
+    whole fp32 gradients against the one-shot attn_bwd (rel-L2 <= 1e-2 per tensor)."""
+    import torch
+    import long_context_exact_fwd_amd as lca
+    from tests.test_parity_ring import ring_backward_accumulate, ring_forward_fused
+    w = si.WORKLOADS["gqa32k"]
+    nchunk = 4
+    print(f"full-size ring case gqa32k in {nchunk} chunks: B={w.batch} Hq={w.hq} Hkv={w.hkv} S={w.seqlen}", flush=True)
+    x = si.workload_inputs(w, with_do=True)
+    q, k, v = _upload(x)
+    do = lca.bf16_from_bits(x.do_bits, "cuda")
+    o, lse = ring_forward_fused(q, k, v, nchunk, True, w.scale)
+    dq, dk, dv = ring_backward_accumulate(q, k, v, o, lse, do, nchunk, True, w.scale)
+    gq1, gk1, gv1 = lca.bwd(q, k, v, o, lse, do, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    print("ring gqa32k: GPU done", flush=True)
+    o_h, lse_h = host(o), host(lse)
+    rows = _sample_rows(w, None, w.seed + 21, 128)
+    # rows around each chunk boundary too: their first key chunk is the diagonal one
+    L = w.seqlen // nchunk
+    rows = np.unique(np.concatenate([rows, [r * L + d for r in range(1, nchunk) for d in (-1, 0, 1, 63, 64)]]))
+    heads = _sample_heads(w.hq, w.seed + 21)
+    picks = [(0, int(h), int(i)) for h in heads for i in rows]
+    qv, kv, vv = _forward_rows_check(w, x, o_h, lse_h, picks, tag=f"ring gqa32k fwd ({len(picks)} rows)")
+    dov = x.values("do")
+    dq_h, dk_h, dv_h = host(dq), host(dk), host(dv)
+    rq = oracle.attention_dq_rows(qv, kv, vv, dov, picks, causal=True, scale=w.scale)
+    e_q = rel_l2(np.stack([dq_h[b, i, h] for b, h, i in picks]), rq)
+    kvh = int(si.sample_indices(w.seed + 23, w.hkv, 1)[0])
+    keys = _sample_rows(w, None, w.seed + 25, 128)
+    kpicks = [(0, kvh, int(j)) for j in keys]
+    rk, rv = oracle.attention_dkdv_rows(qv, kv, vv, dov, kpicks, causal=True, scale=w.scale)
+    e_k = rel_l2(np.stack([dk_h[b, j, h] for b, h, j in kpicks]), rk)
+    e_v = rel_l2(np.stack([dv_h[b, j, h] for b, h, j in kpicks]), rv)
+    one = [rel_l2(a, host(r)) for a, r in ((dq_h, gq1), (dk_h, gk1), (dv_h, gv1))]
+    print(f"ring gqa32k bwd sampled: dQ relL2={e_q:.3e} dK relL2={e_k:.3e} dV relL2={e_v:.3e}; against the one-shot "
+          f"backward: dQ {one[0]:.3e} dK {one[1]:.3e} dV {one[2]:.3e}", flush=True)
+    assert np.all(np.isfinite(dq_h)) and np.all(np.isfinite(dk_h)) and np.all(np.isfinite(dv_h))
+    assert max(e_q, e_k, e_v) <= TOL_GRAD_REL and max(one) <= TOL_GRAD_REL
