@@ -7,9 +7,14 @@ C ABI:
 * attn_bwd: dQ, dK, dV rel-L2 <= 1e-2 (check_grads);
 * attn_fwd_merge: one ring step into a random running result, against the
   oracle's merge;
-* attn_bwd_accumulate (accumulate off): rounds to attn_bwd's output bit for bit.
+* attn_bwd_accumulate (accumulate off): rounds to attn_bwd's output bit for bit;
+and the head-dim-128 draws through attn_fwd_fp8, attn_bwd_fp8 and
+attn_fwd_fp8_merge against the oracle on the dequantised inputs.
 The draws are fixed by the seed, so a failure names a reproducible case.
+ATTN_SWEEP_CASES=N widens the sweep to the first N draws.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -38,7 +43,8 @@ def _draw(i):
     return B, g * hkv, hkv, S, D, causal, lengths
 
 
-CASES = [_draw(i) for i in range(24)]
+# 24 cases by default; ATTN_SWEEP_CASES=N runs the first N draws (the same 24 first)
+CASES = [_draw(i) for i in range(int(os.environ.get("ATTN_SWEEP_CASES", "24")))]
 
 
 @pytest.mark.parametrize("case", range(len(CASES)))
@@ -75,3 +81,63 @@ def test_sweep_case(case):
     torch.cuda.synchronize()
     mo, ml = oracle.merge_partials(o1.astype(np.float64), l1.astype(np.float64), ro, rl)
     check_fwd(host(o_acc), host(l_acc), mo, ml, tag="fwd_merge")
+
+
+FP8_CASES = [c for c in CASES if c[4] == 128][: max(8, len(CASES) // 3)]
+
+
+@pytest.mark.parametrize("case", range(len(FP8_CASES)))
+def test_sweep_fp8_case(case):
+    """The head-dim-128 draws through the fp8 entry points: attn_fwd_fp8 (O rel-L2 <= 5e-2, LSE <= 1e-3),
+    attn_bwd_fp8 from the exact O (rel-L2 <= 1e-2) and attn_fwd_fp8_merge (fp8 bounds), against the oracle on the
+    dequantised inputs."""
+    import torch
+    import long_context_exact_fwd_amd as lca
+    from tests.gpu_helpers import TOL_FP8_REL, TOL_LSE, dev_u8, max_abs, rel_l2
+    B, Hq, Hkv, S, D, causal, lengths = FP8_CASES[case]
+    print(f"fp8 sweep {case}: B={B} Hq={Hq} Hkv={Hkv} S={S} causal={causal} lengths={lengths}", flush=True)
+    x = si.make_inputs(B, Hq, Hkv, S, D, seed=4000 + case, lengths=lengths, fp8=True)
+    q8, k8, v8 = dev_u8(x.q_bits), dev_u8(x.k_bits), dev_u8(x.v_bits)
+    ds = [torch.tensor([float(d)], dtype=torch.float32, device="cuda") for d in x.descale]
+    cu = dev_i32(x.cu_seqlens) if x.cu_seqlens is not None else None
+    scale = 1.0 / np.sqrt(D)
+    qv, kv, vv = (oracle.e4m3_decode(b) * float(d) for b, d in zip((x.q_bits, x.k_bits, x.v_bits), x.descale))
+    ro, rl = oracle.attention_fwd(qv, kv, vv, causal=causal, scale=scale, cu_seqlens=x.cu_seqlens, workers=None)
+    o, lse = lca.fwd_fp8(q8, k8, v8, *ds, causal=causal, cu_seqlens=cu, scale=scale)
+    torch.cuda.synchronize()
+    e_o, e_l = rel_l2(host(o), ro), max_abs(host(lse), rl)
+    print(f"fp8 fwd O relL2={e_o:.3e} LSE maxabs={e_l:.3e}", flush=True)
+    assert e_o <= TOL_FP8_REL and e_l <= TOL_LSE
+    # backward from the exact O rounded to bf16 and the exact LSE: the gradient of the dequantised attention
+    o_ex = torch.from_numpy(ro).to(torch.bfloat16).cuda()
+    lse_ex = torch.from_numpy(rl).to(torch.float32).cuda()
+    do = dev_bf16(x.do_bits)
+    dq, dk, dv = lca.bwd_fp8(q8, k8, v8, *ds, o_ex, lse_ex, do, causal=causal, cu_seqlens=cu, scale=scale)
+    torch.cuda.synchronize()
+    dov = x.values("do")
+    rq, rk, rv = oracle.attention_bwd(qv, kv, vv, dov, causal=causal, scale=scale, cu_seqlens=x.cu_seqlens,
+                                      workers=None)
+    if np.any(rq != 0):
+        check_grads([("dQ", host(dq), rq), ("dK", host(dk), rk), ("dV", host(dv), rv)], tag="fp8 bwd")
+    else:
+        # every row sees one key (S = 1 or segments of length 1 with the causal mask): the exact dQ and dK are
+        # zero, and what the kernel returns is the effect of the bf16 rounding of the O it is given. With
+        # delta_i = sum_d |dO_id (O_id - bf16(O_id))| the error of Delta_i, |dS_ij| <= delta_i + fp32 noise,
+        # so |dQ|, |dK| <= scale * max delta * max(|K|, |Q|), plus the 1e-3 of the zero-reference bound.
+        o_b = host(o_ex)
+        dmax = float(np.max(np.sum(np.abs(dov * (ro - o_b)), axis=-1)))
+        bound = 1e-3 + scale * dmax * float(max(np.abs(kv).max(), np.abs(qv).max()))
+        e_q, e_k, e_v = max_abs(host(dq), rq), max_abs(host(dk), rk), rel_l2(host(dv), rv)
+        print(f"fp8 bwd (one key per row): dQ maxabs={e_q:.3e} dK maxabs={e_k:.3e} bound {bound:.3e}, "
+              f"dV relL2={e_v:.3e}", flush=True)
+        assert e_q <= bound and e_k <= bound and e_v <= 1e-2
+    rng = np.random.default_rng(5000 + case)
+    o1 = rng.standard_normal((B, S, Hq, D)).astype(np.float32)
+    l1 = rng.uniform(-2.0, 8.0, (B, Hq, S)).astype(np.float32)
+    o_acc, l_acc = torch.from_numpy(o1.copy()).cuda(), torch.from_numpy(l1.copy()).cuda()
+    lca.fwd_fp8_merge(q8, k8, v8, *ds, o_acc, l_acc, causal=causal, accumulate=True, cu_seqlens=cu, scale=scale)
+    torch.cuda.synchronize()
+    mo, ml = oracle.merge_partials(o1.astype(np.float64), l1.astype(np.float64), ro, rl)
+    e_mo, e_ml = rel_l2(host(o_acc), mo), max_abs(host(l_acc), ml)
+    print(f"fp8 fwd_merge O relL2={e_mo:.3e} LSE maxabs={e_ml:.3e}", flush=True)
+    assert e_mo <= TOL_FP8_REL and e_ml <= TOL_LSE
