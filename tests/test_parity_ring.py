@@ -429,3 +429,27 @@ def test_bwd_accumulate_matches_bwd(B, Hq, Hkv, S, D, causal, lengths):
         excess = float(((a - want).abs() - bound).max())
         print(f"{name} accumulate=True max excess over one fp32 rounding {excess:.3e}", flush=True)
         assert excess <= 0.0, name
+
+
+@pytest.mark.parametrize("qk_std,lse_span", [(1.0, 100.0), (3.0, 30.0)])
+def test_fwd_merge_extreme_weights(qk_std, lse_span):
+    """attn_fwd_merge where the running LSE is far above or below the new part's (weights that underflow to 0 on
+    either side) and, with Q and K scaled by 3, peaky rows that take the tiled kernel's lazy rescale before the
+    merge. Bars as the other forward tests (the O max-abs budget doubled for the scaled inputs, as in the
+    forward stress test)."""
+    import torch
+    lca = _lib()
+    B, Hq, Hkv, S, D = 1, 4, 2, 700, 128
+    print(f"fwd_merge extreme qk_std={qk_std} lse_span={lse_span}", flush=True)
+    x = si.make_inputs(B, Hq, Hkv, S, D, seed=77, with_do=False, qk_std=qk_std)
+    rng = np.random.default_rng(78)
+    o1 = rng.standard_normal((B, S, Hq, D)).astype(np.float32)
+    l1 = rng.uniform(-lse_span, lse_span, (B, Hq, S)).astype(np.float32)
+    q, k, v = dev_bf16(x.q_bits), dev_bf16(x.k_bits), dev_bf16(x.v_bits)
+    o_acc, l_acc = torch.from_numpy(o1.copy()).cuda(), torch.from_numpy(l1.copy()).cuda()
+    scale = 1.0 / np.sqrt(D)
+    lca.fwd_merge(q, k, v, o_acc, l_acc, causal=True, accumulate=True, scale=scale)
+    torch.cuda.synchronize()
+    po, pl = oracle.attention_fwd(x.values("q"), x.values("k"), x.values("v"), causal=True, scale=scale, workers=None)
+    ro, rl = oracle.merge_partials(o1.astype(np.float64), l1.astype(np.float64), po, pl)
+    check_fwd(host(o_acc), host(l_acc), ro, rl, tag="fwd_merge extreme", abs_factor=2.0 if qk_std != 1.0 else 1.0)
