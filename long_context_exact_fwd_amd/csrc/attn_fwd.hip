@@ -32,6 +32,10 @@
 //   * Key split (grids too small to fill the GPU, chosen on the host): the key
 //     tiles of a query block are shared over key_split workgroups, which write
 //     fp32 partial results; attn_fwd_combine_kernel merges them.
+//   * Ring merge (attn_fwd_merge): the same kernels, with epilogues that fold
+//     the call's result into a running fp32 (O, LSE) (the Ring-Attention
+//     paragraph of the page's sequence-parallel section accumulates partial
+//     results per arriving K/V block) instead of writing O and LSE.
 #include "attn_device.h"
 #include "attn_internal.h"
 
