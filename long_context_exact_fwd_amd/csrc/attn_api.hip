@@ -66,6 +66,12 @@ int fwd_block_waves_env() {
   return atoi(env);
 }
 
+int bwd_dq_waves_env() {
+  const char* env = getenv("ATTN_DQ_WAVES");
+  if (env == nullptr) return 0;
+  return atoi(env);
+}
+
 attn_status hip_result(hipError_t e) {
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
@@ -121,6 +127,7 @@ attn_status bwd_launch(unsigned phases, const void* q, const void* k, const void
   p.order = reinterpret_cast<int*>(ws + bwd_order_offset(batch, hq, seqlen));
   p.head_split = head_split;
   p.key_split = key_split;
+  p.dq_waves = bwd_dq_block_waves(seqlen, head_dim, causal, cu_seqlens != nullptr, key_split);
   p.part = head_split > 1 ? reinterpret_cast<float*>(ws + bwd_part_offset(batch, hq, seqlen, head_split, key_split))
                           : nullptr;
   p.dq_part = key_split > 1 ? reinterpret_cast<float*>(ws + bwd_dq_part_offset(batch, hq, hkv, seqlen, head_dim,

@@ -19,8 +19,9 @@
 //     other's MFMAs). The loop covers every query head of the
 //     GQA group and every visible 64-query tile, so the group sum needs no
 //     reduction across workgroups.
-//   * dQ: the forward's layout (4 waves of 32 queries, two workgroups per CU):
-//     Q and dO stay in VGPRs, K and V tiles stream through LDS.
+//   * dQ: the forward's layout (waves of 32 queries; 4 per workgroup, two
+//     workgroups per CU, or 8, one per CU, by the sizes): Q and dO stay in
+//     VGPRs, K and V tiles stream through LDS.
 // Tiles reach LDS through buffer loads that write LDS directly; rows past the
 // sequence end read as zeros and are masked.
 #include "attn_device.h"
@@ -34,8 +35,9 @@ constexpr int kQT = 64;  // queries per tile (dK/dV pass)
 constexpr int kKT = 64;  // keys per tile (dQ pass)
 
 // ---------------------------------------------------------------------------
-// Work order. The dK/dV and dQ passes run one workgroup per 128-row block
-// (dK/dV: per block and share of the group's query heads), and a workgroup's
+// Work order. The dK/dV pass runs one workgroup per 128-row key block and
+// share of the group's query heads, the dQ pass one per 128- or 256-row query
+// block (dq_waves) and share of its key tiles, and a workgroup's
 // cost is the number of 64-row tiles of the other operand it visits, times
 // its heads. Under a causal or packed mask the costs differ by up to the
 // longest segment over the tile size, and with a few workgroups per CU the
@@ -45,8 +47,9 @@ constexpr int kKT = 64;  // keys per tile (dQ pass)
 // ---------------------------------------------------------------------------
 template <bool CAUSAL>
 __device__ int block_tiles(const BwdParams& p, int pass, int blk) {
-  const int r0 = blk * 128;
-  const int r1 = min(r0 + 128, p.seqlen) - 1;
+  const int rows = pass == 1 ? 32 * p.dq_waves : 128;
+  const int r0 = blk * rows;
+  const int r1 = min(r0 + rows, p.seqlen) - 1;
   int s0a, s1a, s0b, s1b;
   segment_of(p.cu_seqlens, p.num_seqs, p.seqlen, r0, s0a, s1a);
   segment_of(p.cu_seqlens, p.num_seqs, p.seqlen, r1, s0b, s1b);
@@ -76,7 +79,7 @@ __device__ int entry_cost(const BwdParams& p, int pass, int e) {
 template <bool CAUSAL>
 __device__ void block_order(const BwdParams& p, int wg) {
   __shared__ int cost[256];
-  const int n0 = p.num_blk * p.head_split, n1 = p.num_blk * p.key_split;
+  const int n0 = p.num_blk * p.head_split, n1 = p.num_dq_blk * p.key_split;
   const int c0 = (n0 + 255) / 256;
   const int pass = wg < c0 ? 0 : 1;
   const int n = pass == 0 ? n0 : n1;
@@ -99,7 +102,7 @@ __device__ void block_order(const BwdParams& p, int wg) {
 
 // ---------------------------------------------------------------------------
 // Delta_i = dO_i . O_i and LSE_i * log2(e), both fp32 [B, Hq, S]; the last
-// ceil(num_blk * head_split / 256) + ceil(num_blk * key_split / 256)
+// ceil(num_blk * head_split / 256) + ceil(num_dq_blk * key_split / 256)
 // workgroups write the work order instead.
 // ---------------------------------------------------------------------------
 // Rows per thread of the Delta kernel: all their loads are issued before the
@@ -601,17 +604,20 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_reduce_kernel(BwdParams p) 
 // ---------------------------------------------------------------------------
 // ACC: dQ is added to (or written to) the fp32 accumulator of
 // attn_bwd_accumulate instead of being rounded to bf16.
-template <int D, bool CAUSAL, bool ACC>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
+// WAVES waves of 32 queries per workgroup: 4 (128-query blocks, two
+// workgroups per CU) or 8 (256-query blocks, one per CU sharing each K/V
+// tile); bwd_dq_block_waves() picks one.
+template <int D, bool CAUSAL, bool ACC, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void attn_bwd_dq_kernel(BwdParams p) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int TILE = kKT * D;
-  constexpr int NI = TILE * 2 / (4 * 1024);
+  constexpr int NI = TILE * 2 / (WAVES * 1024);
   __shared__ __attribute__((aligned(1024))) __bf16 k_lds0[TILE];  // dual layout: rows and K^T reads
   __shared__ __attribute__((aligned(1024))) __bf16 k_lds1[TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 v_lds0[TILE];  // row reads only
   __shared__ __attribute__((aligned(1024))) __bf16 v_lds1[TILE];
-  __shared__ int red[2][4];
+  __shared__ int red[2][WAVES];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -625,10 +631,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   const int hk = hq / (p.hq / p.hkv);
   const int nks = p.key_split;
   const int qentry =
-      (int)min((unsigned)p.order[p.num_blk * p.head_split + blockIdx.y], (unsigned)(p.num_blk * nks - 1));
+      (int)min((unsigned)p.order[p.num_blk * p.head_split + blockIdx.y], (unsigned)(p.num_dq_blk * nks - 1));
   const int qblk = __builtin_amdgcn_readfirstlane(qentry / nks);
   const int ksplit = __builtin_amdgcn_readfirstlane(qentry - qblk * nks);
-  const int my_q = qblk * 128 + wave * 32 + n;
+  const int my_q = qblk * (32 * WAVES) + wave * 32 + n;
   const bool q_ok = my_q < p.seqlen;
   const int q_stride = p.hq * D;
   const int kv_stride = p.hkv * D;
@@ -653,7 +659,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   __syncthreads();
   int wg_lo = INT32_MAX, wg_hi = INT32_MIN;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < WAVES; ++w) {
     wg_lo = min(wg_lo, red[0][w]);
     wg_hi = max(wg_hi, red[1][w]);
   }
@@ -698,7 +704,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
   uint32_t ld_koff[NI], ld_voff[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int e = tile_dma_elem(i, 4, wave, lane);
+    const int e = tile_dma_elem(i, WAVES, wave, lane);
     ld_koff[i] = dma_src_dual<D>(e, kv_stride);
     ld_voff[i] = dma_src_b128<D>(e, kv_stride);
   }
@@ -710,7 +716,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(BwdParams p) {
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + (size_t)t0 * kv_stride, nbytes);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int el = tile_dma_elem(i, 4, wave, 0);
+      const int el = tile_dma_elem(i, WAVES, wave, 0);
       dma16_buf(rk, ld_koff[i], kd + el);
       dma16_buf(rv, ld_voff[i], vd + el);
     }
@@ -904,12 +910,15 @@ template <int D, bool CAUSAL>
 hipError_t launch_bwd(const BwdParams& p_in, unsigned phases, hipStream_t stream) {
   BwdParams q = p_in;
   q.num_blk = (q.seqlen + 127) / 128;
+  if (q.dq_waves != 8) q.dq_waves = 4;
+  q.num_dq_blk = (q.seqlen + 32 * q.dq_waves - 1) / (32 * q.dq_waves);
   if (phases & kBwdDelta) {
     constexpr int RPW = 256 / (D / 8) * kDeltaRows;
     const long nrows = (long)q.batch * q.seqlen * q.hq;
     const long nstat = (nrows + RPW - 1) / RPW;
     const long npadwg = ((long)q.batch * q.hq * (q.stat_stride - q.seqlen) + 255) / 256;
-    const long norder = (q.num_blk * (long)q.head_split + 255) / 256 + (q.num_blk * (long)q.key_split + 255) / 256;
+    const long norder =
+        (q.num_blk * (long)q.head_split + 255) / 256 + (q.num_dq_blk * (long)q.key_split + 255) / 256;
     dim3 grid((unsigned)(nstat + npadwg + norder));
     hipLaunchKernelGGL((attn_bwd_delta_kernel<D, CAUSAL>), grid, dim3(256), 0, stream, q);
     hipError_t e = hipGetLastError();
@@ -932,11 +941,17 @@ hipError_t launch_bwd(const BwdParams& p_in, unsigned phases, hipStream_t stream
     }
   }
   if (phases & kBwdDq) {
-    dim3 grid(q.batch * q.hq, q.num_blk * q.key_split);
-    if (q.dq_acc != nullptr) {
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL, true>), grid, dim3(256), 0, stream, q);
+    dim3 grid(q.batch * q.hq, q.num_dq_blk * q.key_split);
+    if (q.dq_waves == 8) {
+      if (q.dq_acc != nullptr) {
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL, true, 8>), grid, dim3(512), 0, stream, q);
+      } else {
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL, false, 8>), grid, dim3(512), 0, stream, q);
+      }
+    } else if (q.dq_acc != nullptr) {
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL, true, 4>), grid, dim3(256), 0, stream, q);
     } else {
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL, false>), grid, dim3(256), 0, stream, q);
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL, false, 4>), grid, dim3(256), 0, stream, q);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -73,7 +73,7 @@ struct BwdParams {
   float* delta;  // workspace [B, Hq, stat_stride]: Delta_i = dO_i . O_i
   float* lse2;   // workspace [B, Hq, stat_stride]: LSE_i * log2(e)
   int stat_stride;  // seqlen rounded up to kStatAlign; the padding holds zeros
-  int* order;       // workspace: dK/dV work order [num_blk * head_split], then dQ's [num_blk * key_split]
+  int* order;       // workspace: dK/dV work order [num_blk * head_split], then dQ's [num_dq_blk * key_split]
   float* part;      // workspace [2][head_split][B][S][Hkv][D] fp32 partial dK, dV (head_split > 1 only)
   float* dq_part;   // workspace [key_split][B][S][Hq][D] fp32 partial dQ (key_split > 1 only)
   int head_split;   // query heads of a GQA group split over this many dK/dV workgroups
@@ -84,7 +84,9 @@ struct BwdParams {
   int causal;
   float scale;
   float scale_log2e;
-  int num_blk;  // 128-row blocks along the sequence; set by the launcher
+  int num_blk;     // 128-row blocks along the sequence (dK/dV key blocks); set by the launcher
+  int dq_waves;    // dQ block geometry: 4 (128-query blocks) or 8 (256-query blocks)
+  int num_dq_blk;  // dQ query blocks of 32 * dq_waves rows; set by the launcher
   // fp8 inputs (null for bf16): q, k, v then hold the E4M3 codes widened to
   // bf16 (exact), and the real inputs are code * descale. The kernels fold the
   // descales into their constants (scores, Delta and the dK, dQ outputs).
@@ -119,6 +121,26 @@ struct BwdParams {
 int fwd_block_waves_env();  // 0 when unset
 inline int fwd_block_waves(int seqlen, int head_dim, int causal, bool packed) {
   const int forced = fwd_block_waves_env();
+  if (forced == 4 || forced == 8) return forced;
+  if (packed || head_dim != 128) return 4;
+  return seqlen >= (causal ? 16384 : 4096) ? 8 : 4;
+}
+// The dQ pass's block height, the same choice for the backward: 128 queries
+// (4 waves, two workgroups per CU) or 256 (8 waves, one per CU, each K/V
+// tile copied into LDS once per CU). Measured on MI355X (B * S = 32768
+// tokens, Hq = 28, Hkv = 4), dQ time of 8 waves over 4:
+//   D = 128 causal:     S = 2048 1.09, 4096 1.02, 8192 1.00, 16384 0.99, 32768 0.99
+//   D = 128 non-causal: S = 2048 1.00, 4096 0.97, 8192 0.98, 16384 0.98, 32768 0.97
+//   D = 64:             1.03 - 1.35 at every S, both masks
+// so 8 waves are taken for D = 128 without packing or key split from
+// S = 16384 (causal) or S = 4096 (non-causal). ATTN_DQ_WAVES=4 or 8
+// overrides it (for tests and tuning; a split dQ always runs 4 waves). The
+// Delta phase, which writes the dQ work order, and the dQ phase must see the
+// same choice.
+int bwd_dq_waves_env();  // 0 when unset
+inline int bwd_dq_block_waves(int seqlen, int head_dim, int causal, bool packed, int key_split) {
+  if (key_split > 1) return 4;
+  const int forced = bwd_dq_waves_env();
   if (forced == 4 || forced == 8) return forced;
   if (packed || head_dim != 128) return 4;
   return seqlen >= (causal ? 16384 : 4096) ? 8 : 4;

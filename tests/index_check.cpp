@@ -274,15 +274,17 @@ void check_layouts() {
     check_row_frags<D>(t, true, what);
     check_tr_frags<D>(t, true, false, what);
   }
-  // dQ: K tile dual (rows for S, transposed for dQ), V tile B128 rows, 4 waves
-  snprintf(what, sizeof what, "dq D=%d K", D);
-  {
-    const std::vector<Tag> t = fill_tile<D>(kDual, 4, what);
-    check_row_frags<D>(t, true, what);
-    check_tr_frags<D>(t, true, false, what);
+  // dQ: K tile dual (rows for S, transposed for dQ), V tile B128 rows, 4 or 8 waves
+  for (int waves : {4, 8}) {
+    snprintf(what, sizeof what, "dq D=%d waves=%d K", D, waves);
+    {
+      const std::vector<Tag> t = fill_tile<D>(kDual, waves, what);
+      check_row_frags<D>(t, true, what);
+      check_tr_frags<D>(t, true, false, what);
+    }
+    snprintf(what, sizeof what, "dq D=%d waves=%d V", D, waves);
+    check_row_frags<D>(fill_tile<D>(kB128, waves, what), false, what);
   }
-  snprintf(what, sizeof what, "dq D=%d V", D);
-  check_row_frags<D>(fill_tile<D>(kB128, 4, what), false, what);
 }
 
 // ---------------------------------------------------------------------------

@@ -1,5 +1,6 @@
 """The backward's work order (GPU): the Delta phase writes, for the dK/dV and
-the dQ kernels, the order in which they take their 128-row blocks. Each list
+the dQ kernels, the order in which they take their blocks (128 keys for
+dK/dV; 128 or 256 queries for dQ, by the block-height rule below). Each list
 must be a permutation of the blocks (or some block would be computed twice and
 another never), sorted by cost, heaviest first, ties by block index.
 
@@ -8,6 +9,8 @@ mask lets it see: under a causal mask key j sees queries j.. of its segment and
 query i sees keys up to i; with packing only its own segment; otherwise the
 whole sequence.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -32,8 +35,22 @@ def _ksplit(B, Hq, S):
     return 1 if units >= 1024 else min(4, -(-1024 // units))
 
 
-def _cost(cu, S, causal, pass_, blk):
-    first, last = blk * 128, min(blk * 128 + 128, S) - 1
+def _dq_rows(S, D, causal, packed, nk):
+    """Rows of a dQ block: 256 (8 waves) for D = 128 without packing or key
+    split from S = 16384 causal / 4096 non-causal, else 128; ATTN_DQ_WAVES=4|8
+    forces it unless the key tiles are split."""
+    if nk > 1:
+        return 128
+    forced = os.environ.get("ATTN_DQ_WAVES", "")
+    if forced in ("4", "8"):
+        return 32 * int(forced)
+    if packed or D != 128:
+        return 128
+    return 256 if S >= (16384 if causal else 4096) else 128
+
+
+def _cost(cu, S, causal, pass_, blk, rows=128):
+    first, last = blk * rows, min(blk * rows + rows, S) - 1
     if pass_ == 0:  # keys first..last: the union of the queries they see
         lo = first if causal else _segment(cu, first)[0]
         hi = _segment(cu, last)[1]
@@ -50,6 +67,7 @@ CASES = [
     (4096, True, None),
     (32768, True, si.packed_lengths(np.random.default_rng(4))),
     (32768, False, si.packed_lengths(np.random.default_rng(7))),
+    (20000, False, None),
     (70000, True, None),
 ]
 
@@ -71,16 +89,18 @@ def test_block_order(S, causal, lengths):
     torch.cuda.synchronize()
     nblk = -(-S // 128)
     ns, nk = _split(B, Hq, Hkv, S), _ksplit(B, Hq, S)
+    rows = _dq_rows(S, D, causal, lengths is not None, nk)
+    nqblk = -(-S // rows)
     G = Hq // Hkv
     off = 2 * B * Hq * (-(-S // 64) * 64)  # int32 words before the order
-    order = ws[off:off + nblk * (ns + nk)].cpu().numpy()
+    order = ws[off:off + nblk * ns + nqblk * nk].cpu().numpy()
     # dK/dV entries e = key block * ns + share of the group's heads; cost = tiles * heads in the share.
     # dQ entries e = query block * nk + share of the block's key tiles; cost = tiles in the share.
     share = lambda n, m, i: (i + 1) * n // m - i * n // m
-    for pass_, got, n in ((0, order[:nblk * ns], nblk * ns), (1, order[nblk * ns:], nblk * nk)):
+    for pass_, got, n in ((0, order[:nblk * ns], nblk * ns), (1, order[nblk * ns:], nqblk * nk)):
         assert sorted(got.tolist()) == list(range(n)), f"pass {pass_}: not a permutation"
         if pass_ == 0:
             keys = [(-_cost(cu_h, S, causal, 0, int(e) // ns) * share(G, ns, int(e) % ns), int(e)) for e in got]
         else:
-            keys = [(-share(_cost(cu_h, S, causal, 1, int(e) // nk), nk, int(e) % nk), int(e)) for e in got]
+            keys = [(-share(_cost(cu_h, S, causal, 1, int(e) // nk, rows), nk, int(e) % nk), int(e)) for e in got]
         assert keys == sorted(keys), f"pass {pass_}: not heaviest first"
