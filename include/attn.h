@@ -62,6 +62,14 @@
  *     except ATTN_ERR_HIP, which reports a failed copy or launch
  *     (attn_last_hip_error() then gives the hipError_t value).
  *   - Determinism: no atomics; identical inputs give bitwise identical outputs.
+ *   - Debug build: libmi355attn_debug.so exports this same interface, built
+ *     with -DATTN_DEBUG. Its kernels check each LDS access made through the
+ *     library's access helpers (tile copies, fragment and statistics reads,
+ *     the few-key kernel's rows) against the workgroup's LDS allocation and
+ *     the access's alignment before issuing it, skip a failing access, and
+ *     record it; each entry point then synchronises `stream` and returns
+ *     ATTN_ERR_DEBUG_CHECK if any access failed. It gives bitwise the same
+ *     outputs as this library and is much slower; it is meant for tests.
  */
 #ifndef MI355ATTN_ATTN_H_
 #define MI355ATTN_ATTN_H_
@@ -80,7 +88,8 @@ typedef enum attn_status {
   ATTN_ERR_INVALID_ARGUMENT = 1, /* inconsistent shape, flag or pointer; nothing enqueued */
   ATTN_ERR_UNSUPPORTED = 2,      /* valid request the library has no kernel for; caller may fall back */
   ATTN_ERR_HIP = 3,              /* a kernel launch failed; see attn_last_hip_error() */
-  ATTN_ERR_SCRATCH_TOO_SMALL = 4 /* attn_bwd_noalloc: the request needs more than its fixed scratch; nothing enqueued */
+  ATTN_ERR_SCRATCH_TOO_SMALL = 4, /* attn_bwd_noalloc: the request needs more than its fixed scratch; nothing enqueued */
+  ATTN_ERR_DEBUG_CHECK = 5        /* debug build only: a kernel's LDS access check failed; outputs are invalid */
 } attn_status;
 
 /* Bytes of device workspace attn_fwd (and attn_fwd_fp8) can use for these sizes: 0 when the

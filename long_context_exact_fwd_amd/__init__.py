@@ -19,12 +19,16 @@ from typing import Optional
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmi355attn.so")
+# Same C ABI, built with -DATTN_DEBUG: LDS accesses bounds-checked on the
+# device and a synchronising check after every call (ATTN_ERR_DEBUG_CHECK).
+DEBUG_LIB_PATH = os.path.join(_PKG, "libmi355attn_debug.so")
 
 ATTN_OK = 0
 ATTN_ERR_INVALID_ARGUMENT = 1
 ATTN_ERR_UNSUPPORTED = 2
 ATTN_ERR_HIP = 3
 ATTN_ERR_SCRATCH_TOO_SMALL = 4
+ATTN_ERR_DEBUG_CHECK = 5
 NOALLOC_SCRATCH_BYTES = 64 << 20  # ATTN_NOALLOC_SCRATCH_BYTES in include/attn.h
 
 _lib = None
@@ -80,6 +84,14 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     if path is None:
         _lib = lib
     return lib
+
+
+def use_debug_library(debug: bool = True) -> ctypes.CDLL:
+    """Route every call of this module through libmi355attn_debug.so (or back to libmi355attn.so)."""
+    global _lib
+    _lib = None
+    _lib = load_library(DEBUG_LIB_PATH if debug else LIB_PATH)
+    return _lib
 
 
 EXPORTED = ("attn_fwd", "attn_fwd_workspace_bytes", "attn_fwd_fp8", "attn_bwd", "attn_bwd_phases",

@@ -3,8 +3,12 @@
     python -m long_context_exact_fwd_amd.build [--jobs N]
 
 Every HIP source under csrc/ is compiled for gfx950 and linked into
-long_context_exact_fwd_amd/libmi355attn.so. The measurement probes under
-csrc/probe/ (not part of the attention library) go into libmi355probe.so.
+long_context_exact_fwd_amd/libmi355attn.so. The same sources compiled with
+-DATTN_DEBUG give libmi355attn_debug.so: the same C ABI, with every LDS
+access made through the checked helpers bounds-checked on the device and a
+synchronising check after each call (ATTN_ERR_DEBUG_CHECK). The measurement
+probes under csrc/probe/ (not part of the attention library) go into
+libmi355probe.so.
 Packed fp32 VALU instructions are disabled (``-packed-fp32-ops``); hipcc's
 host pass warns that it does not know that feature, which is harmless.
 """
@@ -21,6 +25,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmi355attn.so")
+DEBUG_LIB = os.path.join(PKG, "libmi355attn_debug.so")
 PROBE_LIB = os.path.join(PKG, "libmi355probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -32,9 +37,10 @@ CFLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+def _compile(job) -> str:
+    src, debug = job
+    obj = os.path.join(BUILD, os.path.basename(src) + (".debug.o" if debug else ".o"))
+    cmd = [HIPCC, *CFLAGS, *(["-DATTN_DEBUG"] if debug else []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if "not a recognized feature" not in ln]
     if r.returncode != 0:
@@ -51,23 +57,29 @@ def _link(objs, lib: str) -> None:
     os.replace(tmp, lib)
 
 
-def build(jobs: int = 0) -> str:
+def build(jobs: int = 0, debug: bool = True) -> str:
+    """Builds libmi355attn.so and libmi355probe.so, and libmi355attn_debug.so unless debug is False."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     probes = sorted(glob.glob(os.path.join(CSRC, "probe", "*.hip")))
-    jobs = jobs or min(8, len(srcs) + len(probes), os.cpu_count() or 1)
+    jobs_list = [(f, False) for f in srcs + probes] + ([(f, True) for f in srcs] if debug else [])
+    jobs = jobs or min(8, len(jobs_list), os.cpu_count() or 1)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs + probes))
-    _link(objs[:len(srcs)], LIB)
-    _link(objs[len(srcs):], PROBE_LIB)
+        objs = list(ex.map(_compile, jobs_list))
+    n, m = len(srcs), len(srcs) + len(probes)
+    _link(objs[:n], LIB)
+    _link(objs[n:m], PROBE_LIB)
+    if debug:
+        _link(objs[m:], DEBUG_LIB)
     return LIB
 
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=0)
+    ap.add_argument("--no-debug", action="store_true", help="skip libmi355attn_debug.so")
     a = ap.parse_args(argv)
-    print(build(a.jobs))
+    print(build(a.jobs, debug=not a.no_debug))
     return 0
 
 

@@ -80,6 +80,25 @@ attn_status hip_result(hipError_t e) {
   return ATTN_OK;
 }
 
+attn_status launched(hipError_t e, hipStream_t stream) {
+  const attn_status st = hip_result(e);
+#ifdef ATTN_DEBUG
+  if (st != ATTN_OK) return st;
+  hipError_t r = hipStreamSynchronize(stream);
+  unsigned int faults = 0;
+  for (hipError_t (*take)(unsigned int*) : {lds_faults_fwd, lds_faults_fp8, lds_faults_bwd, lds_faults_merge}) {
+    unsigned int w = 0;
+    if (r == hipSuccess) r = take(&w);
+    faults |= w;
+  }
+  if (r != hipSuccess) return hip_result(r);
+  if (faults != 0) return ATTN_ERR_DEBUG_CHECK;
+#else
+  (void)stream;
+#endif
+  return st;
+}
+
 attn_status bwd_check(unsigned phases, const void* q, const void* k, const void* v, const void* o, const float* lse,
                       const void* dout, void* dq, void* dk, void* dv, const void* workspace, bool need_workspace,
                       int batch, int hq, int hkv, int seqlen, int head_dim, int causal, const int32_t* cu_seqlens,
@@ -146,7 +165,7 @@ attn_status bwd_launch(unsigned phases, const void* q, const void* k, const void
   p.descale_q = descale_q;
   p.descale_k = descale_k;
   p.descale_v = descale_v;
-  return hip_result(run_bwd(p, phases, stream));
+  return launched(run_bwd(p, phases, stream), stream);
 }
 
 }  // namespace mi355attn
@@ -160,6 +179,7 @@ const char* attn_status_str(attn_status s) {
     case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
     case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
     case ATTN_ERR_SCRATCH_TOO_SMALL: return "ATTN_ERR_SCRATCH_TOO_SMALL";
+    case ATTN_ERR_DEBUG_CHECK: return "ATTN_ERR_DEBUG_CHECK";
   }
   return "ATTN_ERR_UNKNOWN";
 }
@@ -214,7 +234,8 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
     p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                           mi355attn::fwd_part_lse_offset(batch, hq, seqlen, head_dim, ks));
   }
-  return mi355attn::hip_result(mi355attn::run_fwd_bf16(p, reinterpret_cast<hipStream_t>(stream)));
+  return mi355attn::launched(mi355attn::run_fwd_bf16(p, reinterpret_cast<hipStream_t>(stream)),
+                               reinterpret_cast<hipStream_t>(stream));
 }
 
 attn_status attn_fwd_merge(const void* q, const void* k, const void* v, float* o_acc, float* lse_acc, void* o_out,
@@ -258,7 +279,8 @@ attn_status attn_fwd_merge(const void* q, const void* k, const void* v, float* o
     p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                           mi355attn::fwd_part_lse_offset(batch, hq, seqlen, head_dim, ks));
   }
-  return mi355attn::hip_result(mi355attn::run_fwd_bf16(p, reinterpret_cast<hipStream_t>(stream)));
+  return mi355attn::launched(mi355attn::run_fwd_bf16(p, reinterpret_cast<hipStream_t>(stream)),
+                               reinterpret_cast<hipStream_t>(stream));
 }
 
 attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* descale_q,
@@ -303,7 +325,8 @@ attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const f
     p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                           mi355attn::fwd_part_lse_offset(batch, hq, seqlen, head_dim, ks));
   }
-  return mi355attn::hip_result(mi355attn::run_fwd_fp8(p, reinterpret_cast<hipStream_t>(stream)));
+  return mi355attn::launched(mi355attn::run_fwd_fp8(p, reinterpret_cast<hipStream_t>(stream)),
+                               reinterpret_cast<hipStream_t>(stream));
 }
 
 attn_status attn_fwd_fp8_merge(const void* q8, const void* k8, const void* v8, const float* descale_q,
@@ -353,7 +376,8 @@ attn_status attn_fwd_fp8_merge(const void* q8, const void* k8, const void* v8, c
     p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                           mi355attn::fwd_part_lse_offset(batch, hq, seqlen, head_dim, ks));
   }
-  return mi355attn::hip_result(mi355attn::run_fwd_fp8(p, reinterpret_cast<hipStream_t>(stream)));
+  return mi355attn::launched(mi355attn::run_fwd_fp8(p, reinterpret_cast<hipStream_t>(stream)),
+                               reinterpret_cast<hipStream_t>(stream));
 }
 
 attn_status attn_bwd_phases(unsigned phases, const void* q, const void* k, const void* v, const void* o,
@@ -430,7 +454,8 @@ attn_status attn_merge(float* o_acc, float* lse_acc, const void* o_part, const f
   p.heads = heads;
   p.head_dim = head_dim;
   p.accumulate = accumulate;
-  return mi355attn::hip_result(mi355attn::run_merge(p, reinterpret_cast<hipStream_t>(stream)));
+  return mi355attn::launched(mi355attn::run_merge(p, reinterpret_cast<hipStream_t>(stream)),
+                               reinterpret_cast<hipStream_t>(stream));
 }
 
 attn_status attn_bwd_accumulate(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -24,6 +24,7 @@
 //     VGPRs, K and V tiles stream through LDS.
 // Tiles reach LDS through buffer loads that write LDS directly; rows past the
 // sequence end read as zeros and are masked.
+#define ATTN_LDS_FAULT_WORD g_lds_fault_bwd
 #include "attn_device.h"
 #include "attn_internal.h"
 
@@ -450,8 +451,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
         for (int qb = 0; qb < 2; ++qb) {
           const f32x16& s = sc[qb];
           // C rows of this lane: queries qb*32 + c_key(r, h), two runs of 8
-          const f32x4* l4 = reinterpret_cast<const f32x4*>(st + qb * 32 + 8 * h);
-          const f32x4 la = l4[0], lb = l4[1], lc = l4[4], ld = l4[5];
+          const float* l4 = st + qb * 32 + 8 * h;
+          const f32x4 la = lds_load16<f32x4>(l4), lb = lds_load16<f32x4>(l4 + 4);
+          const f32x4 lc = lds_load16<f32x4>(l4 + 16), ld = lds_load16<f32x4>(l4 + 20);
           float pr[16];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -493,8 +495,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           // dS = P (dP - Delta), P widened from the bf16 exchange
-          const f32x4* d4 = reinterpret_cast<const f32x4*>(st + kQT + qb * 32 + 8 * h);
-          const f32x4 da = d4[0], dd = d4[1], dc = d4[4], de = d4[5];
+          const float* d4 = st + kQT + qb * 32 + 8 * h;
+          const f32x4 da = lds_load16<f32x4>(d4), dd = lds_load16<f32x4>(d4 + 4);
+          const f32x4 dc = lds_load16<f32x4>(d4 + 16), de = lds_load16<f32x4>(d4 + 20);
           const u32x4 w0 = xchg[xs][pair][qb][0][lane], w1 = xchg[xs][pair][qb][1][lane];
           auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
           auto hi = [](uint32_t w) { return __uint_as_float(w & 0xffff0000u); };
@@ -979,5 +982,9 @@ hipError_t run_bwd(const BwdParams& p, unsigned phases, hipStream_t stream) {
   }
   return p.causal ? launch_bwd<64, true>(p, phases, stream) : launch_bwd<64, false>(p, phases, stream);
 }
+
+#ifdef ATTN_DEBUG
+hipError_t lds_faults_bwd(unsigned int* out) { return take_lds_fault_word(out); }
+#endif
 
 }  // namespace mi355attn

@@ -33,6 +33,45 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
+// Debug builds (-DATTN_DEBUG, linked into libmi355attn_debug.so) check every
+// LDS access made through the helpers below before issuing it: the access
+// must lie inside the kernel's static LDS allocation and be aligned to its
+// size (lds_access_ok). A failing access is not made (a read returns zeros, a
+// store or tile copy is dropped), so no kernel reaches LDS outside its
+// allocation, and it sets a bit of this source file's fault word: 1 for a
+// read, 2 for a store, 4 for a tile copy. The C ABI then synchronises after
+// each call, reads and clears the words and returns ATTN_ERR_DEBUG_CHECK if
+// one is set. Device variables belong to one source file here, so each
+// kernel file names its word (ATTN_LDS_FAULT_WORD) before including this
+// header. Fixed-shape arrays indexed by wave, lane or compile-time slot
+// (the reduction scratch, the dK/dV probability exchange) are not routed
+// through the checks; their bounds hold by construction. Release builds
+// compile none of this.
+#ifdef ATTN_DEBUG
+#ifndef ATTN_LDS_FAULT_WORD
+#error "define ATTN_LDS_FAULT_WORD before including attn_device.h in a debug build"
+#endif
+__device__ unsigned int ATTN_LDS_FAULT_WORD;
+__device__ __forceinline__ bool lds_ok(const void* p, uint32_t bytes, unsigned int bit) {
+  const uint32_t addr = (uint32_t)(uintptr_t)LDS_PTR(const char, p);
+  const uint32_t align = bytes >= 16u ? 16u : bytes;
+  if (mi355attn::lds_access_ok(addr, bytes, align, __builtin_amdgcn_groupstaticsize())) return true;
+  atomicOr(&ATTN_LDS_FAULT_WORD, bit);
+  return false;
+}
+#define ATTN_LDS_CHECK(p, bytes, bit, on_fail) \
+  if (!lds_ok((p), (bytes), (bit))) on_fail
+// Reads and clears this file's fault word on the current device.
+static inline hipError_t take_lds_fault_word(unsigned int* out) {
+  const unsigned int zero = 0;
+  hipError_t e = hipMemcpyFromSymbol(out, HIP_SYMBOL(ATTN_LDS_FAULT_WORD), sizeof(unsigned int));
+  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(ATTN_LDS_FAULT_WORD), &zero, sizeof(unsigned int));
+  return e;
+}
+#else
+#define ATTN_LDS_CHECK(p, bytes, bit, on_fail)
+#endif
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // A running row maximum below any real scaled score; exp2(-1e30 - x) == 0.
@@ -70,11 +109,28 @@ __device__ __forceinline__ float sum_lane_halves(float x) {
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const __bf16* base, int elem_off) {
+  ATTN_LDS_CHECK(base + elem_off, 16u, 1u, return bf16x8{});
   return *LDS_PTR(const bf16x8, base + elem_off);
 }
 
 __device__ __forceinline__ bf16x4 lds_read_tr(const __bf16* base, int elem_off) {
+  ATTN_LDS_CHECK(base + elem_off, 8u, 1u, return bf16x4{});
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, const_cast<__bf16*>(base) + elem_off));
+}
+
+// Plain 16-byte LDS loads and stores through a generic pointer into a
+// __shared__ array (fp32 row statistics, the few-key kernel's rows).
+template <typename T>
+__device__ __forceinline__ T lds_load16(const void* p) {
+  static_assert(sizeof(T) == 16, "16-byte accesses only");
+  ATTN_LDS_CHECK(p, 16u, 1u, return T{});
+  return *reinterpret_cast<const T*>(p);
+}
+template <typename T>
+__device__ __forceinline__ void lds_store16g(void* p, const T& v) {
+  static_assert(sizeof(T) == 16, "16-byte accesses only");
+  ATTN_LDS_CHECK(p, 16u, 2u, return);
+  *reinterpret_cast<T*>(p) = v;
 }
 
 // Two transposing reads, 4 rows apart in a TR tile: elem_off is the first
@@ -93,6 +149,7 @@ __device__ __forceinline__ bf16x8 tr_read_pair(const __bf16* tile, int elem_off,
 // same for every lane of the wave (it goes to M0). Completion is tracked by
 // vmcnt, so wait_dma() must precede the barrier after which the data is read.
 __device__ __forceinline__ void dma16(const void* g, const void* lds_wave_base) {
+  ATTN_LDS_CHECK(static_cast<const char*>(lds_wave_base) + 16 * __lane_id(), 16u, 4u, return);
   __builtin_amdgcn_global_load_lds(g, LDS_PTR(void, const_cast<void*>(lds_wave_base)), 16, 0, 0);
 }
 // Buffer resource over [base, base + nbytes) (raw, stride 0): a load whose
@@ -103,6 +160,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // buffer_load_dwordx4 ... lds: lane L copies 16 bytes at byte offset voff of
 // the buffer into lds_wave_base + 16 L (same M0 rule as dma16).
 __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, const void* lds_wave_base) {
+  ATTN_LDS_CHECK(static_cast<const char*>(lds_wave_base) + 16 * __lane_id(), 16u, 4u, return);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, const_cast<void*>(lds_wave_base)), 16, voff, 0, 0, 0);
 }
 // s_waitcnt vmcnt(0), other counters left alone (expcnt 7, lgkmcnt 15).
@@ -125,6 +183,7 @@ __device__ __forceinline__ u32x4 load16_pred(const __bf16* p, bool ok) {
   return ok ? *reinterpret_cast<const u32x4*>(p) : z;
 }
 __device__ __forceinline__ void lds_store16(__bf16* base, int elem_off, u32x4 v) {
+  ATTN_LDS_CHECK(base + elem_off, 16u, 2u, return);
   *LDS_PTR(u32x4, base + elem_off) = v;
 }
 

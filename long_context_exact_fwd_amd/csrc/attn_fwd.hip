@@ -36,6 +36,7 @@
 //     the call's result into a running fp32 (O, LSE) (the Ring-Attention
 //     paragraph of the page's sequence-parallel section accumulates partial
 //     results per arriving K/V block) instead of writing O and LSE.
+#define ATTN_LDS_FAULT_WORD g_lds_fault_fwd
 #include "attn_device.h"
 #include "attn_internal.h"
 
@@ -503,8 +504,8 @@ __global__ __launch_bounds__(256) void attn_fwd_fewkeys_kernel(FwdParams p) {
   const int tid = threadIdx.x;
   for (int e = tid; e < nrows * C; e += 256) {
     const int j = e / C, c = e % C;
-    *reinterpret_cast<u32x4*>(&ks[j][((c + j) % C) * 8]) = load16(kg + (size_t)j * kv_stride + c * 8);
-    *reinterpret_cast<u32x4*>(&vs[j][c * 8]) = load16(vg + (size_t)j * kv_stride + c * 8);
+    lds_store16g(&ks[j][((c + j) % C) * 8], load16(kg + (size_t)j * kv_stride + c * 8));
+    lds_store16g(&vs[j][c * 8], load16(vg + (size_t)j * kv_stride + c * 8));
   }
   for (int e = tid; e < kFewRowsPerWg * D; e += 256) {
     const int w = e / D, d = e % D;
@@ -522,7 +523,7 @@ __global__ __launch_bounds__(256) void attn_fwd_fewkeys_kernel(FwdParams p) {
     float dot = 0.f;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      const bf16x8 kv = *reinterpret_cast<const bf16x8*>(&ks[lane][((c + lane) % C) * 8]);
+      const bf16x8 kv = lds_load16<bf16x8>(&ks[lane][((c + lane) % C) * 8]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(qs[wave][c * 8 + e], (float)kv[e], dot);
     }
@@ -628,5 +629,9 @@ hipError_t run_fwd_bf16(const FwdParams& p, hipStream_t stream) {
   }
   return p.causal ? launch_fwd<64, true>(p, stream) : launch_fwd<64, false>(p, stream);
 }
+
+#ifdef ATTN_DEBUG
+hipError_t lds_faults_fwd(unsigned int* out) { return take_lds_fault_word(out); }
+#endif
 
 }  // namespace mi355attn

@@ -30,6 +30,7 @@
 //     subtracted so that small probabilities keep E4M3 precision instead of
 //     flushing to zero; the offset cancels in O = acc / l and is added back
 //     in the LSE.
+#define ATTN_LDS_FAULT_WORD g_lds_fault_fp8
 #include "attn_device.h"
 #include "attn_internal.h"
 
@@ -45,6 +46,16 @@ constexpr int kBN = 64;       // keys per tile
 constexpr int kTileBytes = kBN * kD;
 constexpr float kP8Offset = 8.0f;       // log2 units subtracted from the running maximum
 constexpr float kP8Threshold = 0.5f;    // lazy rescale threshold for the fp8 path
+
+// 16 bytes of a K tile, and the transposing 8-byte read of a V tile.
+__device__ __forceinline__ u32x4 lds_read_u8x16(const uint8_t* p) {
+  ATTN_LDS_CHECK(p, 16u, 1u, return u32x4{});
+  return *LDS_PTR(const u32x4, p);
+}
+__device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* p) {
+  ATTN_LDS_CHECK(p, 8u, 1u, return i32x2{});
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i32x2, const_cast<uint8_t*>(p)));
+}
 
 __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
   // formats 0/0 = E4M3 for A and B; E8M0 block scales 127 = 1.0
@@ -187,8 +198,8 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void attn_fwd_fp8_kernel(Fp8
         s[kb] = f32x16{};
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const u32x4 lo = *LDS_PTR(const u32x4, ks + koff[t][0] + kb * 32 * kD);
-          const u32x4 hi = *LDS_PTR(const u32x4, ks + koff[t][1] + kb * 32 * kD);
+          const u32x4 lo = lds_read_u8x16(ks + koff[t][0] + kb * 32 * kD);
+          const u32x4 hi = lds_read_u8x16(ks + koff[t][1] + kb * 32 * kD);
           const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
           s[kb] = mfma_fp8(a, qf[t], s[kb]);
         }
@@ -239,8 +250,7 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void attn_fwd_fp8_kernel(Fp8
         i32x8 a;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              LDS_PTR(i32x2, const_cast<uint8_t*>(vs) + voff[db] + q * 16 * kD));
+          const i32x2 t = lds_read_tr8(vs + voff[db] + q * 16 * kD);
           a[2 * q] = t[0];
           a[2 * q + 1] = t[1];
         }
@@ -378,5 +388,9 @@ hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream) {
 hipError_t run_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream) {
   return p.causal ? launch_fwd_fp8<true>(p, stream) : launch_fwd_fp8<false>(p, stream);
 }
+
+#ifdef ATTN_DEBUG
+hipError_t lds_faults_fp8(unsigned int* out) { return take_lds_fault_word(out); }
+#endif
 
 }  // namespace mi355attn

@@ -20,6 +20,13 @@ namespace mi355attn {
 ATTN_HD int imin(int a, int b) { return a < b ? a : b; }
 ATTN_HD int imax(int a, int b) { return a > b ? a : b; }
 
+// The LDS access rule of the debug build (-DATTN_DEBUG): an access of
+// `bytes` bytes at LDS byte address `addr` must lie inside the workgroup's
+// allocation of `size` bytes and be aligned to `align` (a power of two).
+ATTN_HD bool lds_access_ok(uint32_t addr, uint32_t bytes, uint32_t align, uint32_t size) {
+  return (addr & (align - 1u)) == 0u && addr <= size && bytes <= size - addr;
+}
+
 // Swap bits 2 and 3 of a row index in [0, 32): the K (or Q, dO) row a lane
 // loads for the score product, so that C-layout register r of lane half h
 // holds key 16 * (r / 8) + 8 * h + r % 8.

@@ -178,6 +178,17 @@ hipError_t run_widen_fp8(const uint8_t* src, __bf16* dst, size_t n, hipStream_t 
 // ATTN_OK for hipSuccess; otherwise records e for attn_last_hip_error() and
 // returns ATTN_ERR_HIP.
 attn_status hip_result(hipError_t e);
+// hip_result of a call's last launch. Debug builds (ATTN_DEBUG) then
+// synchronise `stream`, read and clear every kernel file's LDS fault word
+// and return ATTN_ERR_DEBUG_CHECK if one was set.
+attn_status launched(hipError_t e, hipStream_t stream);
+#ifdef ATTN_DEBUG
+// Each kernel file's LDS fault word, read and cleared (synchronous copies).
+hipError_t lds_faults_fwd(unsigned int* out);
+hipError_t lds_faults_fp8(unsigned int* out);
+hipError_t lds_faults_bwd(unsigned int* out);
+hipError_t lds_faults_merge(unsigned int* out);
+#endif
 
 // Argument checks shared by the backward entry points (no HIP call); a
 // workspace pointer is required only when need_workspace is set.

@@ -16,6 +16,7 @@
 // vector loads, so a wave reads whole rows contiguously. The D / 8 threads of
 // a row sit in one wave; the one holding d = 0..7 writes the row's LSE after
 // every lane of the wave has read it.
+#define ATTN_LDS_FAULT_WORD g_lds_fault_merge
 #include "attn_device.h"
 #include "attn_internal.h"
 
@@ -89,5 +90,9 @@ hipError_t run_merge(const MergeParams& p, hipStream_t stream) {
   }
   return hipGetLastError();
 }
+
+#ifdef ATTN_DEBUG
+hipError_t lds_faults_merge(unsigned int* out) { return take_lds_fault_word(out); }
+#endif
 
 }  // namespace mi355attn

@@ -393,7 +393,24 @@ void check_workspace(int B, int Hq, int Hkv, int S, int D) {
   CHECK((uint64_t)S * Hq * D <= (uint64_t)INT32_MAX, "element offsets of S=%d Hq=%d D=%d exceed 31 bits", S, Hq, D);
 }
 
+// The debug build's LDS access rule (lds_access_ok): inside the allocation,
+// aligned, and no wrap-around at the top of the 32-bit address range.
+void check_lds_rule() {
+  CHECK(lds_access_ok(0, 16, 16, 16), "lds rule: whole allocation");
+  CHECK(lds_access_ok(48, 16, 16, 64), "lds rule: last chunk");
+  CHECK(!lds_access_ok(64, 16, 16, 64), "lds rule: one past the end");
+  CHECK(!lds_access_ok(56, 16, 16, 64), "lds rule: straddles the end (and misaligned)");
+  CHECK(!lds_access_ok(8, 16, 16, 64), "lds rule: misaligned 16-byte access");
+  CHECK(lds_access_ok(8, 8, 8, 64), "lds rule: aligned 8-byte access");
+  CHECK(!lds_access_ok(4, 8, 8, 64), "lds rule: misaligned 8-byte access");
+  CHECK(!lds_access_ok(0xFFFFFFF0u, 16, 16, 64), "lds rule: address beyond the allocation");
+  CHECK(!lds_access_ok(0xFFFFFFF0u, 32, 16, 0xFFFFFFF8u), "lds rule: wrap-around");
+  CHECK(lds_access_ok(160 * 1024 - 16, 16, 16, 160 * 1024), "lds rule: top of a 160 KB allocation");
+  CHECK(!lds_access_ok(0, 16, 16, 0), "lds rule: empty allocation");
+}
+
 int main() {
+  check_lds_rule();
   check_layouts<128>();
   check_layouts<64>();
   check_fp8();

@@ -30,12 +30,26 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+@pytest.mark.skipif(not os.path.exists(lca.DEBUG_LIB_PATH), reason="debug library not built")
+def test_debug_library_exports_and_checks_like_the_release_one():
+    """libmi355attn_debug.so (the -DATTN_DEBUG build) has the same ABI and argument checks."""
+    dbg = lca.load_library(lca.DEBUG_LIB_PATH)
+    for name in _declared():
+        assert hasattr(dbg, name), name
+    assert dbg.attn_status_str(lca.ATTN_ERR_DEBUG_CHECK) == b"ATTN_ERR_DEBUG_CHECK"
+    rel = lca.load_library()
+    args = [NULL] * 6 + [1, 4, 2, 128, 128, 1, NULL, 0, 0.125, S0]
+    assert dbg.attn_fwd(*args) == rel.attn_fwd(*args) == lca.ATTN_ERR_INVALID_ARGUMENT
+    assert dbg.attn_bwd_workspace_bytes(1, 28, 4, 32768, 128) == rel.attn_bwd_workspace_bytes(1, 28, 4, 32768, 128)
+
+
 def test_status_strings():
     lib = lca.load_library()
     assert lib.attn_status_str(0) == b"ATTN_OK"
     assert lib.attn_status_str(1) == b"ATTN_ERR_INVALID_ARGUMENT"
     assert lib.attn_status_str(2) == b"ATTN_ERR_UNSUPPORTED"
     assert lib.attn_status_str(3) == b"ATTN_ERR_HIP"
+    assert lib.attn_status_str(5) == b"ATTN_ERR_DEBUG_CHECK"
     assert lib.attn_status_str(77) == b"ATTN_ERR_UNKNOWN"
     assert lib.attn_last_hip_error() == 0
 
