@@ -94,6 +94,84 @@ def test_peaky_scores_exercise_rescaling():
     _run_case(1, 4, 1, 1500, 128, True, seed=46, qk_std=3.0, abs_factor=2.0)
 
 
+def _given_o_gradients(qv, kv, vv, dov, o_given, causal, scale):
+    """The oracle's gradients for a backward given O in bf16, as the C ABI passes it.
+
+    The backward uses Delta_i = dO_i . O_i with the O it is given. Delta enters dS_ij = P_ij (dP_ij - Delta_i)
+    linearly, so with eps_i = dO_i . (O_given - O)_i the gradients are the exact ones minus
+    scale eps_i sum_j P_ij K_j for dQ (the oracle's forward with V := K) and minus
+    scale sum_i P_ij eps_i Q_i for dK (the dV of the oracle's backward with dO := eps Q); dV does not
+    depend on Delta. Rows whose softmax is dominated by one key make dP - Delta a small difference,
+    and this is where the bf16 rounding of O shows: with one outlier channel it moves dQ by ~2e-2."""
+    ro, _ = oracle.attention_fwd(qv, kv, vv, causal=causal, scale=scale, workers=None)
+    rq, rk, rv = oracle.attention_bwd(qv, kv, vv, dov, causal=causal, scale=scale, workers=None)
+    eps = np.einsum("bshd,bshd->bsh", dov, np.asarray(o_given, dtype=np.float64) - ro)[..., None]
+    kbar, _ = oracle.attention_fwd(qv, kv, kv, causal=causal, scale=scale, workers=None)
+    _, _, corr = oracle.attention_bwd(qv, kv, vv, eps * qv, causal=causal, scale=scale, workers=None)
+    return rq - scale * eps * kbar, rk - scale * corr, rv, eps
+
+
+def _run_bits(B, Hq, Hkv, S, D, causal, x, tag, abs_factor=1.0):
+    """Forward against the oracle, and the backward against the oracle's gradients given the kernel's
+    own bf16 O (_given_o_gradients), on the inputs held in x (bf16 bit patterns)."""
+    import torch
+    lca = _lib()
+    q, k, v, do = dev_bf16(x.q_bits), dev_bf16(x.k_bits), dev_bf16(x.v_bits), dev_bf16(x.do_bits)
+    scale = 1.0 / np.sqrt(D)
+    o, lse = lca.fwd(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = lca.bwd(q, k, v, o, lse, do, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    qv, kv, vv, dov = (x.values(n) for n in ("q", "k", "v", "do"))
+    ro, rl = oracle.attention_fwd(qv, kv, vv, causal=causal, scale=scale, workers=None)
+    check_fwd(host(o), host(lse), ro, rl, tag=f"{tag} fwd", abs_factor=abs_factor)
+    rq, rk, rv, eps = _given_o_gradients(qv, kv, vv, dov, host(o), causal, scale)
+    return host(o), (host(dq), host(dk), host(dv)), (rq, rk, rv), (qv, kv, vv, dov, eps, scale)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_all_equal_keys_give_the_mean_of_the_visible_values(causal):
+    """Every key row the same vector: each row's softmax is uniform over its visible keys, so O is the
+    mean of those V rows (checked against the oracle and the running means), and dQ = scale K sum_j dS_ij
+    is zero exactly. The kernel's dQ is then the rounding of dS to bf16 plus the given-O term: each row
+    within scale max|K| (|eps_i| + 2^-8 |dO_i| max_j |V_j|), since sum_j |dS_ij| <= 2 |dO_i| max_j |V_j|."""
+    B, Hq, Hkv, S, D = 1, 4, 2, 700, 128
+    print(f"case all-equal keys causal={causal}", flush=True)
+    x = si.make_inputs(B, Hq, Hkv, S, D, 47, with_do=True)
+    x.k_bits = np.ascontiguousarray(np.broadcast_to(x.k_bits[:, :1], x.k_bits.shape))
+    o, got, ref, (qv, kv, vv, dov, eps, scale) = _run_bits(B, Hq, Hkv, S, D, causal, x,
+                                                           f"all-equal keys causal={causal}")
+    check_grads([("dK", got[1], ref[1]), ("dV", got[2], ref[2])], tag=f"all-equal keys causal={causal} bwd")
+    G = Hq // Hkv
+    vmax = float(np.max(np.linalg.norm(vv, axis=-1)))
+    bound = scale * float(np.max(np.abs(kv))) * (np.abs(eps) + 2.0 ** -8 * np.linalg.norm(dov, axis=-1,
+                                                                                       keepdims=True) * vmax)
+    worst = float(np.max(np.abs(got[0] - ref[0]) / bound))
+    print(f"all-equal keys dQ: max |dQ| = {np.max(np.abs(got[0])):.2e}, worst {worst:.3f} of the bound", flush=True)
+    assert np.all(np.isfinite(got[0])) and worst <= 1.0
+    for h in (0, Hq - 1):
+        vh = vv[0, :, h // G]
+        mean = np.cumsum(vh, axis=0) / np.arange(1, S + 1)[:, None] if causal else np.broadcast_to(vh.mean(0), vh.shape)
+        err = float(np.max(np.abs(o[0, :, h] - mean)))
+        print(f"head {h}: max |O - mean of visible V| = {err:.2e}", flush=True)
+        assert err <= 1e-2
+
+
+def test_one_outlier_channel_dominates_the_scores():
+    """Channel 0 of Q and K scaled by 16: the scores are dominated by one product per pair (a common
+    activation outlier), their spread is large and the running maximum moves. Same stress budget as
+    the peaky case for O (max-abs doubled); the gradients meet the usual 1e-2 against the oracle's
+    gradients given the kernel's bf16 O."""
+    B, Hq, Hkv, S, D = 1, 4, 1, 1200, 64
+    print("case outlier channel", flush=True)
+    x = si.make_inputs(B, Hq, Hkv, S, D, 51, with_do=True)
+    for name in ("q_bits", "k_bits"):
+        vals = si.bf16_bits_to_f64(getattr(x, name))
+        vals[..., 0] *= 16.0  # a power of two: still exactly bf16
+        setattr(x, name, si.bf16_bits_from_f32(vals.astype(np.float32)))
+    _, got, ref, _ = _run_bits(B, Hq, Hkv, S, D, True, x, "outlier channel", abs_factor=2.0)
+    check_grads([("dQ", got[0], ref[0]), ("dK", got[1], ref[1]), ("dV", got[2], ref[2])], tag="outlier channel bwd")
+
+
 SPLIT = [
     # B, Hq, Hkv, S, D, causal, lengths, expected key split
     (1, 2, 1, 4096, 128, True, None, 2),
