@@ -76,11 +76,15 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // A running row maximum below any real scaled score; exp2(-1e30 - x) == 0.
 constexpr float kMaxInit = -1.0e30f;
-// The running maximum used for exponentiation is only moved when the tile
-// maximum exceeds it by more than this (log2 units). Probabilities are then
-// at most 2^8 before normalisation, well inside fp32 and bf16 range; the
-// final division uses the same offset, so the result is unchanged.
+// Where the bf16 forward tracks a running maximum (its redo pass), it is only
+// moved when the tile maximum exceeds it by more than this (log2 units). Probabilities are then at most 2^8 before
+// normalisation, well inside fp32 and bf16 range; the final division uses
+// the same offset, so the result is unchanged.
 constexpr float kRescaleThreshold = 8.0f;
+// The bf16 forward's first-tile maximum is kept while each lane's
+// probability sum over a tile stays at most this (2^64): P, the row sum and
+// O's accumulator then stay far inside the fp32 and bf16 range.
+constexpr float kTileSumLimit = 18446744073709551616.0f;
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

@@ -24,6 +24,15 @@
 //   * Software pipeline: the scores of tile j + 1 are computed in the same
 //     straight block as the exp/sum/pack of tile j, so their MFMAs interleave
 //     with the softmax VALU work; K is kept one tile ahead of V.
+//   * Running maximum: a row's maximum over the first tile where it sees
+//     keys, kept for the rest of the row. The online softmax only needs some
+//     common offset per row that keeps the probabilities in range; for the
+//     scores met in practice the first tile's maximum does, so the later
+//     tiles compute no maximum and never rescale (5-7 % of the kernel's time
+//     on MI355X against tracking the maximum with a lazy rescale). A wave in
+//     which a lane's probability sum over a tile passes 2^64 (scores rising
+//     by ~64 in log2 units past the row's first tile) redoes its rows with
+//     the tracked maximum.
 //   * Tiles partly (or wholly) outside a wave's visible keys are masked per
 //     element. Every LDS address is a per-lane base computed once plus a
 //     compile-time offset, and every per-tile branch is scalar.
@@ -197,92 +206,129 @@ __global__ __launch_bounds__(WAVES * 64, (D == 64 ? 16 : 8) / WAVES) void attn_f
   };
 
   f32x16 acc[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
-  float m_run = kMaxInit;  // running maximum (scaled, log2 units)
-  float l_run = 0.f;       // partial row sum over this lane's keys
+  float m_run;  // running maximum (scaled, log2 units)
+  float l_run;  // partial row sum over this lane's keys
   const float c = p.scale_log2e;
+  const int ntile = tile_end - tile_begin;
 
+  // First key tile of this lane's row within this workgroup's share.
+  const int kfirst = max(kstart, tile_begin * kBN) / kBN * kBN;
+
+  // One pass over the workgroup's tiles. FAST: the running maximum of a row
+  // is its maximum over the first tile where it sees keys, and it stays
+  // there: no tile maximum and no rescale afterwards. That is exact as long
+  // as no probability overflows; the pass returns whether some lane's sum
+  // over a tile went above 2^64 (it cannot underflow: the first tile's
+  // largest probability is 1). !FAST: the maximum follows every tile with
+  // the lazy rescale. A wave that is not `active` only copies tiles and
+  // meets the barriers, keeping its results.
+  //
   // Software pipeline: the scores of tile j + 1 are computed while the
   // softmax of tile j runs, so K is kept one tile ahead of V. Tile
   // tile_begin + i has its K in buffer i & 1 and its V in buffer i & 1.
-  const int ntile = tile_end - tile_begin;
-  f32x16 s_cur[2];
-  if (ntile > 0) {
-    issue_k(tile_begin * kBN, std::integral_constant<int, 0>{});
-    issue_v(tile_begin * kBN, std::integral_constant<int, 0>{});
-    if (ntile > 1) issue_k((tile_begin + 1) * kBN, std::integral_constant<int, 1>{});
-  }
-  wait_dma();
-  __syncthreads();
-  if (ntile > 0) scores(k_lds0, s_cur);
-  __syncthreads();  // K of the first tile is read before its buffer is refilled
-
-  auto body = [&](int i, auto par_c) {
-    constexpr int par = decltype(par_c)::value;
-    const int t0 = (tile_begin + i) * kBN;
-    if (i + 2 < ntile) issue_k(t0 + 2 * kBN, std::integral_constant<int, par>{});
-    if (i + 1 < ntile) issue_v(t0 + kBN, std::integral_constant<int, par ^ 1>{});
-    // Tiles a wave cannot see at all are fully masked (no per-wave skipping,
-    // which keeps the loop body one straight block for the scheduler).
-    const bool full = (t0 >= lo_max) && (t0 + kBN <= hi_min);
-    if (!full) {
+  auto run_tiles = [&](auto fast_c, bool active) {
+    constexpr bool FAST = decltype(fast_c)::value;
+    if (active) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = t0 + kb * 32 + c_key(r, h);
-          s_cur[kb][r] = (key < kstart || key >= kend) ? -INFINITY : s_cur[kb][r];
-        }
+      for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+      m_run = kMaxInit;
+      l_run = 0.f;
     }
-    float mx = fmaxf(s_cur[0][0], s_cur[1][0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = max3f(mx, s_cur[0][r], s_cur[1][r]);
-    mx = max_lane_halves(mx);
-    const float m_tile = mx * c;
-    if (__any(m_tile > m_run + kRescaleThreshold)) {
-      const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = fast_exp2(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int k = 0; k < DB; ++k) acc[k] *= alpha;
-      m_run = m_new;
+    bool over = false;
+    f32x16 s_cur[2];
+    if (ntile > 0) {
+      issue_k(tile_begin * kBN, std::integral_constant<int, 0>{});
+      issue_v(tile_begin * kBN, std::integral_constant<int, 0>{});
+      if (ntile > 1) issue_k((tile_begin + 1) * kBN, std::integral_constant<int, 1>{});
     }
-    // scores of the next tile (its K is already in LDS); on the last tile
-    // this reads a stale buffer and the result is dropped
-    f32x16 s_nxt[2];
-    scores(par ? k_lds0 : k_lds1, s_nxt);
-    const float neg_m = -m_run;
-    bf16x8 pb[4];
-    float lp[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: no serial chain of adds
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float e[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        e[r] = fast_exp2(__builtin_fmaf(s_cur[kb][r], c, neg_m));
-        lp[r & 3] += e[r];
-      }
-      pb[2 * kb] = pack_bf16(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-      pb[2 * kb + 1] = pack_bf16(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
-    }
-    l_run += (lp[0] + lp[1]) + (lp[2] + lp[3]);
-    const __bf16* vs = par ? v_lds1 : v_lds0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-        acc[db] = mfma32(tr_read_pair(vs, voff[db] + 16 * u * D, 4 * D), pb[u], acc[db]);
-    s_cur[0] = s_nxt[0];
-    s_cur[1] = s_nxt[1];
     wait_dma();
     __syncthreads();
+    if (active && ntile > 0) scores(k_lds0, s_cur);
+    __syncthreads();  // K of the first tile is read before its buffer is refilled
+
+    auto body = [&](int i, auto par_c) {
+      constexpr int par = decltype(par_c)::value;
+      const int t0 = (tile_begin + i) * kBN;
+      if (i + 2 < ntile) issue_k(t0 + 2 * kBN, std::integral_constant<int, par>{});
+      if (i + 1 < ntile) issue_v(t0 + kBN, std::integral_constant<int, par ^ 1>{});
+      if (active) {
+        // Tiles a wave cannot see at all are fully masked (no per-wave
+        // skipping, which keeps the loop body one straight block).
+        const bool full = (t0 >= lo_max) && (t0 + kBN <= hi_min);
+        if (!full) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = t0 + kb * 32 + c_key(r, h);
+              s_cur[kb][r] = (key < kstart || key >= kend) ? -INFINITY : s_cur[kb][r];
+            }
+        }
+        if (!FAST || __any(t0 == kfirst)) {
+          float mx = fmaxf(s_cur[0][0], s_cur[1][0]);
+#pragma unroll
+          for (int r = 1; r < 16; ++r) mx = max3f(mx, s_cur[0][r], s_cur[1][r]);
+          const float m_tile = max_lane_halves(mx) * c;
+          if (FAST) {
+            // rows entering their first tile (a row without keys here keeps
+            // kMaxInit, and all its probabilities are 0)
+            if (t0 == kfirst && m_tile > kMaxInit) m_run = m_tile;
+          } else if (__any(m_tile > m_run + kRescaleThreshold)) {
+            const float m_new = fmaxf(m_run, m_tile);
+            const float alpha = fast_exp2(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int k = 0; k < DB; ++k) acc[k] *= alpha;
+            m_run = m_new;
+          }
+        }
+        // scores of the next tile (its K is already in LDS); on the last tile
+        // this reads a stale buffer and the result is dropped
+        f32x16 s_nxt[2];
+        scores(par ? k_lds0 : k_lds1, s_nxt);
+        const float neg_m = -m_run;
+        bf16x8 pb[4];
+        float lp[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: no serial chain of adds
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          float e[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            e[r] = fast_exp2(__builtin_fmaf(s_cur[kb][r], c, neg_m));
+            lp[r & 3] += e[r];
+          }
+          pb[2 * kb] = pack_bf16(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+          pb[2 * kb + 1] = pack_bf16(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
+        }
+        const float l_tile = (lp[0] + lp[1]) + (lp[2] + lp[3]);
+        if (FAST) over = over || !(l_tile <= kTileSumLimit);
+        l_run += l_tile;
+        const __bf16* vs = par ? v_lds1 : v_lds0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            acc[db] = mfma32(tr_read_pair(vs, voff[db] + 16 * u * D, 4 * D), pb[u], acc[db]);
+        s_cur[0] = s_nxt[0];
+        s_cur[1] = s_nxt[1];
+      }
+      wait_dma();
+      __syncthreads();
+    };
+
+    for (int i = 0; i < ntile; i += 2) {
+      body(i, std::integral_constant<int, 0>{});
+      if (i + 1 < ntile) body(i + 1, std::integral_constant<int, 1>{});
+    }
+    return over;
   };
 
-  for (int i = 0; i < ntile; i += 2) {
-    body(i, std::integral_constant<int, 0>{});
-    if (i + 1 < ntile) body(i + 1, std::integral_constant<int, 1>{});
-  }
+  // The fast pass, then, for the waves where a probability overflowed, the
+  // pass with the tracked maximum (rare: scores rising by more than 64 in
+  // log2 units past a row's first tile). Redoing whole waves keeps every row's
+  // result independent of the workgroup's other waves.
+  const bool redo = __any(run_tiles(std::true_type{}, true));
+  if (__syncthreads_or(redo)) run_tiles(std::false_type{}, redo);
 
   // epilogue: O = acc / l, LSE = (m + log2 l) * ln 2; with a key split the
   // share's fp32 O and m + log2 l, combined by attn_fwd_combine_kernel; in a
