@@ -25,11 +25,17 @@
 //     source lanes t / 8 + 2e (e = 0..7), so source lane s points at key row
 //     16q + 8h + s / 2, column half s % 2 of the lane group's 16 d-columns.
 //   * v_cvt_pk_fp8_f32 rounds to nearest even and turns values above 464
-//     into NaN. The exponent offset keeps P at most 2^8.5: the running maximum
-//     used for exponentiation is at most 0.5 (log2 units) stale, and 8 is
-//     subtracted so that small probabilities keep E4M3 precision instead of
-//     flushing to zero; the offset cancels in O = acc / l and is added back
-//     in the LSE.
+//     into NaN. P = 2^(S c - m + 8): the offset of 8 keeps small
+//     probabilities in E4M3's normal range instead of flushing them to zero,
+//     and cancels in O = acc / l (it is added back in the LSE).
+//   * Running maximum m: as in the bf16 forward, a row keeps the maximum of
+//     its first tile, here raised by kP8Margin = 6, so P stays below 448
+//     while later scores exceed that tile's maximum by less than about 6.8
+//     (log2 units): no tile maximum and no rescale in the loop, 6-16 %
+//     faster on MI355X, the kernel being bound by its VALU work. A
+//     probability beyond the range becomes NaN and reaches O's accumulator;
+//     a wave that finds one redoes its rows with the tracked maximum, moved
+//     when a tile's maximum exceeds it by 0.5, which keeps P at most 2^8.5.
 #define ATTN_LDS_FAULT_WORD g_lds_fault_fp8
 #include "attn_device.h"
 #include "attn_internal.h"
@@ -46,6 +52,7 @@ constexpr int kBN = 64;       // keys per tile
 constexpr int kTileBytes = kBN * kD;
 constexpr float kP8Offset = 8.0f;       // log2 units subtracted from the running maximum
 constexpr float kP8Threshold = 0.5f;    // lazy rescale threshold for the fp8 path
+constexpr float kP8Margin = 6.0f;       // first-tile maximum raised by this (log2 units) in the fast pass
 
 // 16 bytes of a K tile, and the transposing 8-byte read of a V tile.
 __device__ __forceinline__ u32x4 lds_read_u8x16(const uint8_t* p) {
@@ -175,96 +182,125 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void attn_fwd_fp8_kernel(Fp8
   const float c = p.scale * dq * dk * kLog2e;  // raw fp8 dot product -> log2 units
 
   f32x16 acc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
-  float m_run = kMaxInit;
-  float l_run = 0.f;
+  float m_run, l_run;
+  // First key tile of this lane's row within this workgroup's share.
+  const int kfirst = max(kstart, tile_begin * kBN) / kBN * kBN;
 
-  if (tile_begin < tile_end) issue_tile(tile_begin * kBN, std::integral_constant<int, 0>{});
-  wait_dma();
-  __syncthreads();
-
-  auto tile_body = [&](int it, auto cur_c) {
-    constexpr int cur = decltype(cur_c)::value;
-    const int t0 = it * kBN;
-    if (it + 1 < tile_end) issue_tile(t0 + kBN, std::integral_constant<int, cur ^ 1>{});
-    if ((t0 < hi_max) && (t0 + kBN > lo_min)) {
-      const bool full = (t0 >= lo_max) && (t0 + kBN <= hi_min);
-      const uint8_t* ks = cur ? k_lds1 : k_lds0;
-      const uint8_t* vs = cur ? v_lds1 : v_lds0;
-      f32x16 s[2];
+  // One pass over the tiles. FAST: a row's running maximum is its maximum
+  // over its first tile plus kP8Margin, kept for the rest of the row (no
+  // tile maximum, no rescale); a probability that then exceeds the E4M3
+  // range turns into NaN in the conversion, and the wave redoes its rows
+  // with the tracked maximum (!FAST). A wave that is not `active` only
+  // copies tiles and meets the barriers.
+  auto run_tiles = [&](auto fast_c, bool active) {
+    constexpr bool FAST = decltype(fast_c)::value;
+    if (active) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const u32x4 lo = lds_read_u8x16(ks + koff[t][0] + kb * 32 * kD);
-          const u32x4 hi = lds_read_u8x16(ks + koff[t][1] + kb * 32 * kD);
-          const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          s[kb] = mfma_fp8(a, qf[t], s[kb]);
-        }
-      }
-      if (!full) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = t0 + kb * 32 + c_key(r, h);
-            s[kb][r] = (key < kstart || key >= kend) ? -INFINITY : s[kb][r];
-          }
-      }
-      float mx = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = max3f(mx, s[0][r], s[1][r]);
-      mx = max_lane_halves(mx);
-      const float m_tile = mx * c;
-      if (__any(m_tile > m_run + kP8Threshold)) {
-        const float m_new = fmaxf(m_run, m_tile);
-        const float alpha = fast_exp2(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] *= alpha;
-        m_run = m_new;
-      }
-      const float neg_m = kP8Offset - m_run;
-      // P^T bytes: byte 8q + e = key 16q + 8h + e = register 8(q & 1) + e of key block q / 2
-      i32x8 pf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float e[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          e[r] = fast_exp2(__builtin_fmaf(s[kb][r], c, neg_m));
-          l_run += e[r];
-        }
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          int word = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w], e[4 * w + 1], 0, false);
-          word = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w + 2], e[4 * w + 3], word, true);
-          pf[4 * kb + w] = word;
-        }
-      }
-      // O^T += V^T P^T
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        i32x8 a;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const i32x2 t = lds_read_tr8(vs + voff[db] + q * 16 * kD);
-          a[2 * q] = t[0];
-          a[2 * q + 1] = t[1];
-        }
-        acc[db] = mfma_fp8(a, pf, acc[db]);
-      }
+      for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+      m_run = kMaxInit;
+      l_run = 0.f;
     }
+    if (tile_begin < tile_end) issue_tile(tile_begin * kBN, std::integral_constant<int, 0>{});
     wait_dma();
     __syncthreads();
+
+  auto tile_body = [&](int it, auto cur_c) {
+      constexpr int cur = decltype(cur_c)::value;
+      const int t0 = it * kBN;
+      if (it + 1 < tile_end) issue_tile(t0 + kBN, std::integral_constant<int, cur ^ 1>{});
+      if (active && (t0 < hi_max) && (t0 + kBN > lo_min)) {
+        const bool full = (t0 >= lo_max) && (t0 + kBN <= hi_min);
+        const uint8_t* ks = cur ? k_lds1 : k_lds0;
+        const uint8_t* vs = cur ? v_lds1 : v_lds0;
+        f32x16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb] = f32x16{};
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const u32x4 lo = lds_read_u8x16(ks + koff[t][0] + kb * 32 * kD);
+            const u32x4 hi = lds_read_u8x16(ks + koff[t][1] + kb * 32 * kD);
+            const i32x8 a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            s[kb] = mfma_fp8(a, qf[t], s[kb]);
+          }
+        }
+        if (!full) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = t0 + kb * 32 + c_key(r, h);
+              s[kb][r] = (key < kstart || key >= kend) ? -INFINITY : s[kb][r];
+            }
+        }
+        if (!FAST || __any(t0 == kfirst)) {
+          float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+          for (int r = 1; r < 16; ++r) mx = max3f(mx, s[0][r], s[1][r]);
+          mx = max_lane_halves(mx);
+          const float m_tile = mx * c;
+          if (FAST) {
+            // rows entering their first tile; a row without keys here keeps kMaxInit
+            if (t0 == kfirst && m_tile > kMaxInit) m_run = m_tile + kP8Margin;
+          } else if (__any(m_tile > m_run + kP8Threshold)) {
+            const float m_new = fmaxf(m_run, m_tile);
+            const float alpha = fast_exp2(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] *= alpha;
+            m_run = m_new;
+          }
+        }
+        const float neg_m = kP8Offset - m_run;
+        // P^T bytes: byte 8q + e = key 16q + 8h + e = register 8(q & 1) + e of key block q / 2
+        i32x8 pf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          float e[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            e[r] = fast_exp2(__builtin_fmaf(s[kb][r], c, neg_m));
+            l_run += e[r];
+          }
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            int word = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w], e[4 * w + 1], 0, false);
+            word = __builtin_amdgcn_cvt_pk_fp8_f32(e[4 * w + 2], e[4 * w + 3], word, true);
+            pf[4 * kb + w] = word;
+          }
+        }
+        // O^T += V^T P^T
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          i32x8 a;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const i32x2 t = lds_read_tr8(vs + voff[db] + q * 16 * kD);
+            a[2 * q] = t[0];
+            a[2 * q + 1] = t[1];
+          }
+          acc[db] = mfma_fp8(a, pf, acc[db]);
+        }
+      }
+      wait_dma();
+      __syncthreads();
+    };
+
+
+    for (int it = tile_begin; it < tile_end; it += 2) {
+      tile_body(it, std::integral_constant<int, 0>{});
+      if (it + 1 < tile_end) tile_body(it + 1, std::integral_constant<int, 1>{});
+    }
   };
 
-  for (int it = tile_begin; it < tile_end; it += 2) {
-    tile_body(it, std::integral_constant<int, 0>{});
-    if (it + 1 < tile_end) tile_body(it + 1, std::integral_constant<int, 1>{});
-  }
+  run_tiles(std::true_type{}, true);
+  bool nan = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) nan = nan || (acc[i][r] != acc[i][r]);
+  const bool redo = __any(nan);
+  if (__syncthreads_or(redo)) run_tiles(std::false_type{}, redo);
 
   // O = acc * descale_v / l; LSE = (m - offset + log2 l) * ln 2
   const float l_tot = sum_lane_halves(l_run);
