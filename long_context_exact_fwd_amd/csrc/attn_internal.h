@@ -108,22 +108,25 @@ struct BwdParams {
 // (256-query blocks, one per CU, each K/V tile copied into LDS once per CU
 // instead of twice). Both give bitwise the same results. Taller blocks cost
 // more masked work on the causal diagonal and at segment boundaries and fill
-// the CUs less evenly; with D = 64 the 4-wave kernel also runs more waves
-// per SIMD (three at 161 VGPRs when measured, four now). Measured on MI355X (B * S = 32768 tokens,
-// Hq = 28, Hkv = 4), time of 8 waves over 4:
-//   D = 128 causal:     S = 2048 1.11, 4096 0.98, 8192 1.01, 16384 1.00, 32768 0.99
-//   D = 128 non-causal: S = 2048 0.99, 4096 0.92, 8192 0.97, 16384 0.98, 32768 0.97
-//   D = 64:             1.10 - 1.35 at every S, both masks
-//   packed (Hq 14, Hkv 2, seed-4 lengths): D = 128 1.07, D = 64 1.20
-// so 8 waves are taken for D = 128 without packing from S = 16384 (causal) or
-// S = 4096 (non-causal). The environment variable ATTN_FWD_WAVES=4 or 8
-// overrides the choice (for tests and tuning).
+// the CUs less evenly; with D = 64 the 4-wave kernel also runs four waves per
+// SIMD. Measured on MI355X (B * S = 32768 tokens, Hq = 28, Hkv = 4), time of
+// 8 waves over 4:
+//   D = 128 causal:     S = 2048 1.00, 4096 0.93, 8192 0.99, 16384 0.98, 32768 0.98
+//   D = 128 non-causal: S = 2048 0.95, 4096 0.85, 8192 0.97, 16384 0.97, 32768 0.97
+//   D = 64:             1.09 - 1.37 at every S, both masks
+//   other shapes (D = 128): B=2 Hq=Hkv=32 S=8192 causal 1.00, non-causal 0.96;
+//   B=4 Hq=Hkv=32 S=4096 causal 1.08; B=8 Hq=Hkv=32 S=2048 non-causal 0.94;
+//   packed (Hq 14, Hkv 2, seed-4 lengths) causal 1.01, non-causal 1.00
+// so 8 waves are taken for D = 128 without packing from S = 16384 (causal),
+// where they win on every shape measured, or S = 2048 (non-causal). The
+// environment variable ATTN_FWD_WAVES=4 or 8 overrides the choice (for tests
+// and tuning).
 int fwd_block_waves_env();  // 0 when unset
 inline int fwd_block_waves(int seqlen, int head_dim, int causal, bool packed) {
   const int forced = fwd_block_waves_env();
   if (forced == 4 || forced == 8) return forced;
   if (packed || head_dim != 128) return 4;
-  return seqlen >= (causal ? 16384 : 4096) ? 8 : 4;
+  return seqlen >= (causal ? 16384 : 2048) ? 8 : 4;
 }
 // The dQ pass's block height, the same choice for the backward: 128 queries
 // (4 waves, two workgroups per CU) or 256 (8 waves, one per CU, each K/V
