@@ -209,6 +209,17 @@ def test_rising_scores_redo_with_the_tracked_maximum(B, Hq, Hkv, S, D, causal, m
         assert all(np.all(np.isfinite(g)) for g in got) and max(errs) <= 2 * TOL_GRAD_REL
         outs.append(o)
     assert np.array_equal(outs[0], outs[1])
+    # the ring-merge forward redoes the same waves: into an empty running result it gives the forward's O, LSE
+    q, k, v = dev_bf16(x.q_bits), dev_bf16(x.k_bits), dev_bf16(x.v_bits)
+    scale = 1.0 / np.sqrt(D)
+    o_acc = torch.empty((B, S, Hq, D), dtype=torch.float32, device="cuda")
+    l_acc = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    o_out = torch.empty_like(q)
+    lca.fwd_merge(q, k, v, o_acc, l_acc, causal=causal, accumulate=False, o_out=o_out, scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_fwd(x.values("q"), x.values("k"), x.values("v"), causal=causal, scale=scale,
+                                  workers=None)
+    check_fwd(host(o_out), host(l_acc), ro, rl, tag="rising scores fwd_merge", abs_factor=2.0)
 
 
 def test_rising_scores_with_a_key_split():

@@ -130,6 +130,16 @@ def test_fp8_rising_scores_redo_with_the_tracked_maximum(B, Hq, Hkv, S, causal, 
         if not split:
             outs.append((o, lse))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    # the ring-merge forward redoes the same waves: into an empty running result it gives the forward's O, LSE
+    o_acc = torch.empty((B, S, Hq, D), dtype=torch.float32, device="cuda")
+    l_acc = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    lca.fwd_fp8_merge(q8, k8, v8, *ds, o_acc, l_acc, causal=causal, accumulate=False, scale=scale)
+    torch.cuda.synchronize()
+    o_h, l_h = host(o_acc), host(l_acc)
+    rr = rel_l2(o_h, ro)
+    worst = float(np.max(np.abs(l_h - rl) / lse_bound))
+    print(f"fwd_fp8_merge: O relL2={rr:.3e} LSE {worst:.2f} of its bound", flush=True)
+    assert np.all(np.isfinite(o_h)) and rr <= TOL_FP8_REL and worst <= 1.0
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,S,causal,lengths,ks", [(1, 1, 1, 8192, True, None, 4),
