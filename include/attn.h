@@ -62,6 +62,13 @@
  *     except ATTN_ERR_HIP, which reports a failed copy or launch
  *     (attn_last_hip_error() then gives the hipError_t value).
  *   - Determinism: no atomics; identical inputs give bitwise identical outputs.
+ *   - Tiling: the kernels pick their block heights from the sizes (128- or
+ *     256-query blocks for the forward and for the backward's dQ pass) and
+ *     split small grids; every choice gives results within the stated
+ *     tolerances, and the two block heights give bitwise the same results.
+ *     The environment variables ATTN_FWD_WAVES=4|8 and ATTN_DQ_WAVES=4|8
+ *     force the forward's and the dQ pass's block height (4 waves: 128
+ *     queries; 8 waves: 256), for tests and tuning.
  *   - Debug build: libmi355attn_debug.so exports this same interface, built
  *     with -DATTN_DEBUG. Its kernels check each LDS access made through the
  *     library's access helpers (tile copies, fragment and statistics reads,
