@@ -135,6 +135,8 @@ inline int fwd_block_waves(int seqlen, int head_dim, int causal, bool packed) {
 //   D = 128 causal:     S = 2048 1.09, 4096 1.02, 8192 1.00, 16384 0.99, 32768 0.99
 //   D = 128 non-causal: S = 2048 1.00, 4096 0.97, 8192 0.98, 16384 0.98, 32768 0.97
 //   D = 64:             1.03 - 1.35 at every S, both masks
+//   packed32k (Hq 14, Hkv 2, seed-4 lengths): causal 1.04, non-causal 1.02;
+//   B=2 Hq=Hkv=32 S=8192 causal 1.02
 // so 8 waves are taken for D = 128 without packing or key split from
 // S = 16384 (causal) or S = 4096 (non-causal). ATTN_DQ_WAVES=4 or 8
 // overrides it (for tests and tuning; a split dQ always runs 4 waves). The
