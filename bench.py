@@ -34,6 +34,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -75,13 +76,21 @@ KERNEL_OF_PHASE = {"attn_fwd": "attn_fwd_bf16_kernel", "bwd_delta": "attn_bwd_de
                    "bwd_dkdv": "attn_bwd_dkdv_kernel", "bwd_dq": "attn_bwd_dq_kernel"}
 
 
+def code_text(source: str) -> str:
+    """C++/HIP source with comments removed and blank space collapsed."""
+    source = re.sub(r"/\*.*?\*/", " ", source, flags=re.S)
+    source = re.sub(r"//[^\n]*", " ", source)
+    return " ".join(source.split())
+
+
 def kernel_source_hash(kernel: str) -> str:
-    """Hash of the source files a kernel is built from (counter records go stale when it changes)."""
+    """Hash of the code of the source files a kernel is built from (counter records go stale when the code
+    changes, not when its comments do)."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "long_context_exact_fwd_amd", "csrc", name), "rb") as f:
+        with open(os.path.join(ROOT, "long_context_exact_fwd_amd", "csrc", name), encoding="utf-8") as f:
             h.update(name.encode())
-            h.update(f.read())
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

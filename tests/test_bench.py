@@ -49,6 +49,13 @@ def test_kernel_sources_exist_and_hash_stably():
     assert set(bench.KERNEL_OF_PHASE.values()) <= set(bench.KERNEL_SOURCES)
 
 
+def test_counter_record_hash_ignores_comments_only():
+    code = "int f(int a) {\n  return a + 1;  // one more\n}\n/* note */\n"
+    assert bench.code_text(code) == bench.code_text(code.replace("one more", "plus one").replace("note", "x"))
+    assert bench.code_text(code) == bench.code_text(code.replace("\n", "\n\n  "))
+    assert bench.code_text(code) != bench.code_text(code.replace("a + 1", "a + 2"))
+
+
 def test_cpu_baseline_fields_and_extrapolation():
     """The CPU baseline reports threads and host cores apart, the CPU model, a single-thread time, the
     flops the oracle executes (12 D per pair) and whole-workload times labelled as extrapolated."""
