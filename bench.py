@@ -568,6 +568,23 @@ def mfma_ceiling_case(dev, iters=40000, reps=5):
     return res
 
 
+def build_info() -> dict:
+    """How libmi355attn.so was compiled (the flags long_context_exact_fwd_amd/build.py passes to hipcc)."""
+    from long_context_exact_fwd_amd import build as b
+    flags = [f for f in b.CFLAGS if not f.startswith("-I") and not os.path.isabs(f) and "include" not in f]
+    return {"compiler": os.path.basename(b.HIPCC), "arch": b.ARCH, "flags": " ".join(flags),
+            "library": os.path.basename(b.LIB)}
+
+
+def device_info(dev) -> dict:
+    """What the HIP runtime reports for the device; the clock under load is measured by mfma_ceiling."""
+    import torch
+    pr = torch.cuda.get_device_properties(dev)
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", ""), "compute_units": pr.multi_processor_count,
+            "memory_gib": round(pr.total_memory / 2 ** 30, 1), "torch": torch.__version__,
+            "hip": getattr(torch.version, "hip", None)}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -671,6 +688,8 @@ def main(argv=None) -> int:
         "kernels": per_kernel,
         "cpu_baseline": None,
         "workloads": None,
+        "build": build_info(),
+        "device": device_info(dev),
     }
     if not a.no_secondary:
         del step

@@ -49,6 +49,12 @@ def test_kernel_sources_exist_and_hash_stably():
     assert set(bench.KERNEL_OF_PHASE.values()) <= set(bench.KERNEL_SOURCES)
 
 
+def test_build_info_names_the_compile_flags():
+    info = bench.build_info()
+    assert info["arch"] == "gfx950" and "--offload-arch=gfx950" in info["flags"] and "-packed-fp32-ops" in info["flags"]
+    assert not any(tok.startswith("/") for tok in info["flags"].split())
+
+
 def test_counter_record_hash_ignores_comments_only():
     code = "int f(int a) {\n  return a + 1;  // one more\n}\n/* note */\n"
     assert bench.code_text(code) == bench.code_text(code.replace("one more", "plus one").replace("note", "x"))
