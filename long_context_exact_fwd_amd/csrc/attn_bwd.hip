@@ -8,6 +8,8 @@
 //   dV_j = sum_i P_ij dO_i            dP_ij = dO_i . V_j
 //   Delta_i = dO_i . O_i              dS_ij = P_ij (dP_ij - Delta_i)
 //   dQ_i = scale sum_j dS_ij K_j      dK_j = scale sum_i dS_ij Q_i
+// (Delta_i = sum_j P_ij dP_ij in rows that see fewer than 64 keys, where the
+// bf16 rounding of the given O would dominate dP - Delta.)
 // Split into two passes so that nothing is accumulated with atomics:
 //   * dK/dV: one workgroup of 8 waves per (b, h_kv, 128 keys). Two waves share
 //     each 32 keys: wave A holds K, computes S and P and accumulates dV^T;
@@ -102,7 +104,8 @@ __device__ void block_order(const BwdParams& p, int wg) {
 }
 
 // ---------------------------------------------------------------------------
-// Delta_i = dO_i . O_i and LSE_i * log2(e), both fp32 [B, Hq, S]; the last
+// Delta_i = dO_i . O_i and LSE_i * log2(e), both fp32 [B, Hq, S] (the rows
+// with fewer than 64 keys get their Delta again from the next kernel); the last
 // ceil(num_blk * head_split / 256) + ceil(num_dq_blk * key_split / 256)
 // workgroups write the work order instead.
 // ---------------------------------------------------------------------------
@@ -172,6 +175,92 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
       p.lse2[bh * p.stat_stride + i] = p.lse[bh * p.seqlen + i] * kLog2e;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Delta of the rows that see fewer than 64 keys, from its definition:
+// Delta_i = sum_j P_ij dP_ij, with P_ij = exp2(s_ij c - LSE_i log2 e) and
+// dP_ij = dO_i . V_j, instead of dO_i . O_i. O reaches the backward rounded
+// to bf16; in a row whose softmax sits on a few keys, dP - Delta is a small
+// difference that this rounding would dominate (a two-key row can lose the
+// gradient's second digit). Launched after attn_bwd_delta_kernel in the
+// Delta phase, over the first 63 rows of each causal segment (every row of
+// a shorter non-causal segment), one wave per row and lane = key, as the
+// forward's few-key kernel. With fp8 inputs q, k, v hold the E4M3 codes and c
+// carries the descales of Q and K; dP then lacks d_v, which is how Delta is
+// stored for those inputs.
+// ---------------------------------------------------------------------------
+constexpr int kFewRowsPerWgB = 4;  // one wave per row
+constexpr int kFewBlocksB = (kFewKeyLimit - 1 + kFewRowsPerWgB - 1) / kFewRowsPerWgB;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_bwd_delta_fewkeys_kernel(BwdParams p) {
+  constexpr int C = D / 8;  // 16-byte chunks per row
+  // K and V rows with chunk c of row j stored at chunk (c + j) % C, so that
+  // 64 lanes reading one chunk each of 64 different rows hit different banks
+  __shared__ __attribute__((aligned(16))) __bf16 ks[kFewKeyLimit - 1][D];
+  __shared__ __attribute__((aligned(16))) __bf16 vs[kFewKeyLimit - 1][D];
+  __shared__ __attribute__((aligned(16))) float qs[kFewRowsPerWgB][D];
+  __shared__ __attribute__((aligned(16))) float gs[kFewRowsPerWgB][D];
+  const int hq = blockIdx.y;
+  const int b = blockIdx.z;
+  const int seg = (int)blockIdx.x / kFewBlocksB;
+  const int rblk = (int)blockIdx.x % kFewBlocksB;
+  int s0 = 0, s1 = p.seqlen;
+  if (p.cu_seqlens != nullptr) {
+    // clamped to [0, seqlen): a malformed array gives meaningless rows, never a stray address
+    s0 = max(0, min(p.cu_seqlens[seg], p.seqlen));
+    s1 = max(s0, min(p.cu_seqlens[seg + 1], p.seqlen));
+  }
+  const int len = s1 - s0;
+  // these rows see keys [s0, s0 + nrows) only
+  const int nrows = few_key_rows(len, CAUSAL);
+  if (rblk * kFewRowsPerWgB >= nrows) return;  // uniform over the workgroup
+  const int hk = hq / (p.hq / p.hkv);
+  const size_t q_stride = (size_t)p.hq * D, kv_stride = (size_t)p.hkv * D;
+  const __bf16* kg = p.k + ((size_t)b * p.seqlen + s0) * kv_stride + hk * D;
+  const __bf16* vg = p.v + ((size_t)b * p.seqlen + s0) * kv_stride + hk * D;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < nrows * C; e += 256) {
+    const int j = e / C, cc = e % C;
+    lds_store16g(&ks[j][((cc + j) % C) * 8], load16(kg + (size_t)j * kv_stride + cc * 8));
+    lds_store16g(&vs[j][((cc + j) % C) * 8], load16(vg + (size_t)j * kv_stride + cc * 8));
+  }
+  for (int e = tid; e < kFewRowsPerWgB * D; e += 256) {
+    const int w = e / D, d = e % D;
+    const int rl = min(rblk * kFewRowsPerWgB + w, nrows - 1);
+    const size_t at = ((size_t)b * p.seqlen + s0 + rl) * q_stride + hq * D + d;
+    qs[w][d] = (float)p.q[at];
+    gs[w][d] = (float)p.dout[at];
+  }
+  __syncthreads();
+  const int wave = tid >> 6, lane = tid & 63;
+  const int row_local = rblk * kFewRowsPerWgB + wave;
+  if (row_local >= nrows) return;  // whole waves leave
+  const int r = s0 + row_local;
+  const int nk = CAUSAL ? row_local + 1 : nrows;  // keys s0 .. s0 + nk - 1
+  float c = p.scale_log2e;
+  if (p.descale_q != nullptr) c = p.scale * p.descale_q[0] * p.descale_k[0] * kLog2e;
+  const size_t bh = (size_t)b * p.hq + hq;
+  const float lse2 = p.lse[bh * p.seqlen + r] * kLog2e;
+  float pdp = 0.f;
+  if (lane < nk) {
+    float sdot = 0.f, gdot = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < C; ++cc) {
+      const bf16x8 kv = lds_load16<bf16x8>(&ks[lane][((cc + lane) % C) * 8]);
+      const bf16x8 vv = lds_load16<bf16x8>(&vs[lane][((cc + lane) % C) * 8]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sdot = __builtin_fmaf(qs[wave][cc * 8 + e], (float)kv[e], sdot);
+        gdot = __builtin_fmaf(gs[wave][cc * 8 + e], (float)vv[e], gdot);
+      }
+    }
+    pdp = exp2f(sdot * c - lse2) * gdot;
+  }
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) pdp += __shfl_xor(pdp, x);
+  if (lane == 0) p.delta[bh * p.stat_stride + r] = pdp;
 }
 
 // ---------------------------------------------------------------------------
@@ -924,6 +1013,12 @@ hipError_t launch_bwd(const BwdParams& p_in, unsigned phases, hipStream_t stream
         (q.num_blk * (long)q.head_split + 255) / 256 + (q.num_dq_blk * (long)q.key_split + 255) / 256;
     dim3 grid((unsigned)(nstat + npadwg + norder));
     hipLaunchKernelGGL((attn_bwd_delta_kernel<D, CAUSAL>), grid, dim3(256), 0, stream, q);
+    // rows with fewer than 64 visible keys: none for a dense non-causal call with S >= 64
+    if (CAUSAL || q.cu_seqlens != nullptr || q.seqlen < kFewKeyLimit) {
+      const int nseg = q.cu_seqlens != nullptr ? q.num_seqs : 1;
+      const dim3 fgrid((unsigned)nseg * kFewBlocksB, q.hq, q.batch);
+      hipLaunchKernelGGL((attn_bwd_delta_fewkeys_kernel<D, CAUSAL>), fgrid, dim3(256), 0, stream, q);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

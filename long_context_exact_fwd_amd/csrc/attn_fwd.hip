@@ -56,7 +56,7 @@ namespace {
 constexpr int kBN = 64;  // keys per tile
 // Rows that see fewer keys than this are recomputed (or, in a ring merge,
 // merged) by attn_fwd_fewkeys_kernel, not by the tiled kernel.
-constexpr int kFewKeys = 64;
+constexpr int kFewKeys = kFewKeyLimit;
 
 // WAVES waves of 32 queries per workgroup: 4 (128-query blocks, two
 // workgroups per CU) or 8 (256-query blocks, one workgroup per CU, so each
@@ -541,7 +541,7 @@ __global__ __launch_bounds__(256) void attn_fwd_fewkeys_kernel(FwdParams p) {
   }
   const int len = s1 - s0;
   // these rows see keys [s0, s0 + nrows) only
-  const int nrows = CAUSAL ? min(kFewKeys - 1, len) : (len < kFewKeys ? len : 0);
+  const int nrows = few_key_rows(len, CAUSAL);
   if (rblk * kFewRowsPerWg >= nrows) return;  // uniform over the workgroup
   const int hk = hq / (p.hq / p.hkv);
   const size_t q_stride = (size_t)p.hq * D, kv_stride = (size_t)p.hkv * D;

@@ -27,6 +27,15 @@ ATTN_HD bool lds_access_ok(uint32_t addr, uint32_t bytes, uint32_t align, uint32
   return (addr & (align - 1u)) == 0u && addr <= size && bytes <= size - addr;
 }
 
+// Rows that see fewer than 64 keys: the first 63 rows of a causal segment of
+// `len` rows, every row of a shorter non-causal segment. They are rows
+// [0, n) of the segment, n = few_key_rows(len, causal), and see at most keys
+// [0, n) of it; the tiled kernels leave them to the one-wave-per-row kernels.
+constexpr int kFewKeyLimit = 64;
+ATTN_HD int few_key_rows(int len, bool causal) {
+  return causal ? imin(kFewKeyLimit - 1, len) : (len < kFewKeyLimit ? len : 0);
+}
+
 // Swap bits 2 and 3 of a row index in [0, 32): the K (or Q, dO) row a lane
 // loads for the score product, so that C-layout register r of lane half h
 // holds key 16 * (r / 8) + 8 * h + r % 8.

@@ -70,7 +70,7 @@ struct BwdParams {
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
-  float* delta;  // workspace [B, Hq, stat_stride]: Delta_i = dO_i . O_i
+  float* delta;  // workspace [B, Hq, stat_stride]: Delta_i = dO_i . O_i (sum_j P_ij dP_ij with < 64 keys)
   float* lse2;   // workspace [B, Hq, stat_stride]: LSE_i * log2(e)
   int stat_stride;  // seqlen rounded up to kStatAlign; the padding holds zeros
   int* order;       // workspace: dK/dV work order [num_blk * head_split], then dQ's [num_dq_blk * key_split]

@@ -41,6 +41,21 @@ TOL_ZERO_GRAD_ABS = 1e-3  # where the exact gradient is zero
 TOL_FP8_REL = 5e-2
 
 
+def delta_from_o_rows(S, causal, cu_seqlens=None) -> np.ndarray:
+    """Rows [S] whose Delta the backward takes from the O it is given (Delta_i = dO_i . O_i): rows with at
+    least 64 visible keys. The others (the first 63 rows of a causal segment, every row of a non-causal
+    segment shorter than 64) get Delta_i = sum_j P_ij dP_ij from its definition, so the rounding of the
+    given O does not reach their gradients."""
+    edges = np.asarray(cu_seqlens if cu_seqlens is not None else [0, S], dtype=np.int64)
+    out = np.zeros(S, dtype=bool)
+    for a, b in zip(edges[:-1], edges[1:]):
+        if causal:
+            out[a + 63:b] = True
+        elif b - a >= 64:
+            out[a:b] = True
+    return out
+
+
 def bf16_ulp(x) -> np.ndarray:
     """Spacing of bfloat16 values (8 significant bits) at |x|: 2^(floor(log2|x|) - 7)."""
     a = np.abs(np.asarray(x, dtype=np.float64))

@@ -409,8 +409,37 @@ void check_lds_rule() {
   CHECK(!lds_access_ok(0, 16, 16, 0), "lds rule: empty allocation");
 }
 
+// The rows of the one-wave-per-row kernels (the forward's few-key rows and
+// the backward's Delta from its definition): for every segment length and
+// mask, row r of the segment is one of rows [0, few_key_rows) exactly when it
+// sees fewer than 64 keys, the grid's 4-row blocks cover those rows, and the
+// keys a row reads and the staged K/V rows stay inside the 63-row LDS arrays.
+void check_few_key_rows() {
+  constexpr int kBlocks = 16, kRowsPerWg = 4, kLdsRows = kFewKeyLimit - 1;
+  for (int len = 0; len <= 300; ++len)
+    for (bool causal : {true, false}) {
+      const int n = few_key_rows(len, causal);
+      CHECK(0 <= n && n <= len && n <= kLdsRows, "few-key rows: len %d causal %d gives %d rows", len, causal, n);
+      CHECK(n <= kBlocks * kRowsPerWg, "few-key rows: %d rows, %d blocks of %d", n, kBlocks, kRowsPerWg);
+      for (int r = 0; r < len; ++r) {
+        const int visible = causal ? r + 1 : len;
+        CHECK((visible < kFewKeyLimit) == (r < n), "few-key rows: len %d causal %d row %d sees %d keys", len, causal,
+              r, visible);
+        if (r < n) CHECK(visible <= n, "few-key rows: row %d reads %d keys of %d staged", r, visible, n);
+      }
+    }
+  // the bank swizzle (c + j) % C of the staged rows is a permutation of each row's chunks
+  for (int C : {8, 16})
+    for (int j = 0; j < kLdsRows; ++j) {
+      std::set<int> seen;
+      for (int c = 0; c < C; ++c) seen.insert((c + j) % C);
+      CHECK((int)seen.size() == C, "few-key rows: swizzle of row %d", j);
+    }
+}
+
 int main() {
   check_lds_rule();
+  check_few_key_rows();
   check_layouts<128>();
   check_layouts<64>();
   check_fp8();

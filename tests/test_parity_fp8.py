@@ -215,3 +215,35 @@ def test_fp8_forward_then_backward(B, Hq, Hkv, S, causal, lengths):
     """attn_fwd_fp8 then attn_bwd_fp8 on its own O and LSE: the forward's fp8 probabilities enter the
     gradient through Delta = rowsum(dO * O), so the fp8 bound applies, rel-L2 <= 5e-2 per tensor."""
     _fp8_bwd_case(B, Hq, Hkv, S, causal, lengths, exact_o=False)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,causal,lengths", [(1, 2, 1, 2, True, None), (2, 4, 2, 9, True, None),
+                                                       (1, 4, 2, 33, False, None),
+                                                       (1, 4, 1, 128, True, [1, 2, 7, 50, 68])])
+def test_fp8_few_key_rows_backward_against_the_exact_gradient(B, Hq, Hkv, S, causal, lengths):
+    """attn_bwd_fp8 on rows that see fewer than 64 keys, given the exact O (bf16) and LSE: Delta comes from
+    its definition there (the widened codes are exact, so P and dP are those of the dequantised inputs),
+    and the gradients are held to rel-L2 <= 5e-3 of the exact ones, half the general bar, on three seeds."""
+    import torch
+    import long_context_exact_fwd_amd as lca
+    D = 128
+    for seed in (91, 92, 93):
+        tag = f"fp8 few keys B={B} Hq={Hq} Hkv={Hkv} S={S} causal={causal} lengths={lengths} seed={seed}"
+        print(tag, flush=True)
+        x = si.make_inputs(B, Hq, Hkv, S, D, seed, lengths=lengths, fp8=True, with_do=True)
+        q8, k8, v8 = dev_u8(x.q_bits), dev_u8(x.k_bits), dev_u8(x.v_bits)
+        ds = [torch.tensor([float(d)], dtype=torch.float32, device="cuda") for d in x.descale]
+        cu = dev_i32(x.cu_seqlens) if x.cu_seqlens is not None else None
+        scale = 1.0 / np.sqrt(D)
+        qv, kv, vv = (oracle.e4m3_decode(b) * float(d) for b, d in zip((x.q_bits, x.k_bits, x.v_bits), x.descale))
+        ro, rl = oracle.attention_fwd(qv, kv, vv, causal=causal, scale=scale, cu_seqlens=x.cu_seqlens, workers=None)
+        o = torch.from_numpy(ro).to(torch.bfloat16).cuda()
+        lse = torch.from_numpy(rl).to(torch.float32).cuda()
+        do = lca.bf16_from_bits(x.do_bits, "cuda")
+        dq, dk, dv = lca.bwd_fp8(q8, k8, v8, *ds, o, lse, do, causal=causal, cu_seqlens=cu, scale=scale)
+        torch.cuda.synchronize()
+        rq, rk, rv = oracle.attention_bwd(qv, kv, vv, x.values("do"), causal=causal, scale=scale,
+                                          cu_seqlens=x.cu_seqlens, workers=None)
+        errs = [rel_l2(host(g), r) for g, r in ((dq, rq), (dk, rk), (dv, rv))]
+        print(f"{tag}: dQ {errs[0]:.3e} dK {errs[1]:.3e} dV {errs[2]:.3e}", flush=True)
+        assert max(errs) <= 5e-3, tag

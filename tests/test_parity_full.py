@@ -17,8 +17,8 @@ import pytest
 
 import oracle
 import seeded_inputs as si
-from tests.gpu_helpers import (TOL_FP8_REL, TOL_GRAD_REL, TOL_LSE, check_fwd, dev_i32, dev_u8, host, max_abs,
-                               rel_l2)
+from tests.gpu_helpers import (TOL_FP8_REL, TOL_GRAD_REL, TOL_LSE, check_fwd, delta_from_o_rows, dev_i32, dev_u8,
+                               host, max_abs, rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -185,10 +185,12 @@ def test_long_sequence_256k_sampled():
     gq = np.stack([dq_h[0, i, h] for _, h, i in picks])
     e_q = rel_l2(gq, rq)
     # the same rows against the oracle's dQ given the kernel's bf16 O (Delta = dO . O with that O enters
-    # dS linearly: dQ_i moves by -scale eps_i sum_j P_ij K_j, eps_i = dO_i . (O_given - O)_i)
+    # dS linearly: dQ_i moves by -scale eps_i sum_j P_ij K_j, eps_i = dO_i . (O_given - O)_i, in the rows
+    # that see at least 64 keys; the first 63 take Delta from its definition)
     kbar, _ = oracle.attention_fwd_rows(qv, kv, kv, picks, causal=True, scale=scale)
     go = np.stack([o_h[0, i, h] for _, h, i in picks])
     eps = np.einsum("nd,nd->n", np.stack([dov[0, i, h] for _, h, i in picks]), go - ro)[:, None]
+    eps *= delta_from_o_rows(S, True)[[i for _, _, i in picks]][:, None]
     e_q_given = rel_l2(gq, rq - scale * eps * kbar)
     sk = dk_h[0, :, 0].sum(axis=0)
     e_k = float(np.linalg.norm(sk) / np.linalg.norm(dk_h[0, :, 0]))

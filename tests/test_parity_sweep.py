@@ -47,11 +47,26 @@ def _draw(i):
 CASES = [_draw(i) for i in range(int(os.environ.get("ATTN_SWEEP_CASES", "24")))]
 
 
+# draws past the default 24 that failed a wider sweep once, kept as regression cases
+REGRESSION = [
+    457,  # S=2 causal, D=64: Delta from the bf16 O dominated dP - Delta (fixed by Delta from its definition)
+]
+
+
 @pytest.mark.parametrize("case", range(len(CASES)))
 def test_sweep_case(case):
+    _sweep_case(case, CASES[case])
+
+
+@pytest.mark.parametrize("draw", REGRESSION)
+def test_sweep_regression(draw):
+    _sweep_case(draw, _draw(draw))
+
+
+def _sweep_case(case, shape):
     import torch
     import long_context_exact_fwd_amd as lca
-    B, Hq, Hkv, S, D, causal, lengths = CASES[case]
+    B, Hq, Hkv, S, D, causal, lengths = shape
     print(f"sweep {case}: B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} causal={causal} lengths={lengths}", flush=True)
     x = si.make_inputs(B, Hq, Hkv, S, D, seed=2000 + case, lengths=lengths)
     q, k, v, do = dev_bf16(x.q_bits), dev_bf16(x.k_bits), dev_bf16(x.v_bits), dev_bf16(x.do_bits)
@@ -86,15 +101,39 @@ def test_sweep_case(case):
 FP8_CASES = [c for c in CASES if c[4] == 128][: max(8, len(CASES) // 3)]
 
 
+def _fp8_draw(j):
+    """The j-th head-dim-128 draw: FP8_CASES[j] of a sweep wide enough to hold it."""
+    i = -1
+    while j >= 0:
+        i += 1
+        if _draw(i)[4] == 128:
+            j -= 1
+    return _draw(i)
+
+
+FP8_REGRESSION = [
+    319,  # S=2 causal: as draw 457 of the bf16 sweep
+]
+
+
 @pytest.mark.parametrize("case", range(len(FP8_CASES)))
 def test_sweep_fp8_case(case):
     """The head-dim-128 draws through the fp8 entry points: attn_fwd_fp8 (O rel-L2 <= 5e-2, LSE <= 1e-3),
     attn_bwd_fp8 from the exact O (rel-L2 <= 1e-2) and attn_fwd_fp8_merge (fp8 bounds), against the oracle on the
     dequantised inputs."""
+    _sweep_fp8_case(case, FP8_CASES[case])
+
+
+@pytest.mark.parametrize("case", FP8_REGRESSION)
+def test_sweep_fp8_regression(case):
+    _sweep_fp8_case(case, _fp8_draw(case))
+
+
+def _sweep_fp8_case(case, shape):
     import torch
     import long_context_exact_fwd_amd as lca
-    from tests.gpu_helpers import TOL_FP8_REL, TOL_LSE, dev_u8, max_abs, rel_l2
-    B, Hq, Hkv, S, D, causal, lengths = FP8_CASES[case]
+    from tests.gpu_helpers import TOL_FP8_REL, TOL_LSE, TOL_ZERO_GRAD_ABS, dev_u8, max_abs, rel_l2
+    B, Hq, Hkv, S, D, causal, lengths = shape
     print(f"fp8 sweep {case}: B={B} Hq={Hq} Hkv={Hkv} S={S} causal={causal} lengths={lengths}", flush=True)
     x = si.make_inputs(B, Hq, Hkv, S, D, seed=4000 + case, lengths=lengths, fp8=True)
     q8, k8, v8 = dev_u8(x.q_bits), dev_u8(x.k_bits), dev_u8(x.v_bits)
@@ -121,16 +160,12 @@ def test_sweep_fp8_case(case):
         check_grads([("dQ", host(dq), rq), ("dK", host(dk), rk), ("dV", host(dv), rv)], tag="fp8 bwd")
     else:
         # every row sees one key (S = 1 or segments of length 1 with the causal mask): the exact dQ and dK are
-        # zero, and what the kernel returns is the effect of the bf16 rounding of the O it is given. With
-        # delta_i = sum_d |dO_id (O_id - bf16(O_id))| the error of Delta_i, |dS_ij| <= delta_i + fp32 noise,
-        # so |dQ|, |dK| <= scale * max delta * max(|K|, |Q|), plus the 1e-3 of the zero-reference bound.
-        o_b = host(o_ex)
-        dmax = float(np.max(np.sum(np.abs(dov * (ro - o_b)), axis=-1)))
-        bound = 1e-3 + scale * dmax * float(max(np.abs(kv).max(), np.abs(qv).max()))
+        # zero. These rows take Delta = P dP from its definition (not dO . O from the bf16 O, whose rounding of
+        # the dequantised values would otherwise show), with P = 1 up to fp32 rounding, so dS is fp32 noise
+        # and dQ, dK stay within the zero-reference bound of 1e-3.
         e_q, e_k, e_v = max_abs(host(dq), rq), max_abs(host(dk), rk), rel_l2(host(dv), rv)
-        print(f"fp8 bwd (one key per row): dQ maxabs={e_q:.3e} dK maxabs={e_k:.3e} bound {bound:.3e}, "
-              f"dV relL2={e_v:.3e}", flush=True)
-        assert e_q <= bound and e_k <= bound and e_v <= 1e-2
+        print(f"fp8 bwd (one key per row): dQ maxabs={e_q:.3e} dK maxabs={e_k:.3e}, dV relL2={e_v:.3e}", flush=True)
+        assert e_q <= TOL_ZERO_GRAD_ABS and e_k <= TOL_ZERO_GRAD_ABS and e_v <= 1e-2
     rng = np.random.default_rng(5000 + case)
     o1 = rng.standard_normal((B, S, Hq, D)).astype(np.float32)
     l1 = rng.uniform(-2.0, 8.0, (B, Hq, S)).astype(np.float32)
