@@ -153,8 +153,9 @@ attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8,
 /* Bytes of device workspace attn_bwd needs for these sizes. It holds, in
  * order: two fp32 per-row arrays [batch, hq, S64] (S64 = seqlen rounded up to
  * a multiple of 64): Delta_i = dO_i . O_i (sum_j P_ij dP_ij in rows that see
- * fewer than 64 keys) and LSE_i * log2(e), the padding rows written as zeros; the int32 work order of the dK/dV and dQ kernels
- * (NB * (hsplit + ksplit) entries, NB = ceil(seqlen / 128)); then, each
+ * fewer than 64 keys, all of them in this call) and LSE_i * log2(e), the
+ * padding rows written as zeros; the int32 work order of the dK/dV and dQ
+ * kernels (NB * (hsplit + ksplit) entries, NB = ceil(seqlen / 128)); then, each
  * 256-byte aligned, fp32 partial dK and dV (8 * hsplit * batch * seqlen * hkv
  * * head_dim bytes) when the dK/dV pass splits a GQA group's query heads over
  * hsplit > 1 workgroups, and fp32 partial dQ (4 * ksplit * batch * seqlen *

@@ -186,11 +186,18 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
 // gradient's second digit). Launched after attn_bwd_delta_kernel in the
 // Delta phase, over the first 63 rows of each causal segment (every row of
 // a shorter non-causal segment), one wave per row and lane = key, as the
-// forward's few-key kernel. With fp8 inputs q, k, v hold the E4M3 codes and c
+// forward's few-key kernel.
+// The sum is Delta only if the call holds every key the row sees: a ring's
+// chunk pair is called with the whole row's O and LSE, and keys of other
+// chunks carry the rest of P. Given the row's LSE, sum_j P_ij over the call's
+// keys is 1 exactly when no key is missing, so a row keeps dO . O unless that
+// sum is within 2^-10 of 1 (then the missing keys hold at most that much of
+// P, and change Delta by at most 2^-10 max |dP|, about the rounding of dO . O). With fp8 inputs q, k, v hold the E4M3 codes and c
 // carries the descales of Q and K; dP then lacks d_v, which is how Delta is
 // stored for those inputs.
 // ---------------------------------------------------------------------------
 constexpr int kFewRowsPerWgB = 4;  // one wave per row
+constexpr float kWholeRowTol = 0.0009765625f;  // 2^-10
 constexpr int kFewBlocksB = (kFewKeyLimit - 1 + kFewRowsPerWgB - 1) / kFewRowsPerWgB;
 
 template <int D, bool CAUSAL>
@@ -243,7 +250,7 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_fewkeys_kernel(BwdParams p
   if (p.descale_q != nullptr) c = p.scale * p.descale_q[0] * p.descale_k[0] * kLog2e;
   const size_t bh = (size_t)b * p.hq + hq;
   const float lse2 = p.lse[bh * p.seqlen + r] * kLog2e;
-  float pdp = 0.f;
+  float pdp = 0.f, psum = 0.f;
   if (lane < nk) {
     float sdot = 0.f, gdot = 0.f;
 #pragma unroll
@@ -256,11 +263,16 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_fewkeys_kernel(BwdParams p
         gdot = __builtin_fmaf(gs[wave][cc * 8 + e], (float)vv[e], gdot);
       }
     }
-    pdp = exp2f(sdot * c - lse2) * gdot;
+    psum = exp2f(sdot * c - lse2);
+    pdp = psum * gdot;
   }
 #pragma unroll
-  for (int x = 32; x >= 1; x >>= 1) pdp += __shfl_xor(pdp, x);
-  if (lane == 0) p.delta[bh * p.stat_stride + r] = pdp;
+  for (int x = 32; x >= 1; x >>= 1) {
+    pdp += __shfl_xor(pdp, x);
+    psum += __shfl_xor(psum, x);
+  }
+  // false for a NaN sum (a non-finite LSE): the row keeps dO . O
+  if (lane == 0 && fabsf(psum - 1.f) <= kWholeRowTol) p.delta[bh * p.stat_stride + r] = pdp;
 }
 
 // ---------------------------------------------------------------------------
