@@ -58,6 +58,10 @@ MUTATIONS = [
     ("segment end not clamped", "end = imin(seqlen, imax(cu[hi], i + 1));", "end = imax(cu[hi], i + 1);"),
     ("workspace order offset overlaps the statistics", "return (size_t)8 * batch * hq * stat_stride_for(seqlen);",
      "return (size_t)4 * batch * hq * stat_stride_for(seqlen);"),
+    ("few-key rows of a causal segment one too many", "return causal ? imin(kFewKeyLimit - 1, len)",
+     "return causal ? imin(kFewKeyLimit, len)"),
+    ("few-key rows of a non-causal segment up to length 64", "(len < kFewKeyLimit ? len : 0)",
+     "(len <= kFewKeyLimit ? len : 0)"),
 ]
 
 
