@@ -453,3 +453,50 @@ def test_fwd_merge_extreme_weights(qk_std, lse_span):
     po, pl = oracle.attention_fwd(x.values("q"), x.values("k"), x.values("v"), causal=True, scale=scale, workers=None)
     ro, rl = oracle.merge_partials(o1.astype(np.float64), l1.astype(np.float64), po, pl)
     check_fwd(host(o_acc), host(l_acc), ro, rl, tag="fwd_merge extreme", abs_factor=2.0 if qk_std != 1.0 else 1.0)
+
+
+def test_few_key_delta_only_where_the_call_holds_the_whole_row():
+    """The Delta phase's two branches, read back from the workspace (its first fp32 array, [B, Hq, S64]).
+
+    A full call: rows 0..62 (fewer than 64 visible keys) hold sum_j P_ij dP_ij, which equals dO_i . O_i for the
+    exact O, so they match the oracle's Delta to fp32 rounding; later rows hold dO_i . O_i of the bf16 O the call
+    was given. A ring's diagonal chunk pair past the first chunk, called with the whole rows' O and LSE: the
+    call's keys carry only part of each row's P, so every row, its first 63 included, keeps dO . O of the given
+    O. The first chunk's diagonal pair holds whole rows and takes the sum again."""
+    import torch
+    lca = _lib()
+    B, Hq, Hkv, S, D, L = 1, 4, 2, 256, 128, 128
+    print(f"few-key Delta branches B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} chunk={L}", flush=True)
+    x, q, k, v, do = _ring_inputs(B, Hq, Hkv, S, D, seed=97)
+    scale = 1.0 / np.sqrt(D)
+    o, lse = lca.fwd(q, k, v, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    qv, kv, vv, dov = (x.values(n) for n in ("q", "k", "v", "do"))
+    ro, _ = oracle.attention_fwd(qv, kv, vv, causal=True, scale=scale, workers=None)
+    exact = np.einsum("bshd,bshd->bhs", dov, ro)                       # sum_j P_ij dP_ij
+    given = np.einsum("bshd,bshd->bhs", dov, host(o))                  # dO . O with the bf16 O
+    mag = np.einsum("bshd,bshd->bhs", np.abs(dov), np.abs(host(o)))   # scale of the fp32 rounding
+
+    def delta_of(a, b, causal_call):
+        n = b - a
+        ws = torch.empty(lca.bwd_workspace_bytes(B, Hq, Hkv, n, D) // 4 + 1, dtype=torch.float32, device="cuda")
+        sl = slice(a, b)
+        lca.bwd(q[:, sl].contiguous(), k[:, sl].contiguous(), v[:, sl].contiguous(), o[:, sl].contiguous(),
+                lse[:, :, sl].contiguous(), do[:, sl].contiguous(), causal=causal_call, scale=scale, workspace=ws,
+                phases=lca.BWD_DELTA)
+        torch.cuda.synchronize()
+        s64 = (n + 63) // 64 * 64
+        return ws[:B * Hq * s64].view(B, Hq, s64)[..., :n].double().cpu().numpy()
+
+    tol = 2.0 ** -18 * (mag + 1.0)
+    full = delta_of(0, S, True)
+    assert np.all(np.abs(full[..., :63] - exact[..., :63]) <= tol[..., :63]), "full call: rows 0..62 are not the sum"
+    assert np.all(np.abs(full[..., 63:] - given[..., 63:]) <= tol[..., 63:]), "full call: rows 63.. are not dO . O"
+    first = delta_of(0, L, True)
+    assert np.all(np.abs(first[..., :63] - exact[..., :63]) <= tol[..., :63]), "first chunk: rows 0..62"
+    pair = delta_of(L, 2 * L, True)
+    assert np.all(np.abs(pair - given[..., L:]) <= tol[..., L:]), "later diagonal chunk: Delta is not dO . O"
+    # the two branches differ here, so the checks above tell them apart
+    gap = float(np.max(np.abs(exact[..., :63] - given[..., :63]) / tol[..., :63]))
+    print(f"few-key Delta: largest |sum - dO.O| over the first 63 rows = {gap:.1f} x the fp32 tolerance", flush=True)
+    assert gap > 4.0
