@@ -171,7 +171,8 @@ size_t attn_bwd_workspace_bytes(int batch, int hq, int hkv, int seqlen, int head
  * bf16 and fully overwritten. For GQA, dk and dv sum over the query heads of
  * each group. workspace: at least attn_bwd_workspace_bytes() bytes, 16-byte
  * aligned, owned by the caller, contents on entry ignored.
- * Three kernels run on `stream` in order: Delta, dK/dV, dQ.
+ * Three phases run on `stream` in order: Delta (one kernel for dO . O and
+ * the work order, a second for the rows with fewer than 64 keys), dK/dV, dQ.
  */
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                      const void* dout, void* dq, void* dk, void* dv, void* workspace,
@@ -197,11 +198,11 @@ attn_status attn_bwd_accumulate(const void* q, const void* k, const void* v, con
                                 int causal, const int32_t* cu_seqlens, int num_seqs,
                                 float scale, attn_stream_t stream);
 
-/* One or more of the three backward kernels, in the fixed order Delta, dK/dV,
+/* One or more of the three backward phases, in the fixed order Delta, dK/dV,
  * dQ: attn_bwd(...) is attn_bwd_phases(ATTN_BWD_ALL, ...). Running the
  * phases as separate calls on one stream (Delta first) gives bitwise the
  * same result. It exists so that callers and profilers can time or schedule
- * each kernel on its own. Arguments as attn_bwd. dK/dV and dQ read the Delta
+ * each phase on its own. Arguments as attn_bwd. dK/dV and dQ read the Delta
  * and the block order that an earlier ATTN_BWD_DELTA call left in `workspace`.
  * phases: nonzero bitmask of the values below; other bits are invalid. */
 #define ATTN_BWD_DELTA 1u
