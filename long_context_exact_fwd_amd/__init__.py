@@ -127,13 +127,15 @@ def _ptr(t) -> ctypes.c_void_p:
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
-def _shape(q, k, cu_seqlens):
+def _shape(q, k, v, cu_seqlens):
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q, k, v must be [B, S, H, D]")
     B, S, Hq, D = q.shape
     Hkv = k.shape[2]
     if k.shape[0] != B or k.shape[1] != S or k.shape[3] != D:
         raise ValueError("k/v shape must be [B, S, Hkv, D] with q's B, S, D")
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError("v must have the shape of k")
     n = 0
     if cu_seqlens is not None:
         import torch
@@ -141,6 +143,19 @@ def _shape(q, k, cu_seqlens):
             raise ValueError("cu_seqlens must be a 1-D int32 device tensor")
         n = cu_seqlens.numel() - 1
     return B, S, Hq, Hkv, D, n
+
+
+def _expect(t, shape, dtype, what):
+    """A tensor the library reads or writes through a bare pointer: its size is fixed by the call's sizes."""
+    if not t.is_cuda or not t.is_contiguous() or t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} must be a contiguous {dtype} device tensor of shape {tuple(shape)}, "
+                         f"got {tuple(t.shape)} {t.dtype}")
+
+
+def _check_descales(*ts):
+    for t in ts:
+        if t.numel() < 1:
+            raise ValueError("descales must hold one float32 element each")
 
 
 def _check_tensors(*ts, dtype=None):
@@ -165,11 +180,13 @@ def fwd(q, k, v, *, causal: bool, cu_seqlens=None, scale: Optional[float] = None
     """
     import torch
     _check_tensors(q, k, v, dtype=torch.bfloat16)
-    B, S, Hq, Hkv, D, n = _shape(q, k, cu_seqlens)
+    B, S, Hq, Hkv, D, n = _shape(q, k, v, cu_seqlens)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     o = out if out is not None else torch.empty_like(q)
     l_ = lse if lse is not None else torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    _expect(o, (B, S, Hq, D), torch.bfloat16, "out")
+    _expect(l_, (B, Hq, S), torch.float32, "lse")
     ws = _fwd_workspace(B, Hq, Hkv, S, D, q.device, workspace, split)
     st = load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l_), _ptr(ws), B, Hq, Hkv, S, D,
                                  int(bool(causal)), _ptr(cu_seqlens), n, float(scale), _stream())
@@ -200,11 +217,14 @@ def fwd_fp8(q8, k8, v8, descale_q, descale_k, descale_v, *, causal: bool, cu_seq
     import torch
     _check_tensors(q8, k8, v8, dtype=torch.uint8)
     _check_tensors(descale_q, descale_k, descale_v, dtype=torch.float32)
-    B, S, Hq, Hkv, D, n = _shape(q8, k8, cu_seqlens)
+    B, S, Hq, Hkv, D, n = _shape(q8, k8, v8, cu_seqlens)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    _check_descales(descale_q, descale_k, descale_v)
     o = out if out is not None else torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device=q8.device)
     l_ = lse if lse is not None else torch.empty((B, Hq, S), dtype=torch.float32, device=q8.device)
+    _expect(o, (B, S, Hq, D), torch.bfloat16, "out")
+    _expect(l_, (B, Hq, S), torch.float32, "lse")
     ws = _fwd_workspace(B, Hq, Hkv, S, D, q8.device, workspace, split) if D == 128 else None
     st = load_library().attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(descale_q), _ptr(descale_k),
                                      _ptr(descale_v), _ptr(o), _ptr(l_), _ptr(ws), B, Hq, Hkv, S, D,
@@ -250,7 +270,7 @@ def fwd_merge(q, k, v, o_acc, lse_acc, *, causal: bool, accumulate: bool = True,
     import torch
     _check_tensors(q, k, v, dtype=torch.bfloat16)
     _check_tensors(o_acc, lse_acc, dtype=torch.float32)
-    B, S, Hq, Hkv, D, n = _shape(q, k, cu_seqlens)
+    B, S, Hq, Hkv, D, n = _shape(q, k, v, cu_seqlens)
     if tuple(o_acc.shape) != (B, S, Hq, D) or tuple(lse_acc.shape) != (B, Hq, S):
         raise ValueError("o_acc must be [B, S, Hq, D] and lse_acc [B, Hq, S]")
     if o_out is not None:
@@ -274,7 +294,8 @@ def fwd_fp8_merge(q8, k8, v8, descale_q, descale_k, descale_v, o_acc, lse_acc, *
     import torch
     _check_tensors(q8, k8, v8, dtype=torch.uint8)
     _check_tensors(descale_q, descale_k, descale_v, o_acc, lse_acc, dtype=torch.float32)
-    B, S, Hq, Hkv, D, n = _shape(q8, k8, cu_seqlens)
+    _check_descales(descale_q, descale_k, descale_v)
+    B, S, Hq, Hkv, D, n = _shape(q8, k8, v8, cu_seqlens)
     if tuple(o_acc.shape) != (B, S, Hq, D) or tuple(lse_acc.shape) != (B, Hq, S):
         raise ValueError("o_acc must be [B, S, Hq, D] and lse_acc [B, Hq, S]")
     if o_out is not None:
@@ -296,6 +317,19 @@ def bwd_workspace_bytes(batch: int, hq: int, hkv: int, seqlen: int, head_dim: in
     return int(load_library().attn_bwd_workspace_bytes(batch, hq, hkv, seqlen, head_dim))
 
 
+def _bwd_operands(o, lse, do, B, S, Hq, D):
+    import torch
+    _expect(o, (B, S, Hq, D), torch.bfloat16, "o")
+    _expect(do, (B, S, Hq, D), torch.bfloat16, "do")
+    _expect(lse, (B, Hq, S), torch.float32, "lse")
+
+
+def _bwd_outputs(dq, dk, dv, B, S, Hq, Hkv, D, dtype):
+    _expect(dq, (B, S, Hq, D), dtype, "dq")
+    _expect(dk, (B, S, Hkv, D), dtype, "dk")
+    _expect(dv, (B, S, Hkv, D), dtype, "dv")
+
+
 def bwd(q, k, v, o, lse, do, *, causal: bool, cu_seqlens=None, scale: Optional[float] = None, workspace=None,
         dq=None, dk=None, dv=None, phases: Optional[int] = None):
     """Backward, bf16. Returns (dq, dk, dv) shaped like q, k, v.
@@ -306,12 +340,14 @@ def bwd(q, k, v, o, lse, do, *, causal: bool, cu_seqlens=None, scale: Optional[f
     import torch
     _check_tensors(q, k, v, o, do, dtype=torch.bfloat16)
     _check_tensors(lse, dtype=torch.float32)
-    B, S, Hq, Hkv, D, n = _shape(q, k, cu_seqlens)
+    B, S, Hq, Hkv, D, n = _shape(q, k, v, cu_seqlens)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    _bwd_operands(o, lse, do, B, S, Hq, D)
     dq = dq if dq is not None else torch.empty_like(q)
     dk = dk if dk is not None else torch.empty_like(k)
     dv = dv if dv is not None else torch.empty_like(v)
+    _bwd_outputs(dq, dk, dv, B, S, Hq, Hkv, D, torch.bfloat16)
     nbytes = bwd_workspace_bytes(B, Hq, Hkv, S, D)
     if workspace is None:
         workspace = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=q.device)
@@ -334,10 +370,9 @@ def bwd_accumulate(q, k, v, o, lse, do, dq_acc, dk_acc, dv_acc, *, causal: bool,
     import torch
     _check_tensors(q, k, v, o, do, dtype=torch.bfloat16)
     _check_tensors(lse, dq_acc, dk_acc, dv_acc, dtype=torch.float32)
-    B, S, Hq, Hkv, D, n = _shape(q, k, cu_seqlens)
-    if tuple(dq_acc.shape) != tuple(q.shape) or tuple(dk_acc.shape) != tuple(k.shape) or \
-            tuple(dv_acc.shape) != tuple(v.shape):
-        raise ValueError("dq_acc, dk_acc, dv_acc must have the shapes of q, k, v")
+    B, S, Hq, Hkv, D, n = _shape(q, k, v, cu_seqlens)
+    _bwd_operands(o, lse, do, B, S, Hq, D)
+    _bwd_outputs(dq_acc, dk_acc, dv_acc, B, S, Hq, Hkv, D, torch.float32)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     nbytes = bwd_workspace_bytes(B, Hq, Hkv, S, D)
@@ -364,12 +399,14 @@ def bwd_noalloc(q, k, v, o, lse, do, *, causal: bool, cu_seqlens=None, scale: Op
     import torch
     _check_tensors(q, k, v, o, do, dtype=torch.bfloat16)
     _check_tensors(lse, dtype=torch.float32)
-    B, S, Hq, Hkv, D, n = _shape(q, k, cu_seqlens)
+    B, S, Hq, Hkv, D, n = _shape(q, k, v, cu_seqlens)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    _bwd_operands(o, lse, do, B, S, Hq, D)
     dq = dq if dq is not None else torch.empty_like(q)
     dk = dk if dk is not None else torch.empty_like(k)
     dv = dv if dv is not None else torch.empty_like(v)
+    _bwd_outputs(dq, dk, dv, B, S, Hq, Hkv, D, torch.bfloat16)
     st = load_library().attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
                                          _ptr(dv), B, Hq, Hkv, S, D, int(bool(causal)), _ptr(cu_seqlens), n,
                                          float(scale), _stream())
@@ -388,12 +425,15 @@ def bwd_fp8(q8, k8, v8, descale_q, descale_k, descale_v, o, lse, do, *, causal: 
     _check_tensors(q8, k8, v8, dtype=torch.uint8)
     _check_tensors(descale_q, descale_k, descale_v, lse, dtype=torch.float32)
     _check_tensors(o, do, dtype=torch.bfloat16)
-    B, S, Hq, Hkv, D, n = _shape(q8, k8, cu_seqlens)
+    B, S, Hq, Hkv, D, n = _shape(q8, k8, v8, cu_seqlens)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    _check_descales(descale_q, descale_k, descale_v)
+    _bwd_operands(o, lse, do, B, S, Hq, D)
     dq = dq if dq is not None else torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device=q8.device)
     dk = dk if dk is not None else torch.empty((B, S, Hkv, D), dtype=torch.bfloat16, device=q8.device)
     dv = dv if dv is not None else torch.empty((B, S, Hkv, D), dtype=torch.bfloat16, device=q8.device)
+    _bwd_outputs(dq, dk, dv, B, S, Hq, Hkv, D, torch.bfloat16)
     nbytes = bwd_fp8_workspace_bytes(B, Hq, Hkv, S, D)
     if workspace is None:
         workspace = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=q8.device)
