@@ -504,7 +504,7 @@ __global__ __launch_bounds__(256) void attn_fwd_combine_kernel(FwdParams p) {
 // Rows that see fewer than 64 keys (the first 63 rows of every causal segment,
 // and every row of a non-causal segment shorter than 64) carry their whole
 // softmax on a handful of probabilities, so the bf16 rounding of P in the
-// tiled kernel (2^-9 relative) shows in their O. This kernel recomputes those
+// tiled kernel (up to 2^-8 relative) shows in their O. This kernel recomputes those
 // rows exactly as the definition reads, in fp32 with unrounded
 // probabilities, and overwrites their O and LSE: scores s_j = scale q . k_j,
 // an online maximum and normaliser over the row's keys, O = sum_j p_j v_j / l,

@@ -176,3 +176,53 @@ def _sweep_fp8_case(case, shape):
     e_mo, e_ml = rel_l2(host(o_acc), mo), max_abs(host(l_acc), ml)
     print(f"fp8 fwd_merge O relL2={e_mo:.3e} LSE maxabs={e_ml:.3e}", flush=True)
     assert e_mo <= TOL_FP8_REL and e_ml <= TOL_LSE
+
+
+# Stress draws: the same random shapes with Q and K scaled (peaky softmax rows: the forward's running maximum
+# moves past the first tile's, the backward's rows are dominated by a few keys). Outside the stated workloads,
+# so O is held to the bound of the kernel's rounding (rounding_o_bound) and the fp8 LSE to fp8_lse_bound; the
+# gradients keep the general 1e-2 (the worst of 1200 such draws: dQ 9.1e-3, dK 9.2e-3).
+# ATTN_STRESS_CASES=N runs the first N.
+STRESS = [(_draw(10000 + i), (2.5, 3.0, 4.0)[i % 3]) for i in range(int(os.environ.get("ATTN_STRESS_CASES", "12")))]
+
+
+@pytest.mark.parametrize("case", range(len(STRESS)))
+def test_sweep_stress_case(case):
+    import torch
+    import long_context_exact_fwd_amd as lca
+    from tests.gpu_helpers import TOL_FP8_REL, dev_u8, fp8_lse_bound, max_abs, rel_l2, rounding_o_bound
+    (B, Hq, Hkv, S, D, causal, lengths), qk_std = STRESS[case]
+    print(f"stress {case}: B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} causal={causal} lengths={lengths} qk_std={qk_std}",
+          flush=True)
+    x = si.make_inputs(B, Hq, Hkv, S, D, seed=20000 + case, lengths=lengths, qk_std=qk_std)
+    q, k, v, do = dev_bf16(x.q_bits), dev_bf16(x.k_bits), dev_bf16(x.v_bits), dev_bf16(x.do_bits)
+    cu = dev_i32(x.cu_seqlens) if x.cu_seqlens is not None else None
+    scale = 1.0 / np.sqrt(D)
+    qv, kv, vv, dov = (x.values(n) for n in ("q", "k", "v", "do"))
+    ro, rl = oracle.attention_fwd(qv, kv, vv, causal=causal, scale=scale, cu_seqlens=x.cu_seqlens, workers=None)
+    abar, _ = oracle.attention_fwd(qv, kv, np.abs(vv), causal=causal, scale=scale, cu_seqlens=x.cu_seqlens,
+                                   workers=None)
+    o, lse = lca.fwd(q, k, v, causal=causal, cu_seqlens=cu, scale=scale)
+    grads = lca.bwd(q, k, v, o, lse, do, causal=causal, cu_seqlens=cu, scale=scale)
+    torch.cuda.synchronize()
+    check_fwd(host(o), host(lse), ro, rl, tag="stress fwd", bound=rounding_o_bound(host(o), ro, abar))
+    rq, rk, rv = oracle.attention_bwd(qv, kv, vv, dov, causal=causal, scale=scale, cu_seqlens=x.cu_seqlens,
+                                      workers=None)
+    check_grads([("dQ", host(grads[0]), rq), ("dK", host(grads[1]), rk), ("dV", host(grads[2]), rv)],
+                tag="stress bwd")
+    if D != 128:
+        return
+    x8 = si.make_inputs(B, Hq, Hkv, S, D, seed=30000 + case, lengths=lengths, fp8=True, qk_std=qk_std,
+                        with_do=False)
+    q8, k8, v8 = dev_u8(x8.q_bits), dev_u8(x8.k_bits), dev_u8(x8.v_bits)
+    ds = [torch.tensor([float(d)], dtype=torch.float32, device="cuda") for d in x8.descale]
+    qv8, kv8, vv8 = (oracle.e4m3_decode(b) * float(d) for b, d in zip((x8.q_bits, x8.k_bits, x8.v_bits), x8.descale))
+    ro8, rl8 = oracle.attention_fwd(qv8, kv8, vv8, causal=causal, scale=scale, cu_seqlens=x8.cu_seqlens,
+                                    workers=None)
+    o8, l8 = lca.fwd_fp8(q8, k8, v8, *ds, causal=causal, cu_seqlens=cu, scale=scale)
+    torch.cuda.synchronize()
+    e_o = rel_l2(host(o8), ro8)
+    worst = float(np.max(np.abs(host(l8) - rl8) / fp8_lse_bound(qv8, kv8, causal, scale, x8.cu_seqlens)))
+    print(f"stress fp8 fwd O relL2={e_o:.3e} LSE maxabs={max_abs(host(l8), rl8):.3e} ({worst:.2f} of its bound)",
+          flush=True)
+    assert np.all(np.isfinite(host(o8))) and e_o <= TOL_FP8_REL and worst <= 1.0
