@@ -59,6 +59,15 @@ def test_tiny_workload(causal):
     _run_case(w.batch, w.hq, w.hkv, w.seqlen, w.head_dim, causal, seed=w.seed)
 
 
+def _short_segments(seed, total, hi):
+    """Seeded segment lengths in [1, hi] summing to total (the last one takes the remainder)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while sum(out) < total:
+        out.append(int(min(rng.integers(1, hi + 1), total - sum(out))))
+    return out
+
+
 EDGE = [
     # B, Hq, Hkv, S, D, causal, lengths
     (1, 1, 1, 1, 64, True, None),
@@ -78,6 +87,9 @@ EDGE = [
     (1, 2, 1, 64, 128, True, [1] * 64),           # every segment one token: O = V, LSE = scale q.k
     (1, 3, 3, 80, 64, False, [1] * 80),
     (1, 3, 3, 320, 64, False, [64, 64, 128, 64]),  # segments ending on tile boundaries
+    # about 150 short segments straddling tiles: nearly every row a few-key row
+    (1, 4, 2, 3000, 128, True, _short_segments(91, 3000, 40)),
+    (1, 2, 1, 2500, 64, False, _short_segments(92, 2500, 90)),  # both sides of 64 keys, non-causal
 ]
 
 
