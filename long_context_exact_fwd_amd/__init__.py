@@ -32,6 +32,7 @@ ATTN_ERR_DEBUG_CHECK = 5
 NOALLOC_SCRATCH_BYTES = 64 << 20  # ATTN_NOALLOC_SCRATCH_BYTES in include/attn.h
 
 _lib = None
+_lib_path = LIB_PATH  # the library load_library() opens: release, or debug after use_debug_library()
 
 
 class AttnError(RuntimeError):
@@ -45,7 +46,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or _lib_path
     if not os.path.exists(p):
         raise ImportError(f"{p} is missing: build it with `python -m long_context_exact_fwd_amd.build`")
     lib = ctypes.CDLL(p)
@@ -86,12 +87,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     return lib
 
 
-def use_debug_library(debug: bool = True) -> ctypes.CDLL:
-    """Route every call of this module through libmi355attn_debug.so (or back to libmi355attn.so)."""
-    global _lib
+def use_debug_library(debug: bool = True) -> None:
+    """Route every later call of this module through libmi355attn_debug.so (or back to libmi355attn.so).
+    The library is loaded by the next call, as the release one is by the first."""
+    global _lib, _lib_path
+    _lib_path = DEBUG_LIB_PATH if debug else LIB_PATH
     _lib = None
-    _lib = load_library(DEBUG_LIB_PATH if debug else LIB_PATH)
-    return _lib
 
 
 EXPORTED = ("attn_fwd", "attn_fwd_workspace_bytes", "attn_fwd_fp8", "attn_bwd", "attn_bwd_phases",
